@@ -1,0 +1,148 @@
+"""Pure-Python model of the paged-KV block manager.  (Test infrastructure.)
+
+Sources:
+* "vLLM的'内存分页'到底多神奇" (xxqk.cn), §2 "PagedAttention核心思想": memory is
+  cut into fixed-size pages; each sequence keeps a page table of the
+  physical pages it uses, which need not be contiguous; a scheduler hands out
+  pages from a free-page list and takes them back when a request ends;
+  sequences with the same prompt prefix can point at the same physical pages.
+* same page, §3 phase 1: a sequence's pages are taken on demand, one more
+  each time the current page fills (with 8-token pages, token 9 opens page 2).
+* same page, §3 phase 3: a finished sequence's pages go back to the free
+  list; pages shared through prefix caching carry a reference count and are
+  returned only when the last sharer ends.
+* same page, §4: admission control refuses (or queues) a request when not
+  enough free pages exist, instead of risking an out-of-memory failure;
+  aborting a request frees all of its pages.
+
+Policy choices the pages leave open (listed in the design doc):
+* the free list is a LIFO stack; it starts as ``free_order`` (or ascending
+  ids) with ``free_order[0]`` on top; a block whose refcount drops to zero is
+  pushed back on top, and a sequence's blocks are pushed in table order;
+* ``append`` is all-or-nothing: if the free list cannot cover the new blocks
+  it fails with NO_BLOCKS and changes nothing;
+* ``fork`` shares whole blocks only: the source length must be a multiple of
+  block_size (copy-on-write of a partly filled shared block is not modelled);
+* block ids are int32; tables export padded with -1.
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, List, Optional, Sequence
+
+OK, ERR_INVALID, ERR_NO_BLOCKS, ERR_UNSUPPORTED, ERR_HIP, ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
+
+
+class BlockManagerModel:
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("free_order must be a permutation of range(num_blocks)")
+        # Python list used as a stack: the top is the last element.
+        self.free: List[int] = list(reversed(order))
+        self.ref: List[int] = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+
+    # ---------------------------------------------------------------- ops
+    def append(self, seq: int, n: int):
+        """Grow ``seq`` by n tokens. Returns (status, slots)."""
+        if n < 0:
+            return ERR_INVALID, []
+        table = self.tables.get(seq, [])
+        L = self.lens.get(seq, 0)
+        bs = self.block_size
+        have = len(table)
+        need = -(-(L + n) // bs) - have
+        if need > len(self.free):
+            return ERR_NO_BLOCKS, []
+        table = list(table)
+        for _ in range(need):
+            blk = self.free.pop()
+            self.ref[blk] += 1
+            table.append(blk)
+        self.tables[seq] = table
+        self.lens[seq] = L + n
+        slots = [table[p // bs] * bs + p % bs for p in range(L, L + n)]
+        return OK, slots
+
+    def fork(self, src: int, dst: int) -> int:
+        if src not in self.tables:
+            return ERR_UNKNOWN_SEQ
+        if dst in self.tables or dst == src:
+            return ERR_INVALID
+        if self.lens[src] % self.block_size:
+            return ERR_UNSUPPORTED
+        self.tables[dst] = list(self.tables[src])
+        self.lens[dst] = self.lens[src]
+        for blk in self.tables[dst]:
+            self.ref[blk] += 1
+        return OK
+
+    def free_seq(self, seq: int) -> int:
+        if seq not in self.tables:
+            return ERR_UNKNOWN_SEQ
+        for blk in self.tables.pop(seq):
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0:
+                self.free.append(blk)
+        del self.lens[seq]
+        return OK
+
+    def block_tables(self, seqs: Iterable[int], max_blocks: int):
+        """(status, tables [n][max_blocks] padded -1, lens [n])."""
+        tables, lens = [], []
+        for s in seqs:
+            if s not in self.tables:
+                return ERR_UNKNOWN_SEQ, None, None
+            t = self.tables[s]
+            if len(t) > max_blocks:
+                return ERR_INVALID, None, None
+            tables.append(t + [-1] * (max_blocks - len(t)))
+            lens.append(self.lens[s])
+        return OK, tables, lens
+
+    def stats(self) -> dict:
+        bs = self.block_size
+        fill = [0] * self.num_blocks
+        for s, t in self.tables.items():
+            L = self.lens[s]
+            for i, blk in enumerate(t):
+                fill[blk] = max(fill[blk], min(bs, L - i * bs))
+        used = sum(1 for r in self.ref if r > 0)
+        return {
+            "free_blocks": len(self.free),
+            "used_blocks": used,
+            "shared_blocks": sum(1 for r in self.ref if r > 1),
+            "filled_slots": sum(fill),
+            "allocated_slots": used * bs,
+        }
+
+    # -------------------------------------------------------------- checks
+    def check_invariants(self) -> None:
+        """Conservation, refcount = table occurrences, and no duplicate frees."""
+        assert len(set(self.free)) == len(self.free), "block on the free list twice"
+        count = [0] * self.num_blocks
+        for t in self.tables.values():
+            for blk in t:
+                count[blk] += 1
+        assert count == self.ref, "refcount != number of table occurrences"
+        used = {b for b in range(self.num_blocks) if self.ref[b] > 0}
+        assert used.isdisjoint(self.free), "a used block is on the free list"
+        assert len(used) + len(self.free) == self.num_blocks, "blocks lost or duplicated"
+        for s, t in self.tables.items():
+            assert len(t) == -(-self.lens[s] // self.block_size), "table length != ceil(L/bs)"
+
+
+def blocks_needed(n_tokens: int, block_size: int) -> int:
+    """Pages a sequence of n tokens occupies: ceil(n / block_size)."""
+    return -(-n_tokens // block_size)
+
+
+def kv_block_bytes(block_size: int, heads: int, head_dim: int, elem_bytes: int) -> int:
+    """K+V bytes of one block: block_size * 2 * heads * head_dim * elem_bytes
+    ("LLM推理优化：技术原理解析总览", §3.3, the per-page size formula)."""
+    return block_size * 2 * heads * head_dim * elem_bytes
