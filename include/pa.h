@@ -1,0 +1,212 @@
+/*
+ * pa.h — paged KV-cache attention for AMD Instinct MI355X (gfx950). C ABI.
+ *
+ * What is computed. A sequence's keys and values live in fixed-size physical
+ * blocks ("pages") of two pools, k_cache and v_cache, each laid out
+ * [num_blocks, block_size, num_kv_heads, head_dim] ("LLM推理优化：技术原理解析
+ * 总览", dpshk.com, §3.3 — the page layout, block_size 16 typical). A
+ * per-sequence block table maps logical block i to a physical block id
+ * ("vLLM的'内存分页'到底多神奇 — PagedAttention原理图解", xxqk.cn, §2: pages,
+ * the per-sequence page table, the free-page list). Attention walks the table,
+ * reads the pages in logical order as one contiguous K/V, and computes
+ * softmax(scale · q·Kᵀ)·V (same page, §3 phase 2).
+ *
+ * Conventions shared by every call:
+ *  - Status: every call returns pa_status (0 = OK) and never throws across the
+ *    ABI. On error nothing is launched and no state changes; pa_last_error()
+ *    gives a thread-local message for the last non-OK status of this thread.
+ *  - Ownership: the library owns only the pool handle and its host-side
+ *    bookkeeping. All device buffers (k_cache, v_cache, q, out, tables,
+ *    workspace) are allocated and owned by the caller, who keeps them alive
+ *    until the stream work that uses them has completed.
+ *  - Pointers marked "device" are device (HBM) addresses on the current HIP
+ *    device; pointers marked "host" are ordinary host memory.
+ *  - Streams: `stream` is a hipStream_t (NULL = the default stream). Device
+ *    calls are asynchronous: they enqueue work and return.
+ *  - Threads: a pool is not thread-safe; callers serialise calls on one pool.
+ *  - Supported set: head_dim ∈ {64, 128}; block_size ∈ {8, 16, 32};
+ *    dtype ∈ {PA_F32, PA_BF16}; num_q_heads a multiple of num_kv_heads with
+ *    group G = num_q_heads / num_kv_heads ∈ {1, 2, 4, 8}. q, out and the pools
+ *    share one dtype. Anything else returns PA_ERR_UNSUPPORTED.
+ *  - Grouped-query attention: q head h reads kv head h / G.
+ *  - Block ids in tables are int32. Table contents are not validated on the
+ *    device: an id outside [0, num_blocks) is undefined (the kernels clamp it
+ *    into range so that it cannot fault, and the result is then meaningless).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* bad argument (null pointer, negative size, bad geometry) */
+  PA_ERR_NO_BLOCKS = -2,   /* free list cannot cover the request; nothing changed      */
+  PA_ERR_UNSUPPORTED = -3, /* valid but outside the supported set                      */
+  PA_ERR_HIP = -4,         /* a HIP runtime call failed (launch, device query)         */
+  PA_ERR_UNKNOWN_SEQ = -5  /* sequence id not known to the pool                        */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Geometry of the two pools. dtype holds a pa_dtype value. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+} pa_kv_layout;
+
+typedef struct pa_pool pa_pool; /* opaque, library-owned */
+
+/* Block accounting ("vLLM的'内存分页'到底多神奇", §5 monitoring: cache usage).
+ * used = refcount > 0; shared = refcount > 1; allocated_slots = used ×
+ * block_size; filled_slots = slots holding a valid token. The difference is
+ * the in-page tail waste, the only fragmentation paging leaves (same page,
+ * §2 comparison table). */
+typedef struct {
+  int32_t free_blocks;
+  int32_t used_blocks;
+  int32_t shared_blocks;
+  int32_t reserved;
+  int64_t filled_slots;
+  int64_t allocated_slots;
+} pa_pool_stats_t;
+
+/* ------------------------------------------------------------------------ */
+/* Pool and host block manager                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Create a pool over caller-owned device buffers k_cache and v_cache, each
+ * layout->num_blocks × block_size × num_kv_heads × head_dim elements of
+ * layout->dtype, row-major in that order. free_order (host, may be NULL) is a
+ * permutation of [0, num_blocks) giving the order in which free blocks are
+ * handed out (free_order[0] first); NULL means ascending ids. The free list is
+ * a LIFO stack: blocks returned by pa_seq_free are reused first.
+ * On success *out receives the handle. Errors: PA_ERR_INVALID (null pointers,
+ * non-positive sizes, free_order not a permutation), PA_ERR_UNSUPPORTED
+ * (geometry outside the supported set). */
+pa_status pa_alloc_pool(const pa_kv_layout* layout, void* k_cache, void* v_cache,
+                        const int32_t* free_order, pa_pool** out);
+
+/* Destroy a pool handle (host bookkeeping only; device buffers stay the
+ * caller's). NULL is ignored. */
+void pa_free_pool(pa_pool* pool);
+
+/* Grow sequence seq_id by n_tokens (creating it if unknown), taking new blocks
+ * from the free list on demand: a token goes into the sequence's last block
+ * until it is full, then a fresh block is taken ("vLLM的'内存分页'到底多神奇",
+ * §3 phase 1). All-or-nothing: if the free list cannot cover the new blocks,
+ * returns PA_ERR_NO_BLOCKS and changes nothing (admission control, same page,
+ * §4). slots_out (host, n_tokens int64, may be NULL when n_tokens == 0)
+ * receives the flat slot of each new token, slot = table[pos / block_size] ×
+ * block_size + pos % block_size, for pos = old_len .. old_len + n_tokens - 1.
+ * Errors: PA_ERR_INVALID (n_tokens < 0, null slots_out, length overflow). */
+pa_status pa_seq_append(pa_pool* pool, int64_t seq_id, int32_t n_tokens, int64_t* slots_out);
+
+/* Make dst a new sequence that shares all of src's blocks (prefix sharing:
+ * same physical blocks, each block's refcount + 1; "vLLM的'内存分页'到底多神奇",
+ * §2 and §3 phase 3). Only whole blocks are shared: src's length must be a
+ * multiple of block_size, else PA_ERR_UNSUPPORTED (no copy-on-write of a
+ * partly filled shared block). Errors: PA_ERR_UNKNOWN_SEQ (src unknown),
+ * PA_ERR_INVALID (dst exists or dst == src). */
+pa_status pa_seq_fork(pa_pool* pool, int64_t src_seq_id, int64_t dst_seq_id);
+
+/* End a sequence: each of its blocks loses one reference; a block whose count
+ * reaches zero goes back on top of the free list, in table order (same page,
+ * §3 phase 3; aborting a request frees its pages, §4). Errors:
+ * PA_ERR_UNKNOWN_SEQ. */
+pa_status pa_seq_free(pa_pool* pool, int64_t seq_id);
+
+/* Export block tables and lengths for n sequences, in the order given by
+ * seq_ids (host, n). tables_out (host, n × max_blocks int32, row-major) gets
+ * each sequence's physical block ids, padded with -1; seq_lens_out (host, n
+ * int32) gets each length. Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID (a
+ * sequence needs more than max_blocks entries, a length above INT32_MAX, or
+ * null/negative arguments). Nothing is written on error. */
+pa_status pa_block_tables(const pa_pool* pool, const int64_t* seq_ids, int32_t n,
+                          int32_t max_blocks, int32_t* tables_out, int32_t* seq_lens_out);
+
+/* Current block accounting into *out (host). */
+pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
+
+/* ------------------------------------------------------------------------ */
+/* Device operations                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* KV append scatter (paging's O(1) append: "LLM推理优化：技术原理解析总览", §2.2).
+ * key, value (device): [T, num_kv_heads, head_dim] of the pool dtype,
+ * contiguous. slot_mapping (device): T int64 flat slots from pa_seq_append.
+ * Row t is copied bit for bit to k_cache/v_cache[slot / block_size][slot %
+ * block_size]. A negative slot is padding and is skipped; a slot ≥
+ * num_blocks × block_size is also skipped (no fault). Two rows with the same
+ * slot race (undefined which lands). T == 0 launches nothing.
+ * Errors: PA_ERR_INVALID (T < 0, null pointers with T > 0), PA_ERR_HIP. */
+pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value,
+                      const int64_t* slot_mapping, int32_t T, void* stream);
+
+/* Bytes of device workspace pa_decode needs for this shape: fp32 partial
+ * states of ceil(max_seq_len / partition_tokens) KV partitions per (sequence,
+ * q head). 0 when a single partition covers max_seq_len. partition_tokens 0
+ * means the default (512). Returns 0 for invalid arguments. */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t partition_tokens);
+
+/* Decode attention: one query token per sequence over its paged cache.
+ * out (device): [B, num_q_heads, head_dim], pool dtype, written.
+ * q (device): [B, num_q_heads, head_dim], pool dtype.
+ * block_tables (device): [B, max_blocks] int32, row b = sequence b's table.
+ * seq_lens (device): [B] int32, valid cache entries of each sequence at call
+ *   time (the new token included, i.e. after pa_write_kv). Entries past
+ *   ceil(L / block_size) and slots past L in the last block are never used.
+ *   A value outside [0, max_seq_len] is clamped into it.
+ * scale: multiplies q·k before the softmax (1/sqrt(head_dim) usually).
+ * max_seq_len: an upper bound on seq_lens (sizes the grid); must satisfy
+ *   max_seq_len ≤ max_blocks × block_size.
+ * partition_tokens: long contexts are split into KV partitions of this many
+ *   tokens, each reduced to (max, sum, Σ weight·V), then merged by
+ *   log-sum-exp. 0 = 512. Must be a multiple of 64, at most 2048, with
+ *   partition_tokens × G ≤ 8192 (else PA_ERR_UNSUPPORTED).
+ * workspace (device) of workspace_bytes ≥ pa_decode_workspace_bytes(...);
+ *   may be NULL when that is 0.
+ * L = 0 gives a zero output row.
+ * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
+pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* block_tables,
+                    int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t num_q_heads,
+                    float scale, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Chunked causal prefill (a long prompt processed in chunks: "LLM推理优化：技术
+ * 原理解析总览", §2.3; prefill and decode mixed in one step: "vLLM 生产级落地
+ * 深剖", musen-ai.com, §2). The chunk's own K/V must already be in the cache
+ * (pa_write_kv). Sequence b's chunk has n_b = cu_q_lens[b+1] - cu_q_lens[b]
+ * query rows; its cache holds L_b = seq_lens[b] tokens (chunk included); row i
+ * sits at absolute position L_b - n_b + i and attends to tokens 0 ..
+ * L_b - n_b + i.
+ * out, q (device): [T, num_q_heads, head_dim] bf16, T = cu_q_lens[B].
+ * cu_q_lens (device): [B + 1] int32, non-decreasing, cu_q_lens[0] = 0.
+ * block_tables (device): [B, max_blocks] int32. seq_lens (device): [B] int32.
+ * max_q_len: an upper bound on n_b (sizes the grid); rows past it are not
+ *   computed. Rows with a negative position (n_b > L_b) get zeros.
+ * seq_lens values are clamped to max_blocks × block_size.
+ * Only PA_BF16 pools are supported here (bf16 MFMA); PA_F32 returns
+ * PA_ERR_UNSUPPORTED. Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
+pa_status pa_prefill(pa_pool* pool, void* out, const void* q, const int32_t* cu_q_lens,
+                     const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                     int32_t B, int32_t num_q_heads, int32_t max_q_len, float scale, void* stream);
+
+/* Thread-local text describing the last non-OK status returned on this
+ * thread ("" if none). Valid until the next call on this thread. */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,219 @@
+"""paged_kv_cache_indirect_amd — paged KV-cache attention on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libpa.so`` (the C ABI declared in
+``include/pa.h``). Each ``pa_*`` function here has the same name as the C
+entry point and only marshals arguments: torch tensors become device
+pointers, numpy arrays become host pointers, the current torch stream becomes
+the hipStream_t. Every step of the computation runs in the library's HIP
+kernels and host block manager. If the library is not built, importing this
+package raises: there is no fallback path.
+
+Build it with ``python -m paged_kv_cache_indirect_amd.build`` (or
+``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "PaError", "PA_OK", "PA_ERR_INVALID", "PA_ERR_NO_BLOCKS", "PA_ERR_UNSUPPORTED", "PA_ERR_HIP",
+    "PA_ERR_UNKNOWN_SEQ", "PA_F32", "PA_BF16", "LIB_PATH", "lib",
+    "pa_alloc_pool", "pa_free_pool", "pa_seq_append", "pa_seq_fork", "pa_seq_free",
+    "pa_block_tables", "pa_pool_stats", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
+    "pa_prefill", "pa_last_error",
+]
+
+PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
+PA_F32, PA_BF16 = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_indirect_amd.build`")
+
+# One HIP runtime per process: torch ships its own libamdhip64 (soname
+# libamdhip64.so.7, the same as the system one). Loading torch first makes the
+# library's libamdhip64.so.7 dependency bind to that already-loaded runtime, so
+# torch's device pointers and streams are valid in the library.
+import torch  # noqa: E402,F401
+
+lib = ctypes.CDLL(LIB_PATH)
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [("free_blocks", ctypes.c_int32), ("used_blocks", ctypes.c_int32),
+                ("shared_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("filled_slots", ctypes.c_int64), ("allocated_slots", ctypes.c_int64)]
+
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "pa_alloc_pool": (_i32, [ctypes.POINTER(_Layout), _vp, _vp, _vp, ctypes.POINTER(_vp)]),
+    "pa_free_pool": (None, [_vp]),
+    "pa_seq_append": (_i32, [_vp, _i64, _i32, _vp]),
+    "pa_seq_fork": (_i32, [_vp, _i64, _i64]),
+    "pa_seq_free": (_i32, [_vp, _i64]),
+    "pa_block_tables": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "pa_pool_stats": (_i32, [_vp, ctypes.POINTER(_Stats)]),
+    "pa_write_kv": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp]),
+    "pa_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.pa_last_error().decode(errors="replace")
+        super().__init__(f"{where} failed with status {status}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != PA_OK:
+        raise PaError(status, where)
+
+
+def _dptr(t) -> int:
+    """Device pointer of a torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------- pools
+def pa_alloc_pool(k_cache, v_cache, free_order: Optional[Sequence[int]] = None) -> int:
+    """Create a pool over k_cache/v_cache (torch device tensors [nb, bs, Hkv, D]).
+    Returns the opaque handle (an int)."""
+    if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.dim() != 4 or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must be matching [num_blocks, block_size, Hkv, D] tensors")
+    nb, bs, hkv, d = (int(x) for x in k_cache.shape)
+    layout = _Layout(nb, bs, hkv, d, _dtype_code(k_cache))
+    order = None
+    if free_order is not None:
+        order = np.ascontiguousarray(free_order, dtype=np.int32)
+        if order.shape != (nb,):
+            raise ValueError("free_order must have num_blocks entries")
+    handle = _vp()
+    _check(lib.pa_alloc_pool(ctypes.byref(layout), _dptr(k_cache), _dptr(v_cache),
+                             None if order is None else order.ctypes.data, ctypes.byref(handle)),
+           "pa_alloc_pool")
+    return handle.value
+
+
+def pa_free_pool(pool: int) -> None:
+    lib.pa_free_pool(pool)
+
+
+def pa_seq_append(pool: int, seq_id: int, n_tokens: int) -> np.ndarray:
+    """Returns the new tokens' flat slots (host int64 array)."""
+    slots = np.empty(max(n_tokens, 0), dtype=np.int64)
+    _check(lib.pa_seq_append(pool, seq_id, n_tokens, slots.ctypes.data if n_tokens > 0 else None),
+           "pa_seq_append")
+    return slots
+
+
+def pa_seq_fork(pool: int, src_seq_id: int, dst_seq_id: int) -> None:
+    _check(lib.pa_seq_fork(pool, src_seq_id, dst_seq_id), "pa_seq_fork")
+
+
+def pa_seq_free(pool: int, seq_id: int) -> None:
+    _check(lib.pa_seq_free(pool, seq_id), "pa_seq_free")
+
+
+def pa_block_tables(pool: int, seq_ids: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Returns (tables int32 [n, max_blocks] padded -1, seq_lens int32 [n]) on the host."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    n = len(ids)
+    tables = np.empty((n, max_blocks), dtype=np.int32)
+    lens = np.empty(n, dtype=np.int32)
+    _check(lib.pa_block_tables(pool, ids.ctypes.data, n, max_blocks, tables.ctypes.data, lens.ctypes.data),
+           "pa_block_tables")
+    return tables, lens
+
+
+def pa_pool_stats(pool: int) -> dict:
+    s = _Stats()
+    _check(lib.pa_pool_stats(pool, ctypes.byref(s)), "pa_pool_stats")
+    return {"free_blocks": s.free_blocks, "used_blocks": s.used_blocks,
+            "shared_blocks": s.shared_blocks, "filled_slots": s.filled_slots,
+            "allocated_slots": s.allocated_slots}
+
+
+def pa_last_error() -> str:
+    return lib.pa_last_error().decode(errors="replace")
+
+
+# ------------------------------------------------------------ device ops
+def pa_write_kv(pool: int, key, value, slot_mapping, stream=None) -> None:
+    """key/value: device [T, Hkv, D]; slot_mapping: device int64 [T]."""
+    T = int(slot_mapping.shape[0])
+    _check(lib.pa_write_kv(pool, _dptr(key), _dptr(value), _dptr(slot_mapping), T, _stream(stream)),
+           "pa_write_kv")
+
+
+def pa_decode_workspace_bytes(B: int, num_q_heads: int, head_dim: int, max_seq_len: int,
+                              partition_tokens: int = 0) -> int:
+    return int(lib.pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_seq_len, partition_tokens))
+
+
+def pa_decode(pool: int, out, q, block_tables, seq_lens, scale: float, max_seq_len: int,
+              partition_tokens: int = 0, workspace=None, stream=None) -> None:
+    """out/q: device [B, Hq, D]; block_tables: device int32 [B, max_blocks];
+    seq_lens: device int32 [B]. ``workspace`` (device uint8 tensor) is
+    allocated here with torch when not given and needed."""
+    B, Hq, D = (int(x) for x in q.shape)
+    need = pa_decode_workspace_bytes(B, Hq, D, max_seq_len, partition_tokens)
+    if need and workspace is None:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_decode(pool, _dptr(out), _dptr(q), _dptr(block_tables), int(block_tables.shape[1]),
+                         _dptr(seq_lens), B, Hq, float(scale), int(max_seq_len), int(partition_tokens),
+                         _dptr(workspace), ws_bytes, _stream(stream)),
+           "pa_decode")
+
+
+def pa_prefill(pool: int, out, q, cu_q_lens, block_tables, seq_lens, scale: float, max_q_len: int,
+               stream=None) -> None:
+    """out/q: device [T, Hq, D] bf16; cu_q_lens: device int32 [B+1];
+    block_tables: device int32 [B, max_blocks]; seq_lens: device int32 [B]."""
+    B = int(seq_lens.shape[0])
+    Hq = int(q.shape[1])
+    _check(lib.pa_prefill(pool, _dptr(out), _dptr(q), _dptr(cu_q_lens), _dptr(block_tables),
+                          int(block_tables.shape[1]), _dptr(seq_lens), B, Hq, int(max_q_len),
+                          float(scale), _stream(stream)),
+           "pa_prefill")

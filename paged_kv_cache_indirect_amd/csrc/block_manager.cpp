@@ -1,0 +1,171 @@
+// Host block manager: see block_manager.h for the paging model it follows.
+#include "block_manager.h"
+
+#include <algorithm>
+#include <climits>
+
+namespace pa {
+
+namespace {
+int64_t CeilDiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+Status BlockManager::Validate(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                              std::string* err) {
+  if (num_blocks <= 0 || block_size <= 0) {
+    *err = "num_blocks and block_size must be positive";
+    return kErrInvalid;
+  }
+  if (free_order) {
+    std::vector<char> seen(static_cast<size_t>(num_blocks), 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[static_cast<size_t>(b)]) {
+        *err = "free_order is not a permutation of [0, num_blocks)";
+        return kErrInvalid;
+      }
+      seen[static_cast<size_t>(b)] = 1;
+    }
+  }
+  return kOk;
+}
+
+BlockManager::BlockManager(int32_t num_blocks, int32_t block_size, const int32_t* free_order)
+    : num_blocks_(num_blocks), block_size_(block_size),
+      ref_(static_cast<size_t>(num_blocks), 0) {
+  free_.resize(static_cast<size_t>(num_blocks));
+  // Stack top is the back: store the hand-out order reversed.
+  for (int32_t i = 0; i < num_blocks; ++i)
+    free_[static_cast<size_t>(num_blocks - 1 - i)] = free_order ? free_order[i] : i;
+}
+
+Status BlockManager::Append(int64_t seq, int32_t n, int64_t* slots_out, std::string* err) {
+  if (n < 0) {
+    *err = "n_tokens must be >= 0";
+    return kErrInvalid;
+  }
+  if (n > 0 && !slots_out) {
+    *err = "slots_out is null";
+    return kErrInvalid;
+  }
+  auto it = seqs_.find(seq);
+  const int64_t old_len = it == seqs_.end() ? 0 : it->second.len;
+  const int64_t new_len = old_len + n;
+  if (new_len > static_cast<int64_t>(INT32_MAX)) {
+    *err = "sequence length would exceed INT32_MAX";
+    return kErrInvalid;
+  }
+  const int64_t have = it == seqs_.end() ? 0 : static_cast<int64_t>(it->second.table.size());
+  const int64_t need = CeilDiv(new_len, block_size_) - have;
+  if (need > static_cast<int64_t>(free_.size())) {
+    *err = "not enough free blocks: need " + std::to_string(need) + ", have " +
+           std::to_string(free_.size());
+    return kErrNoBlocks;
+  }
+  // Everything that can throw happens before the first mutation.
+  if (it == seqs_.end()) it = seqs_.emplace(seq, Seq{}).first;
+  Seq& s = it->second;
+  s.table.reserve(static_cast<size_t>(have + need));
+  for (int64_t i = 0; i < need; ++i) {
+    int32_t blk = free_.back();
+    free_.pop_back();
+    ++ref_[static_cast<size_t>(blk)];
+    s.table.push_back(blk);
+  }
+  s.len = new_len;
+  const int64_t bs = block_size_;
+  for (int64_t p = old_len; p < new_len; ++p)
+    slots_out[p - old_len] = static_cast<int64_t>(s.table[static_cast<size_t>(p / bs)]) * bs + p % bs;
+  return kOk;
+}
+
+Status BlockManager::Fork(int64_t src, int64_t dst, std::string* err) {
+  auto it = seqs_.find(src);
+  if (it == seqs_.end()) {
+    *err = "unknown source sequence " + std::to_string(src);
+    return kErrUnknownSeq;
+  }
+  if (dst == src || seqs_.count(dst)) {
+    *err = "destination sequence " + std::to_string(dst) + " already exists";
+    return kErrInvalid;
+  }
+  if (it->second.len % block_size_) {
+    *err = "fork shares whole blocks only: source length is not a multiple of block_size";
+    return kErrUnsupported;
+  }
+  Seq copy = it->second;  // may throw before any mutation
+  for (int32_t blk : copy.table) ++ref_[static_cast<size_t>(blk)];
+  seqs_.emplace(dst, std::move(copy));
+  return kOk;
+}
+
+Status BlockManager::Free(int64_t seq, std::string* err) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end()) {
+    *err = "unknown sequence " + std::to_string(seq);
+    return kErrUnknownSeq;
+  }
+  // free_ never exceeds num_blocks_ entries: reserve once so push_back cannot throw.
+  free_.reserve(static_cast<size_t>(num_blocks_));
+  for (int32_t blk : it->second.table) {
+    if (--ref_[static_cast<size_t>(blk)] == 0) free_.push_back(blk);
+  }
+  seqs_.erase(it);
+  return kOk;
+}
+
+Status BlockManager::ExportTables(const int64_t* seqs, int32_t n, int32_t max_blocks,
+                                  int32_t* tables, int32_t* lens, std::string* err) const {
+  if (n < 0 || max_blocks < 0) {
+    *err = "n and max_blocks must be >= 0";
+    return kErrInvalid;
+  }
+  if (n > 0 && (!seqs || !lens || (max_blocks > 0 && !tables))) {
+    *err = "null pointer argument";
+    return kErrInvalid;
+  }
+  for (int32_t i = 0; i < n; ++i) {  // validate all before writing anything
+    auto it = seqs_.find(seqs[i]);
+    if (it == seqs_.end()) {
+      *err = "unknown sequence " + std::to_string(seqs[i]);
+      return kErrUnknownSeq;
+    }
+    if (static_cast<int64_t>(it->second.table.size()) > max_blocks) {
+      *err = "sequence " + std::to_string(seqs[i]) + " needs more than max_blocks table entries";
+      return kErrInvalid;
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = seqs_.find(seqs[i])->second;
+    int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
+    std::fill(row, row + max_blocks, -1);
+    std::copy(s.table.begin(), s.table.end(), row);
+    lens[i] = static_cast<int32_t>(s.len);
+  }
+  return kOk;
+}
+
+PoolStats BlockManager::Stats() const {
+  PoolStats st;
+  std::vector<int32_t> fill(static_cast<size_t>(num_blocks_), 0);
+  const int64_t bs = block_size_;
+  for (const auto& kv : seqs_) {
+    const Seq& s = kv.second;
+    for (size_t i = 0; i < s.table.size(); ++i) {
+      int64_t f = std::min<int64_t>(bs, s.len - static_cast<int64_t>(i) * bs);
+      int32_t& cur = fill[static_cast<size_t>(s.table[i])];
+      cur = std::max<int32_t>(cur, static_cast<int32_t>(f));
+    }
+  }
+  for (int32_t b = 0; b < num_blocks_; ++b) {
+    int32_t r = ref_[static_cast<size_t>(b)];
+    if (r > 0) ++st.used_blocks;
+    if (r > 1) ++st.shared_blocks;
+    st.filled_slots += fill[static_cast<size_t>(b)];
+  }
+  st.free_blocks = static_cast<int32_t>(free_.size());
+  st.allocated_slots = static_cast<int64_t>(st.used_blocks) * bs;
+  return st;
+}
+
+}  // namespace pa

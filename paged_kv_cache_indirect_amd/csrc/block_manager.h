@@ -1,0 +1,81 @@
+// Host-side block manager for a paged KV pool: free list, per-sequence block
+// tables, per-block reference counts.
+//
+// Paging model ("vLLM的'内存分页'到底多神奇 — PagedAttention原理图解", xxqk.cn):
+//  §2  the pool is cut into fixed-size pages; a sequence's page table lists
+//      the physical pages it uses, in logical order, and they need not be
+//      contiguous; free pages sit on a free list; sequences with the same
+//      prompt prefix may point at the same physical pages.
+//  §3  phase 1: pages are taken on demand, one more each time the current
+//      page fills; phase 3: a finished sequence's pages return to the free
+//      list, a shared page only when its last user ends (reference count).
+//  §4  admission control: refuse a request that cannot get its pages rather
+//      than run out of memory; abort frees every page of a request.
+//
+// Policy choices where the page is silent: the free list is a LIFO stack
+// seeded from a caller-given order; freed blocks are pushed in table order;
+// append is all-or-nothing; fork shares whole blocks only.
+//
+// Plain C++ (no HIP): it is built into the device library and, on its own,
+// into host-only test drivers.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+namespace pa {
+
+enum Status : int {
+  kOk = 0,
+  kErrInvalid = -1,
+  kErrNoBlocks = -2,
+  kErrUnsupported = -3,
+  kErrHip = -4,
+  kErrUnknownSeq = -5,
+};
+
+struct PoolStats {
+  int32_t free_blocks = 0;
+  int32_t used_blocks = 0;
+  int32_t shared_blocks = 0;
+  int64_t filled_slots = 0;
+  int64_t allocated_slots = 0;
+};
+
+class BlockManager {
+ public:
+  // free_order: nullptr (ascending ids) or a permutation of [0, num_blocks);
+  // free_order[0] is handed out first. Use Validate() first: the constructor
+  // assumes valid arguments.
+  BlockManager(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+
+  static Status Validate(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                         std::string* err);
+
+  Status Append(int64_t seq, int32_t n, int64_t* slots_out, std::string* err);
+  Status Fork(int64_t src, int64_t dst, std::string* err);
+  Status Free(int64_t seq, std::string* err);
+  Status ExportTables(const int64_t* seqs, int32_t n, int32_t max_blocks, int32_t* tables,
+                      int32_t* lens, std::string* err) const;
+  PoolStats Stats() const;
+
+  int32_t num_blocks() const { return num_blocks_; }
+  int32_t block_size() const { return block_size_; }
+  int32_t refcount(int32_t blk) const { return ref_[blk]; }
+  int32_t free_count() const { return static_cast<int32_t>(free_.size()); }
+
+ private:
+  struct Seq {
+    std::vector<int32_t> table;
+    int64_t len = 0;
+  };
+  int32_t num_blocks_;
+  int32_t block_size_;
+  std::vector<int32_t> free_;  // stack: back() is the next block handed out
+  std::vector<int32_t> ref_;
+  std::unordered_map<int64_t, Seq> seqs_;
+};
+
+}  // namespace pa

@@ -1,0 +1,57 @@
+// Kernel launchers called by the C-ABI layer (pa_api.cpp). Arguments are
+// validated by the caller; these only enqueue work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// KV append scatter: rows of `row_bytes` bytes (a multiple of 16).
+hipError_t LaunchWriteKv(const void* key, const void* value, const int64_t* slots, void* k_cache,
+                         void* v_cache, int32_t T, int64_t row_bytes, int64_t num_slots,
+                         hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* ws;          // partial states; null when num_partitions == 1
+  int32_t B, Hq, Hkv, D, G;
+  int32_t block_size, num_blocks, max_blocks;
+  int32_t max_seq_len, partition_tokens, num_partitions;
+  float scale;
+  int dtype;          // pa_dtype
+};
+hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_q_lens;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  int32_t B, Hq, Hkv, D, G;
+  int32_t block_size, num_blocks, max_blocks;
+  int32_t max_q_len;
+  float scale;
+};
+hipError_t LaunchPrefill(const PrefillArgs& a, hipStream_t stream);
+
+// Grid / workspace geometry shared by the API layer and the launchers.
+inline int32_t DecodePartitions(int32_t max_seq_len, int32_t partition_tokens) {
+  int32_t p = (max_seq_len + partition_tokens - 1) / partition_tokens;
+  return p < 1 ? 1 : p;
+}
+// Partial state per (sequence, q head, partition): D accumulators + (max, sum).
+inline size_t DecodeWorkspaceBytes(int32_t B, int32_t Hq, int32_t D, int32_t P) {
+  if (P <= 1) return 0;
+  return static_cast<size_t>(B) * Hq * P * (static_cast<size_t>(D) + 2) * sizeof(float);
+}
+
+}  // namespace pa

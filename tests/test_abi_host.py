@@ -1,0 +1,269 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+* libpa.so loads and exports every function include/pa.h declares;
+* the C++ block manager, driven through the C ABI, matches the Python model
+  bit for bit (statuses, slots, tables, lengths, stats) on seeded op streams;
+* the same C++ block manager built on its own with g++ under AddressSanitizer
+  and UBSan replays the same streams with identical output;
+* argument validation of the device entry points fails before any launch.
+"""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+CSRC = os.path.join(ROOT, "paged_kv_cache_indirect_amd", "csrc")
+
+pa = pytest.importorskip("paged_kv_cache_indirect_amd")
+from oracle.block_manager import BlockManagerModel  # noqa: E402
+
+FAKE_K, FAKE_V = 0x10000, 0x20000   # aligned, never dereferenced by host-only calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(pa.lib, n), f"libpa.so does not export {n}"
+
+
+def make_pool(nb, bs, order=None, hkv=2, d=64, dtype=pa.PA_BF16):
+    layout = pa._Layout(nb, bs, hkv, d, dtype)
+    h = ctypes.c_void_p()
+    arr = None if order is None else np.ascontiguousarray(order, dtype=np.int32)
+    st = pa.lib.pa_alloc_pool(ctypes.byref(layout), FAKE_K, FAKE_V,
+                              None if arr is None else arr.ctypes.data, ctypes.byref(h))
+    return st, h.value
+
+
+def random_ops(rng, n_ops, max_seqs=10, max_tokens=80):
+    ops = []
+    for _ in range(n_ops):
+        r = rng.random()
+        s = int(rng.integers(0, max_seqs))
+        if r < 0.5:
+            ops.append(("append", s, int(rng.integers(0, max_tokens))))
+        elif r < 0.7:
+            ops.append(("fork", s, int(rng.integers(0, max_seqs))))
+        elif r < 0.9:
+            ops.append(("free", s))
+        else:
+            ops.append(("tables", int(rng.integers(0, 12)), [int(x) for x in rng.integers(0, max_seqs, 3)]))
+    return ops
+
+
+def run_model(nb, bs, order, ops):
+    m = BlockManagerModel(nb, bs, order)
+    out = []
+    for op in ops:
+        if op[0] == "append":
+            st, slots = m.append(op[1], op[2])
+            out.append((st, list(slots)))
+        elif op[0] == "fork":
+            out.append((m.fork(op[1], op[2]),))
+        elif op[0] == "free":
+            out.append((m.free_seq(op[1]),))
+        else:
+            st, t, l = m.block_tables(op[2], op[1])
+            out.append((st, l, t))
+        s = m.stats()
+        out.append(tuple(s[k] for k in ("free_blocks", "used_blocks", "shared_blocks", "filled_slots",
+                                        "allocated_slots")))
+    return out
+
+
+def run_abi(pool, ops):
+    out = []
+    for op in ops:
+        if op[0] == "append":
+            slots = np.empty(max(op[2], 1), dtype=np.int64)
+            st = pa.lib.pa_seq_append(pool, op[1], op[2], slots.ctypes.data)
+            out.append((st, slots[:op[2]].tolist() if st == 0 else []))
+        elif op[0] == "fork":
+            out.append((pa.lib.pa_seq_fork(pool, op[1], op[2]),))
+        elif op[0] == "free":
+            out.append((pa.lib.pa_seq_free(pool, op[1]),))
+        else:
+            mb, ids = op[1], np.array(op[2], dtype=np.int64)
+            t = np.zeros((len(ids), max(mb, 1)), np.int32)
+            l = np.zeros(len(ids), np.int32)
+            st = pa.lib.pa_block_tables(pool, ids.ctypes.data, len(ids), mb, t.ctypes.data, l.ctypes.data)
+            out.append((st, l.tolist(), t[:, :mb].tolist()) if st == 0 else (st, None, None))
+        s = pa.pa_pool_stats(pool)
+        out.append(tuple(s[k] for k in ("free_blocks", "used_blocks", "shared_blocks", "filled_slots",
+                                        "allocated_slots")))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cpp_block_manager_matches_model(seed):
+    rng = np.random.default_rng(100 + seed)
+    nb, bs = 48, [8, 16, 32][seed % 3]
+    order = rng.permutation(nb) if seed % 2 else None
+    ops = random_ops(rng, 500)
+    st, pool = make_pool(nb, bs, order)
+    assert st == 0
+    try:
+        assert run_abi(pool, ops) == run_model(nb, bs, order, ops)
+    finally:
+        pa.pa_free_pool(pool)
+
+
+def test_workload_op_streams_match_model():
+    """The tables the named workloads build (tiny, prefix sharing) agree."""
+    import workloads as W
+    for wl in (W.config("tiny"), W.make_prefix_share("p", 16, 64, [0, 5, 16, 40] * 4, 8, 2, 64, 16,
+                                                        "bf16", 7)):
+        st, pool = make_pool(wl.num_blocks, wl.block_size, wl.free_order, wl.Hkv, wl.D)
+        m = BlockManagerModel(wl.num_blocks, wl.block_size, wl.free_order)
+        for op in wl.ops:
+            if op[0] == "append":
+                a = pa.pa_seq_append(pool, op[1], op[2])
+                stm, b = m.append(op[1], op[2])
+                assert stm == 0 and a.tolist() == b
+            else:
+                pa.pa_seq_fork(pool, op[1], op[2])
+                assert m.fork(op[1], op[2]) == 0
+        t, l = pa.pa_block_tables(pool, list(range(wl.B)), wl.max_blocks)
+        stm, tm, lm = m.block_tables(range(wl.B), wl.max_blocks)
+        assert t.tolist() == tm and l.tolist() == lm
+        pa.pa_free_pool(pool)
+
+
+def test_exhaustion_is_atomic_and_no_leaks():
+    st, pool = make_pool(10, 16)
+    pa.pa_seq_append(pool, 1, 100)                         # 7 blocks
+    before = pa.pa_pool_stats(pool)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_seq_append(pool, 2, 64)                      # needs 4, 3 free
+    assert e.value.status == pa.PA_ERR_NO_BLOCKS
+    assert "not enough free blocks" in pa.pa_last_error()
+    assert pa.pa_pool_stats(pool) == before
+    with pytest.raises(pa.PaError):
+        pa.pa_block_tables(pool, [2], 8)                   # sequence 2 was not created
+    pa.pa_seq_append(pool, 1, 12)                          # 112 = 7 blocks exactly
+    pa.pa_seq_fork(pool, 1, 3)
+    pa.pa_seq_free(pool, 1)
+    t, l = pa.pa_block_tables(pool, [3], 8)
+    assert l.tolist() == [112] and (t[0, :7] >= 0).all()
+    pa.pa_seq_free(pool, 3)
+    assert pa.pa_pool_stats(pool)["free_blocks"] == 10
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_seq_free(pool, 3)
+    assert e.value.status == pa.PA_ERR_UNKNOWN_SEQ
+    pa.pa_free_pool(pool)
+
+
+def test_alloc_pool_rejects_bad_geometry():
+    assert make_pool(10, 12)[0] == pa.PA_ERR_UNSUPPORTED       # block_size 12
+    assert make_pool(10, 16, d=96)[0] == pa.PA_ERR_UNSUPPORTED  # head_dim 96
+    assert make_pool(0, 16)[0] == pa.PA_ERR_INVALID
+    assert make_pool(4, 16, order=[0, 1, 1, 2])[0] == pa.PA_ERR_INVALID
+    assert make_pool(4, 16, dtype=7)[0] == pa.PA_ERR_UNSUPPORTED
+
+
+def test_device_entry_points_validate_before_launch():
+    st, pool = make_pool(64, 16, hkv=8, d=128)
+    assert st == 0
+    dummy = 0x40000
+    ws = pa.lib.pa_decode_workspace_bytes(64, 32, 128, 4096, 512)
+    assert ws == 64 * 32 * 8 * 130 * 4
+    assert pa.lib.pa_decode_workspace_bytes(64, 32, 128, 512, 512) == 0
+    # G = 3 is outside the supported set
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 24, 0.1, 4096, 0, dummy, ws, None) \
+        == pa.PA_ERR_UNSUPPORTED
+    # Hq not a multiple of Hkv
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 12, 0.1, 4096, 0, dummy, ws, None) \
+        == pa.PA_ERR_INVALID
+    # max_seq_len beyond the table width
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 16, dummy, 4, 32, 0.1, 4096, 0, dummy, ws, None) \
+        == pa.PA_ERR_INVALID
+    # workspace missing / too small
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 32, 0.1, 4096, 0, None, 0, None) \
+        == pa.PA_ERR_INVALID
+    assert "workspace too small" in pa.pa_last_error()
+    # partition size rules
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 32, 0.1, 4096, 100, dummy, 1 << 30, None) \
+        == pa.PA_ERR_UNSUPPORTED
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 64, 0.1, 4096, 2048, dummy, 1 << 30, None) \
+        == pa.PA_ERR_UNSUPPORTED
+    # misaligned q
+    assert pa.lib.pa_decode(pool, dummy, dummy + 2, dummy, 256, dummy, 4, 32, 0.1, 4096, 0, dummy, ws, None) \
+        == pa.PA_ERR_INVALID
+    # B == 0 is a no-op
+    assert pa.lib.pa_decode(pool, None, None, None, 0, None, 0, 32, 0.1, 0, 0, None, 0, None) == pa.PA_OK
+    assert pa.lib.pa_write_kv(pool, None, None, None, 0, None) == pa.PA_OK
+    assert pa.lib.pa_write_kv(pool, dummy, dummy, None, 5, None) == pa.PA_ERR_INVALID
+    assert pa.lib.pa_write_kv(pool, dummy, dummy, dummy, -1, None) == pa.PA_ERR_INVALID
+    pa.pa_free_pool(pool)
+    st, fpool = make_pool(16, 16, hkv=2, d=64, dtype=pa.PA_F32)
+    assert pa.lib.pa_prefill(fpool, dummy, dummy, dummy, dummy, 4, dummy, 2, 4, 16, 0.1, None) \
+        == pa.PA_ERR_UNSUPPORTED
+    pa.pa_free_pool(fpool)
+
+
+# ----------------------------------------------------------- sanitizers
+def _driver_input(nb, bs, order, ops):
+    lines = [f"{nb} {bs} {0 if order is None else nb} " + ("" if order is None else " ".join(map(str, order)))]
+    for op in ops:
+        if op[0] == "append":
+            lines.append(f"a {op[1]} {op[2]}")
+        elif op[0] == "fork":
+            lines.append(f"f {op[1]} {op[2]}")
+        elif op[0] == "free":
+            lines.append(f"x {op[1]}")
+        else:
+            lines.append(f"t {op[1]} {len(op[2])} " + " ".join(map(str, op[2])))
+        lines.append("s")
+    return "\n".join(lines) + "\n"
+
+
+def _model_lines(nb, bs, order, ops):
+    res = run_model(nb, bs, order, ops)
+    lines = []
+    for op, r, s in zip(ops, res[0::2], res[1::2]):
+        if op[0] == "append":
+            lines.append(" ".join([str(r[0])] + [str(x) for x in r[1]]))
+        elif op[0] in ("fork", "free"):
+            lines.append(str(r[0]))
+        else:
+            if r[0] == 0:
+                lines.append(" ".join([str(r[0])] + [str(x) for x in r[1]] +
+                                      [str(x) for row in r[2] for x in row]))
+            else:
+                lines.append(str(r[0]))
+        lines.append(" ".join(map(str, s)))
+    return lines
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_block_manager_under_asan_ubsan(tmp_path):
+    exe = str(tmp_path / "bm_driver")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+           "-I", CSRC, os.path.join(CSRC, "block_manager.cpp"),
+           os.path.join(os.path.dirname(__file__), "bm_driver.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    for seed in range(4):
+        rng = np.random.default_rng(200 + seed)
+        nb, bs = 40, [8, 16, 32][seed % 3]
+        order = rng.permutation(nb).tolist() if seed % 2 else None
+        ops = random_ops(rng, 400)
+        p = subprocess.run([exe], input=_driver_input(nb, bs, order, ops), capture_output=True, text=True,
+                           env=env, timeout=120)
+        assert p.returncode == 0, p.stderr[-3000:]
+        assert p.stdout.strip().splitlines() == _model_lines(nb, bs, order, ops)

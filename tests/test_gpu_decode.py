@@ -1,0 +1,185 @@
+"""GPU parity: KV scatter and paged decode (HIP, through the C ABI) vs the CPU oracle.
+
+Same seeded inputs on both sides. The GPU side builds its pool with the C++
+block manager + the HIP scatter; the oracle side with the Python model + the
+scatter oracle. Checks:
+* block tables and lengths: bit-exact;
+* the scattered pools: bit-exact, including never-written slots, which both
+  sides poison with NaN (so a kernel reading a tail slot or a padded table
+  entry shows up as NaN in its output);
+* decode outputs: bf16 max-abs <= 2e-2 and mean-abs <= 2e-3; fp32 max-abs
+  <= 1e-5 — over the tiny, 8B-GQA and prefix-sharing workloads in full, the
+  long-context workload on sampled sequences, and small ragged shapes
+  spanning several partitions and a ragged tail, G in {1,2,4,8}, D in
+  {64,128}, block_size in {8,16,32}, empty and one-token sequences;
+* invariance of the output under the KV partition size.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle.attention as OA  # noqa: E402
+import workloads as W  # noqa: E402
+from oracle.cache import OracleCache  # noqa: E402
+
+
+def _harness():
+    from paged_kv_cache_indirect_amd import harness
+    return harness
+
+
+TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-5, 1e-5)}
+
+
+def assert_close(got, ref, dtype, what=""):
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    mx, mean = TOL[dtype]
+    print(f"{what}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
+          f"rel_rms={err.max() / max(np.sqrt((ref ** 2).mean()), 1e-30):.3e}", flush=True)
+    assert err.max() <= mx, f"{what}: max abs err {err.max()}"
+    assert err.mean() <= mean, f"{what}: mean abs err {err.mean()}"
+
+
+def widen_out(t, dtype):
+    h = _harness().to_host(t, dtype)
+    return OA.widen(h, dtype)
+
+
+def build_both(wl, only=None):
+    print(f"[build] {wl.name} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} bs={wl.block_size} "
+          f"{wl.dtype} max_len={wl.max_seq_len} nb={wl.num_blocks}", flush=True)
+    gpu = _harness().GpuCache(wl)
+    ora = OracleCache(wl, only=only)
+    assert np.array_equal(gpu.tables_host, ora.block_tables), "block tables differ"
+    assert np.array_equal(gpu.lens_host, ora.seq_lens), "seq_lens differ"
+    return gpu, ora
+
+
+def oracle_out(wl, ora, seqs=None):
+    seqs = list(range(wl.B)) if seqs is None else list(seqs)
+    q = wl.queries()[seqs]
+    out, _ = OA.paged_decode(q, ora.k_cache, ora.v_cache, ora.block_tables[seqs], ora.seq_lens[seqs],
+                             wl.scale, wl.dtype)
+    return out
+
+
+def small(lens, Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", seed=5, **kw):
+    return W.make_decode(f"small{len(lens)}", lens, Hq=Hq, Hkv=Hkv, D=D, block_size=bs, dtype=dtype,
+                         seed=seed, **kw)
+
+
+# ------------------------------------------------------------------ scatter
+@pytest.mark.parametrize("name", ["tiny", "gqa8b", "prefix"])
+def test_write_kv_bit_exact(name):
+    wl = W.config(name)
+    gpu, ora = build_both(wl)
+    hk = _harness().to_host(gpu.k_cache, wl.dtype)
+    hv = _harness().to_host(gpu.v_cache, wl.dtype)
+    assert np.array_equal(hk.view(np.uint8), ora.k_cache.view(np.uint8)), "k_cache differs"
+    assert np.array_equal(hv.view(np.uint8), ora.v_cache.view(np.uint8)), "v_cache differs"
+    gpu.close()
+
+
+def test_write_kv_skips_negative_and_out_of_range_slots():
+    h = _harness()
+    wl = small([20, 9], Hq=2, Hkv=2, D=64, bs=8, dtype="f32")
+    gpu = h.GpuCache(wl)
+    before = h.to_host(gpu.k_cache, "f32").copy()
+    rng = np.random.default_rng(0)
+    k = rng.standard_normal((4, 2, 64)).astype(np.float32)
+    nslots = wl.num_blocks * wl.block_size
+    gpu.write(k, k, np.array([-1, nslots, nslots + 100, -7]))
+    torch.cuda.synchronize()
+    assert np.array_equal(h.to_host(gpu.k_cache, "f32").view(np.uint8), before.view(np.uint8))
+    gpu.close()
+
+
+# ------------------------------------------------------------------- decode
+def test_decode_tiny_fp32():
+    wl = W.config("tiny")
+    gpu, ora = build_both(wl)
+    got = widen_out(gpu.decode(), wl.dtype)
+    assert_close(got, oracle_out(wl, ora), wl.dtype, "tiny")
+    gpu.close()
+
+
+SMALL_CASES = [
+    # lens, Hq, Hkv, D, bs, dtype, partition_tokens
+    ([1, 7, 16, 17, 63, 64, 65, 500, 1025], 8, 2, 128, 16, "bf16", 128),
+    ([0, 1, 300, 2049], 8, 2, 128, 16, "bf16", 512),
+    ([33, 1000, 5], 4, 4, 128, 8, "bf16", 64),
+    ([777, 64, 31], 16, 2, 128, 32, "bf16", 256),
+    ([900, 2, 129], 2, 1, 64, 16, "bf16", 128),
+    ([450, 3, 1], 16, 2, 64, 32, "bf16", 512),
+    ([7, 16, 33, 50, 600], 2, 2, 64, 16, "f32", 64),
+    ([300, 1, 129], 8, 2, 128, 8, "f32", 128),
+    ([1300, 70], 8, 1, 64, 16, "f32", 256),
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,bs,dtype,pt", SMALL_CASES)
+def test_decode_small_shapes(lens, Hq, Hkv, D, bs, dtype, pt):
+    wl = small(lens, Hq, Hkv, D, bs, dtype)
+    gpu, ora = build_both(wl)
+    ws = gpu.workspace_for(pt)
+    got = widen_out(gpu.decode(pt, ws), dtype)
+    assert_close(got, oracle_out(wl, ora), dtype, f"small {lens} G={Hq // Hkv} D={D} bs={bs} pt={pt}")
+    gpu.close()
+
+
+def test_decode_gqa8b_full():
+    wl = W.config("gqa8b")
+    gpu, ora = build_both(wl)
+    ref = oracle_out(wl, ora)
+    for pt in (512, 256, 1024, 2048):
+        ws = gpu.workspace_for(pt)
+        got = widen_out(gpu.decode(pt, ws), wl.dtype)
+        assert_close(got, ref, wl.dtype, f"gqa8b pt={pt}")
+    gpu.close()
+
+
+def test_decode_long_context_sampled():
+    wl = W.config("long")
+    sample = [0, 5]
+    gpu, ora = build_both(wl, only=sample)
+    got = widen_out(gpu.decode(512, gpu.workspace_for(512)), wl.dtype)[sample]
+    assert_close(got, oracle_out(wl, ora, sample), wl.dtype, "long (sampled seqs 0, 5)")
+    gpu.close()
+
+
+def test_decode_prefix_sharing_full():
+    wl = W.config("prefix")
+    gpu, ora = build_both(wl)
+    from paged_kv_cache_indirect_amd import pa_pool_stats
+    st = pa_pool_stats(gpu.pool)
+    assert st["shared_blocks"] == wl.prefix_len // wl.block_size
+    got = widen_out(gpu.decode(512, gpu.workspace_for(512)), wl.dtype)
+    assert_close(got, oracle_out(wl, ora), wl.dtype, "prefix")
+    gpu.close()
+
+
+def test_decode_partition_invariance_and_max_seq_len_slack():
+    from paged_kv_cache_indirect_amd import pa_decode
+    wl = small([1, 40, 511, 512, 513, 1500], Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", seed=9)
+    gpu, ora = build_both(wl)
+    ref = oracle_out(wl, ora)
+    # A table wider than needed (padded with -1) lets the grid be sized for a
+    # longer max_seq_len than any sequence has.
+    wide = torch.full((wl.B, wl.max_blocks + 50), -1, dtype=torch.int32, device="cuda")
+    wide[:, :wl.max_blocks] = gpu.block_tables
+    outs = []
+    for pt in (64, 128, 512, 2048):
+        for slack in (0, 700):
+            msl = wl.max_seq_len + slack
+            out = torch.empty_like(gpu.q)
+            pa_decode(gpu.pool, out, gpu.q, wide, gpu.seq_lens, wl.scale, msl, pt,
+                      gpu.workspace_for(pt, msl))
+            outs.append(widen_out(out, "bf16"))
+            assert_close(outs[-1], ref, "bf16", f"pt={pt} slack={slack}")
+    spread = max(np.abs(o - outs[0]).max() for o in outs)
+    assert spread <= 2e-2
+    gpu.close()

@@ -144,6 +144,9 @@ class Workload:
     def kv_rows(self, seq: int, start: int, n: int) -> Tuple[np.ndarray, np.ndarray]:
         """Logical K/V rows [start, start+n) of ``seq``: arrays [n, Hkv, D]."""
         P = self.prefix_len
+        if n == 0:
+            e = np.empty((0, self.Hkv, self.D), dtype=np.float32 if self.dtype == "f32" else np.uint16)
+            return e, e.copy()
         parts_k, parts_v = [], []
         if start < P:
             pk, pv = self.prefix_kv()
