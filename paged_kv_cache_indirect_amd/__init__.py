@@ -8,7 +8,7 @@ the hipStream_t. Every step of the computation runs in the library's HIP
 kernels and host block manager. If the library is not built, importing this
 package raises: there is no fallback path.
 
-Build it with ``python -m paged_kv_cache_indirect_amd.build`` (or
+Build it with ``python paged_kv_cache_indirect_amd/build.py`` (or
 ``__graft_entry__.build()``).
 """
 from __future__ import annotations
@@ -33,7 +33,7 @@ PA_F32, PA_BF16 = 0, 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_indirect_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python paged_kv_cache_indirect_amd/build.py`")
 
 # One HIP runtime per process: torch ships its own libamdhip64 (soname
 # libamdhip64.so.7, the same as the system one). Loading torch first makes the

@@ -1,6 +1,6 @@
 """Build libpa.so (HIP kernels + host block manager + C ABI) for gfx950, in-tree.
 
-    python -m paged_kv_cache_indirect_amd.build        # or __graft_entry__.build()
+    python paged_kv_cache_indirect_amd/build.py        # or __graft_entry__.build()
 
 Every source is compiled with hipcc for gfx950 with packed-fp32 instruction
 generation disabled, then linked into ``paged_kv_cache_indirect_amd/libpa.so``.
