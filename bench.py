@@ -1,0 +1,381 @@
+#!/usr/bin/env python3
+"""Paged KV-cache attention benchmark on one MI355X.
+
+Workload: 8B-shaped grouped-query decode — 64 sequences, 32 q heads over 8 kv
+heads, head_dim 128, bf16, block_size 16, lengths uniform in [512, 4096]
+(seed 1001), blocks handed out from a shuffled pool of 1.1x the need.
+
+One step is one decode step of that batch, through the C ABI:
+  1. host block manager: every sequence grows by one token
+     (pa_seq_append_batch) and gets its slot;
+  2. table export (pa_block_tables) into pinned host memory, then one
+     host-to-device copy of (slots, seq_lens, block_tables);
+  3. pa_write_kv scatters the step's new K/V rows into the paged pool;
+  4. pa_decode: split-KV paged attention of the step's queries (512-token
+     partitions, merged by log-sum-exp).
+The step's new K/V rows and queries are generated before timing and are
+resident in HBM. W untimed warm-up steps, then K timed steps between two
+device synchronisations.
+
+Printed: one JSON line. ``value`` is the whole-step KV throughput (logical
+K+V bytes the decode must read per step, over the step time). ``roofline``
+is the decode op (partition + merge kernels) timed with HIP events on the
+stream it runs on, against 8 TB/s HBM. ``cpu_baseline`` is the CPU oracle
+(fp64 gather + softmax attention) timed on this host on the same workload.
+``prefill`` is the chunked causal prefill workload (16 x 512-token chunks
+over U[0, 7680] cached tokens, bs 32) timed the same way against the bf16
+MFMA peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode KV GB/s and % of HBM peak; decode tok/s at batch 64, 8B shape"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "device_common.h", "launch.h"],
+    "prefill": ["prefill.hip", "device_common.h", "launch.h"],
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(which: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[which]:
+        with open(os.path.join(ROOT, "paged_kv_cache_indirect_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(which: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"{which}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(which):
+        return None
+    return float(m_bytes.group(1))
+
+
+def decode_bytes(wl, lens) -> int:
+    """Algorithmic bytes of one decode call: K+V rows of every valid token,
+    q and out, the ceil(L / bs) table entries in use, and seq_lens."""
+    import numpy as np
+    L = np.asarray(lens, dtype=np.int64)
+    kv = int(L.sum()) * wl.Hkv * wl.D * 2 * wl.elem_bytes
+    qo = 2 * wl.B * wl.Hq * wl.D * wl.elem_bytes
+    tables = int(((L + wl.block_size - 1) // wl.block_size).sum()) * 4
+    return kv + qo + tables + 4 * wl.B
+
+
+# --------------------------------------------------------------------- decode
+def run_decode(args):
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_indirect_amd import (harness, pa_block_tables, pa_decode,
+                                             pa_decode_workspace_bytes, pa_seq_append_batch,
+                                             pa_write_kv)
+
+    dev = torch.device("cuda:0")
+    wl = W.config("gqa8b")
+    S = args.warmup + args.steps
+    log(f"[bench] building gqa8b cache: B={wl.B} nb={wl.num_blocks} max_len={wl.max_seq_len}")
+    cache = harness.GpuCache(wl, device=dev, poison=False)
+    pool = cache.pool
+    B, Hq, Hkv, D, bs = wl.B, wl.Hq, wl.Hkv, wl.D, wl.block_size
+
+    # Step inputs, resident in HBM before timing.
+    ks, vs, qs = [], [], []
+    for s in range(S):
+        k, v, q = wl.decode_step_inputs(s)
+        ks.append(k); vs.append(v); qs.append(q)
+    k_steps = harness.to_device(np.stack(ks), wl.dtype, dev)    # [S, B, Hkv, D]
+    v_steps = harness.to_device(np.stack(vs), wl.dtype, dev)
+    q_steps = harness.to_device(np.stack(qs), wl.dtype, dev)    # [S, B, Hq, D]
+    out = torch.empty((B, Hq, D), dtype=q_steps.dtype, device=dev)
+
+    # Grid and table width sized once for the longest sequence after S steps.
+    max_len = wl.max_seq_len + S
+    max_blocks = -(-max_len // bs)
+    pt = args.partition_tokens
+    ws_bytes = pa_decode_workspace_bytes(B, Hq, D, max_len, pt)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    # Packed per-step metadata: slots int64 [B] | seq_lens int32 [B] | tables int32 [B, max_blocks].
+    off_lens = 8 * B
+    off_tab = off_lens + 4 * B
+    nbytes = off_tab + 4 * B * max_blocks
+    ring = 2
+    pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
+    dmeta = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(ring)]
+    copied = [torch.cuda.Event() for _ in range(ring)]
+    host_views = []
+    for p in pinned:
+        a = p.numpy()
+        host_views.append((a[:off_lens].view(np.int64), a[off_lens:off_tab].view(np.int32),
+                           a[off_tab:].view(np.int32)))
+    dev_views = [(d[:off_lens].view(torch.int64), d[off_lens:off_tab].view(torch.int32),
+                  d[off_tab:].view(torch.int32).view(B, max_blocks)) for d in dmeta]
+    seq_ids = np.arange(B, dtype=np.int64)
+    stream = torch.cuda.current_stream()
+
+    ev_dec0 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+    ev_dec1 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+    ev_kv0 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+    lens_per_step = []
+
+    def step(s: int) -> None:
+        r = s % ring
+        copied[r].synchronize()                    # pinned[r]'s previous copy has landed
+        slots_h, lens_h, tab_h = host_views[r]
+        pa_seq_append_batch(pool, seq_ids, 1, slots_h)
+        pa_block_tables(pool, seq_ids, max_blocks, tab_h, lens_h)
+        lens_per_step.append(lens_h.copy())
+        dmeta[r].copy_(pinned[r], non_blocking=True)
+        copied[r].record(stream)
+        slots_d, lens_d, tab_d = dev_views[r]
+        ev_kv0[s].record(stream)
+        pa_write_kv(pool, k_steps[s], v_steps[s], slots_d)
+        ev_dec0[s].record(stream)
+        pa_decode(pool, out, q_steps[s], tab_d, lens_d, wl.scale, max_len, pt, workspace)
+        ev_dec1[s].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    log(f"[bench] warm-up done ({args.warmup} steps); timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for s in range(args.warmup, S):
+        step(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] timed decode steps done: {elapsed * 1e3:.2f} ms")
+
+    timed = range(args.warmup, S)
+    dec_ms = [ev_dec0[s].elapsed_time(ev_dec1[s]) for s in timed]
+    kv_ms = [ev_kv0[s].elapsed_time(ev_dec0[s]) for s in timed]
+    step_bytes = [decode_bytes(wl, lens_per_step[s]) for s in timed]
+    step_kv = [int(np.asarray(lens_per_step[s], np.int64).sum()) * Hkv * D * 2 * wl.elem_bytes for s in timed]
+    dec_avg_s = float(np.mean(dec_ms)) * 1e-3
+    achieved = float(np.mean(step_bytes)) / dec_avg_s / 1e9
+    res = {
+        "elapsed_s": elapsed,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "value": sum(step_kv) / elapsed / 1e9,
+        "tok_per_s": B * args.steps / elapsed,
+        "decode_us_mean": float(np.mean(dec_ms)) * 1e3,
+        "decode_us_median": float(np.median(dec_ms)) * 1e3,
+        "decode_us_min": float(np.min(dec_ms)) * 1e3,
+        "write_kv_us_mean": float(np.mean(kv_ms)) * 1e3,
+        "bytes_per_launch": float(np.mean(step_bytes)),
+        "kv_bytes_per_step": float(np.mean(step_kv)),
+        "achieved_gbps": achieved,
+        "mean_len": float(np.mean([np.mean(lens_per_step[s]) for s in timed])),
+        "max_len_bound": max_len,
+        "num_blocks": wl.num_blocks,
+    }
+    cache.close()
+    del cache, k_steps, v_steps, q_steps, workspace, dmeta
+    torch.cuda.empty_cache()
+    return wl, res
+
+
+# -------------------------------------------------------------------- prefill
+def causal_flops(wl) -> float:
+    """4 * D * Hq * sum_b sum_i (ctx_b + i + 1): QK^T and PV over the
+    causally valid (query, key) pairs only."""
+    total = 0
+    for L, n in zip(wl.seq_lens.tolist(), wl.q_lens.tolist()):
+        ctx = L - n
+        total += n * ctx + n * (n + 1) // 2
+    return 4.0 * wl.D * wl.Hq * total
+
+
+def run_prefill(args):
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_indirect_amd import PaError, harness
+
+    dev = torch.device("cuda:0")
+    wl = W.config("prefill")
+    log(f"[bench] building prefill cache: B={wl.B} T={int(wl.q_lens.sum())} nb={wl.num_blocks}")
+    cache = harness.GpuCache(wl, device=dev, poison=False)
+    try:
+        cache.prefill()
+    except PaError as e:
+        cache.close()
+        return wl, {"status": f"unavailable: {e}"}
+    torch.cuda.synchronize()
+    n = args.prefill_iters
+    for _ in range(3):
+        cache.prefill()
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    for i in range(n):
+        e0[i].record(stream)
+        cache.prefill()
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in zip(e0, e1)]
+    flops = causal_flops(wl)
+    t = float(np.mean(ms)) * 1e-3
+    tflops = flops / t / 1e12
+    cache.close()
+    log(f"[bench] prefill: {t * 1e6:.1f} us, {tflops:.1f} TFLOP/s")
+    traffic = measured_traffic("prefill")
+    return wl, {
+        "workload": "16 x 512-token causal chunks over paged context U[0,7680] (seed 1004), "
+                    "Hq 32 / Hkv 8, D 128, bf16, block_size 32",
+        "us_mean": t * 1e6, "us_median": float(np.median(ms)) * 1e3, "us_min": float(np.min(ms)) * 1e3,
+        "tokens_per_s": int(wl.q_lens.sum()) / t,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
+                     "flops_per_launch": flops},
+    }
+
+
+# --------------------------------------------------------------- CPU oracle
+def run_cpu_baseline(args, wl):
+    """The oracle's fp64 paged decode of the same 64-sequence batch (cache as
+    built before the timed steps), repeated for about ``cpu_seconds``."""
+    import numpy as np
+
+    import oracle.attention as OA
+    from oracle.cache import OracleCache
+
+    log("[bench] cpu baseline: building oracle cache")
+    ora = OracleCache(wl, poison=False)
+    q = wl.queries()
+    nbytes = decode_bytes(wl, ora.seq_lens)
+    kv = int(ora.seq_lens.astype(np.int64).sum()) * wl.Hkv * wl.D * 2 * wl.elem_bytes
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:
+        pass
+    reps, t_total = 0, 0.0
+    while reps == 0 or (t_total < args.cpu_seconds and reps < 100):
+        t0 = time.perf_counter()
+        OA.paged_decode(q, ora.k_cache, ora.v_cache, ora.block_tables, ora.seq_lens, wl.scale, wl.dtype)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        log(f"[bench] cpu baseline rep {reps}: {t_total:.1f} s")
+    t = t_total / reps
+    return {
+        "value": kv / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"full 64-sequence decode batch (one step, mean length {float(ora.seq_lens.mean()):.0f}), "
+                  f"fp64 NumPy gather + exact softmax attention, {reps} repetition(s), {t:.2f} s each; "
+                  f"host has {len(os.sched_getaffinity(0))} cores available",
+        "tok_per_s": wl.B / t,
+        "bytes_per_call": nbytes,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--partition-tokens", type=int, default=512)
+    ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(every workload here runs on a single MI355X); run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        return 2
+    import paged_kv_cache_indirect_amd  # noqa: F401  (fails loudly if libpa.so is missing)
+
+    wl, dec = run_decode(args)
+    frac = dec["achieved_gbps"] / HBM_PEAK_GBPS
+    log(f"[bench] decode: {dec['decode_us_mean']:.1f} us/launch, {dec['achieved_gbps']:.0f} GB/s "
+        f"({100 * frac:.1f}% of HBM peak); step {dec['ms_per_step'] * 1e3:.1f} us")
+    pre = None if args.no_prefill else run_prefill(args)[1]
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, wl)
+
+    line = {
+        "metric": METRIC,
+        "value": dec["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "8B-shaped GQA paged decode step: batch 64, 32 q / 8 kv heads, head_dim 128, "
+                        "bf16, block_size 16, lengths U[512,4096] (seed 1001), shuffled pool of 1.1x need; "
+                        "step = block-manager append + table export/H2D + KV scatter + split-KV decode",
+            "global_batch": wl.B,
+            "partition_tokens": args.partition_tokens,
+            "mean_seq_len": dec["mean_len"],
+        },
+        "decode": {
+            "tok_per_s": dec["tok_per_s"],
+            "tok_per_s_8b_32_layers": dec["tok_per_s"] / 32.0,
+            "kernel_us_mean": dec["decode_us_mean"],
+            "kernel_us_median": dec["decode_us_median"],
+            "kernel_us_min": dec["decode_us_min"],
+            "write_kv_us_mean": dec["write_kv_us_mean"],
+            "kv_gbps_kernel": dec["kv_bytes_per_step"] / (dec["decode_us_mean"] * 1e-6) / 1e9,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": dec["achieved_gbps"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": frac,
+            "traffic": measured_traffic("decode"),
+            "kernel": "paged decode (partition + log-sum-exp merge)",
+            "bytes_per_launch": dec["bytes_per_launch"],
+        },
+        "cpu_baseline": cpu,
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

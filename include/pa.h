@@ -110,6 +110,18 @@ void pa_free_pool(pa_pool* pool);
  * Errors: PA_ERR_INVALID (n_tokens < 0, null slots_out, length overflow). */
 pa_status pa_seq_append(pa_pool* pool, int64_t seq_id, int32_t n_tokens, int64_t* slots_out);
 
+/* One decode step's bookkeeping in one call: grow each of the n distinct
+ * sequences seq_ids[0..n) (host) by n_tokens, exactly as n pa_seq_append
+ * calls in that order would, but all-or-nothing over the whole batch: if the
+ * free list cannot cover every new block of the batch, returns
+ * PA_ERR_NO_BLOCKS and changes nothing (admission control,
+ * "vLLM的'内存分页'到底多神奇", §4). slots_out (host, n × n_tokens int64,
+ * may be NULL when n_tokens == 0): row i holds seq_ids[i]'s new slots.
+ * Errors: PA_ERR_INVALID (negative sizes, null pointers, a sequence id twice
+ * in the batch, length overflow). */
+pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seq_ids, int32_t n, int32_t n_tokens,
+                              int64_t* slots_out);
+
 /* Make dst a new sequence that shares all of src's blocks (prefix sharing:
  * same physical blocks, each block's refcount + 1; "vLLM的'内存分页'到底多神奇",
  * §2 and §3 phase 3). Only whole blocks are shared: src's length must be a

@@ -69,6 +69,24 @@ class BlockManagerModel:
         slots = [table[p // bs] * bs + p % bs for p in range(L, L + n)]
         return OK, slots
 
+    def append_batch(self, seqs: Sequence[int], n: int):
+        """Grow every sequence in ``seqs`` by n tokens as one admission
+        decision: either all of them get their pages or nothing changes
+        (same page, §4). Returns (status, [slots of seqs[0], ...])."""
+        seqs = [int(s) for s in seqs]
+        if n < 0 or len(set(seqs)) != len(seqs):
+            return ERR_INVALID, []
+        bs = self.block_size
+        need = sum(-(-(self.lens.get(s, 0) + n) // bs) - len(self.tables.get(s, [])) for s in seqs)
+        if need > len(self.free):
+            return ERR_NO_BLOCKS, []
+        out = []
+        for s in seqs:
+            st, slots = self.append(s, n)
+            assert st == OK
+            out.append(slots)
+        return OK, out
+
     def fork(self, src: int, dst: int) -> int:
         if src not in self.tables:
             return ERR_UNKNOWN_SEQ

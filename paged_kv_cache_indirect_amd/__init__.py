@@ -22,7 +22,7 @@ import numpy as np
 __all__ = [
     "PaError", "PA_OK", "PA_ERR_INVALID", "PA_ERR_NO_BLOCKS", "PA_ERR_UNSUPPORTED", "PA_ERR_HIP",
     "PA_ERR_UNKNOWN_SEQ", "PA_F32", "PA_BF16", "LIB_PATH", "lib",
-    "pa_alloc_pool", "pa_free_pool", "pa_seq_append", "pa_seq_fork", "pa_seq_free",
+    "pa_alloc_pool", "pa_free_pool", "pa_seq_append", "pa_seq_append_batch", "pa_seq_fork", "pa_seq_free",
     "pa_block_tables", "pa_pool_stats", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
     "pa_prefill", "pa_last_error",
 ]
@@ -61,6 +61,7 @@ _SIGS = {
     "pa_alloc_pool": (_i32, [ctypes.POINTER(_Layout), _vp, _vp, _vp, ctypes.POINTER(_vp)]),
     "pa_free_pool": (None, [_vp]),
     "pa_seq_append": (_i32, [_vp, _i64, _i32, _vp]),
+    "pa_seq_append_batch": (_i32, [_vp, _vp, _i32, _i32, _vp]),
     "pa_seq_fork": (_i32, [_vp, _i64, _i64]),
     "pa_seq_free": (_i32, [_vp, _i64]),
     "pa_block_tables": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
@@ -146,6 +147,22 @@ def pa_seq_append(pool: int, seq_id: int, n_tokens: int) -> np.ndarray:
     return slots
 
 
+def pa_seq_append_batch(pool: int, seq_ids, n_tokens: int, slots_out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Grow every sequence in ``seq_ids`` by ``n_tokens`` (all-or-nothing).
+    Returns host int64 slots [n, n_tokens]; ``slots_out`` (a C-contiguous
+    int64 array of that shape) is filled and returned when given."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    n = len(ids)
+    if slots_out is None:
+        slots_out = np.empty((n, max(n_tokens, 0)), dtype=np.int64)
+    elif slots_out.dtype != np.int64 or not slots_out.flags.c_contiguous or slots_out.size < n * max(n_tokens, 0):
+        raise ValueError("slots_out must be a C-contiguous int64 array of n * n_tokens entries")
+    _check(lib.pa_seq_append_batch(pool, ids.ctypes.data, n, n_tokens,
+                                   slots_out.ctypes.data if n_tokens > 0 else None),
+           "pa_seq_append_batch")
+    return slots_out
+
+
 def pa_seq_fork(pool: int, src_seq_id: int, dst_seq_id: int) -> None:
     _check(lib.pa_seq_fork(pool, src_seq_id, dst_seq_id), "pa_seq_fork")
 
@@ -154,12 +171,18 @@ def pa_seq_free(pool: int, seq_id: int) -> None:
     _check(lib.pa_seq_free(pool, seq_id), "pa_seq_free")
 
 
-def pa_block_tables(pool: int, seq_ids: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Returns (tables int32 [n, max_blocks] padded -1, seq_lens int32 [n]) on the host."""
+def pa_block_tables(pool: int, seq_ids: Sequence[int], max_blocks: int, tables_out: Optional[np.ndarray] = None,
+                    lens_out: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Returns (tables int32 [n, max_blocks] padded -1, seq_lens int32 [n]) on the host.
+    ``tables_out`` / ``lens_out`` (C-contiguous int32 of those sizes) are
+    filled in place when given."""
     ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
     n = len(ids)
-    tables = np.empty((n, max_blocks), dtype=np.int32)
-    lens = np.empty(n, dtype=np.int32)
+    tables = np.empty((n, max_blocks), dtype=np.int32) if tables_out is None else tables_out
+    lens = np.empty(n, dtype=np.int32) if lens_out is None else lens_out
+    for a, size in ((tables, n * max_blocks), (lens, n)):
+        if a.dtype != np.int32 or not a.flags.c_contiguous or a.size < size:
+            raise ValueError("tables_out / lens_out must be C-contiguous int32 arrays large enough")
     _check(lib.pa_block_tables(pool, ids.ctypes.data, n, max_blocks, tables.ctypes.data, lens.ctypes.data),
            "pa_block_tables")
     return tables, lens

@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <unordered_set>
 
 namespace pa {
 
@@ -76,6 +77,63 @@ Status BlockManager::Append(int64_t seq, int32_t n, int64_t* slots_out, std::str
   const int64_t bs = block_size_;
   for (int64_t p = old_len; p < new_len; ++p)
     slots_out[p - old_len] = static_cast<int64_t>(s.table[static_cast<size_t>(p / bs)]) * bs + p % bs;
+  return kOk;
+}
+
+Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_tokens,
+                                 int64_t* slots_out, std::string* err) {
+  if (n < 0 || n_tokens < 0) {
+    *err = "n and n_tokens must be >= 0";
+    return kErrInvalid;
+  }
+  if (n == 0) return kOk;
+  if (!seqs || (n_tokens > 0 && !slots_out)) {
+    *err = "null pointer argument";
+    return kErrInvalid;
+  }
+  // Validate the whole batch and count its new blocks before any mutation.
+  std::unordered_set<int64_t> seen;
+  seen.reserve(static_cast<size_t>(n));
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!seen.insert(seqs[i]).second) {
+      *err = "sequence " + std::to_string(seqs[i]) + " appears twice in the batch";
+      return kErrInvalid;
+    }
+    auto it = seqs_.find(seqs[i]);
+    const int64_t old_len = it == seqs_.end() ? 0 : it->second.len;
+    const int64_t have = it == seqs_.end() ? 0 : static_cast<int64_t>(it->second.table.size());
+    if (old_len + n_tokens > static_cast<int64_t>(INT32_MAX)) {
+      *err = "sequence length would exceed INT32_MAX";
+      return kErrInvalid;
+    }
+    need += CeilDiv(old_len + n_tokens, block_size_) - have;
+  }
+  if (need > static_cast<int64_t>(free_.size())) {
+    *err = "not enough free blocks for the batch: need " + std::to_string(need) + ", have " +
+           std::to_string(free_.size());
+    return kErrNoBlocks;
+  }
+  // New sequences are created before any block moves, so an allocation
+  // failure here leaves the pool unchanged apart from empty entries, which
+  // are removed again.
+  std::vector<int64_t> created;
+  try {
+    for (int32_t i = 0; i < n; ++i)
+      if (seqs_.emplace(seqs[i], Seq{}).second) created.push_back(seqs[i]);
+    for (int32_t i = 0; i < n; ++i) {
+      Seq& s = seqs_.find(seqs[i])->second;
+      s.table.reserve(static_cast<size_t>(CeilDiv(s.len + n_tokens, block_size_)));
+    }
+  } catch (...) {
+    for (int64_t id : created) seqs_.erase(id);
+    throw;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    std::string unused;
+    Append(seqs[i], n_tokens, slots_out ? slots_out + static_cast<int64_t>(i) * n_tokens : nullptr,
+           &unused);  // cannot fail: validated and reserved above
+  }
   return kOk;
 }
 

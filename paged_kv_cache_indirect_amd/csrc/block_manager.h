@@ -55,6 +55,10 @@ class BlockManager {
                          std::string* err);
 
   Status Append(int64_t seq, int32_t n, int64_t* slots_out, std::string* err);
+  // n_tokens more tokens for each of n distinct sequences, all-or-nothing over
+  // the whole batch. slots_out: n × n_tokens, row i for seqs[i].
+  Status AppendBatch(const int64_t* seqs, int32_t n, int32_t n_tokens, int64_t* slots_out,
+                     std::string* err);
   Status Fork(int64_t src, int64_t dst, std::string* err);
   Status Free(int64_t seq, std::string* err);
   Status ExportTables(const int64_t* seqs, int32_t n, int32_t max_blocks, int32_t* tables,

@@ -113,6 +113,15 @@ pa_status pa_seq_append(pa_pool* pool, int64_t seq_id, int32_t n_tokens, int64_t
   });
 }
 
+pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seq_ids, int32_t n, int32_t n_tokens,
+                              int64_t* slots_out) {
+  return Guard([&]() -> pa_status {
+    if (!pool) return Fail(PA_ERR_INVALID, "null pool");
+    std::string err;
+    return FromBm(pool->bm.AppendBatch(seq_ids, n, n_tokens, slots_out, &err), err);
+  });
+}
+
 pa_status pa_seq_fork(pa_pool* pool, int64_t src_seq_id, int64_t dst_seq_id) {
   return Guard([&]() -> pa_status {
     if (!pool) return Fail(PA_ERR_INVALID, "null pool");

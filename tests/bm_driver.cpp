@@ -3,7 +3,8 @@
 // prints every result, so the tests can compare it with the Python model.
 //
 // Input:  nb bs k order[0..k)   (k = 0: ascending order)
-//         then lines: a <seq> <n> | f <src> <dst> | x <seq> | t <mb> <n> <ids...> | s
+//         then lines: a <seq> <n> | b <n_tokens> <n> <ids...> | f <src> <dst> | x <seq> |
+//                     t <mb> <n> <ids...> | s
 // Output: one line per op.
 #include <cstdio>
 #include <string>
@@ -33,6 +34,21 @@ int main() {
       std::printf("%d", st);
       if (st == 0)
         for (int64_t s : slots) std::printf(" %lld", static_cast<long long>(s));
+      std::printf("\n");
+    } else if (op[0] == 'b') {
+      int nt, n;
+      std::scanf("%d %d", &nt, &n);
+      std::vector<int64_t> ids(static_cast<size_t>(n));
+      for (int i = 0; i < n; ++i) {
+        long long v;
+        std::scanf("%lld", &v);
+        ids[static_cast<size_t>(i)] = v;
+      }
+      std::vector<int64_t> slots(static_cast<size_t>(n) * (nt > 0 ? nt : 0) + 1);
+      int st = bm.AppendBatch(ids.data(), n, nt, slots.data(), &err);
+      std::printf("%d", st);
+      if (st == 0)
+        for (int i = 0; i < n * nt; ++i) std::printf(" %lld", static_cast<long long>(slots[static_cast<size_t>(i)]));
       std::printf("\n");
     } else if (op[0] == 'f') {
       long long a, b;

@@ -53,8 +53,15 @@ def random_ops(rng, n_ops, max_seqs=10, max_tokens=80):
     for _ in range(n_ops):
         r = rng.random()
         s = int(rng.integers(0, max_seqs))
-        if r < 0.5:
+        if r < 0.4:
             ops.append(("append", s, int(rng.integers(0, max_tokens))))
+        elif r < 0.5:
+            # a batch of distinct sequences (sometimes a repeated id: rejected)
+            k = int(rng.integers(0, 5))
+            ids = [int(x) for x in rng.choice(max_seqs + 2, size=k, replace=False)]
+            if k and rng.random() < 0.1:
+                ids.append(ids[0])
+            ops.append(("batch", int(rng.integers(0, max_tokens // 3)), ids))
         elif r < 0.7:
             ops.append(("fork", s, int(rng.integers(0, max_seqs))))
         elif r < 0.9:
@@ -71,6 +78,9 @@ def run_model(nb, bs, order, ops):
         if op[0] == "append":
             st, slots = m.append(op[1], op[2])
             out.append((st, list(slots)))
+        elif op[0] == "batch":
+            st, slots = m.append_batch(op[2], op[1])
+            out.append((st, [x for row in slots for x in row]))
         elif op[0] == "fork":
             out.append((m.fork(op[1], op[2]),))
         elif op[0] == "free":
@@ -91,6 +101,11 @@ def run_abi(pool, ops):
             slots = np.empty(max(op[2], 1), dtype=np.int64)
             st = pa.lib.pa_seq_append(pool, op[1], op[2], slots.ctypes.data)
             out.append((st, slots[:op[2]].tolist() if st == 0 else []))
+        elif op[0] == "batch":
+            ids = np.array(op[2], dtype=np.int64)
+            slots = np.empty(max(len(ids) * op[1], 1), dtype=np.int64)
+            st = pa.lib.pa_seq_append_batch(pool, ids.ctypes.data, len(ids), op[1], slots.ctypes.data)
+            out.append((st, slots[:len(ids) * op[1]].tolist() if st == 0 else []))
         elif op[0] == "fork":
             out.append((pa.lib.pa_seq_fork(pool, op[1], op[2]),))
         elif op[0] == "free":
@@ -166,6 +181,27 @@ def test_exhaustion_is_atomic_and_no_leaks():
     pa.pa_free_pool(pool)
 
 
+def test_append_batch_is_all_or_nothing():
+    st, pool = make_pool(10, 16)
+    pa.pa_seq_append(pool, 1, 16)                          # 1 block, full
+    before = pa.pa_pool_stats(pool)
+    with pytest.raises(pa.PaError) as e:                   # needs 1 + 5 + 5 = 11 > 9
+        pa.pa_seq_append_batch(pool, [1, 2, 3], 80)
+    assert e.value.status == pa.PA_ERR_NO_BLOCKS
+    assert pa.pa_pool_stats(pool) == before
+    with pytest.raises(pa.PaError):
+        pa.pa_block_tables(pool, [2], 8)                   # not created
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_seq_append_batch(pool, [1, 1], 1)
+    assert e.value.status == pa.PA_ERR_INVALID
+    slots = pa.pa_seq_append_batch(pool, [1, 2, 3], 1)     # 3 new blocks: 1 crosses, 2/3 are new
+    assert slots.shape == (3, 1)
+    t, l = pa.pa_block_tables(pool, [1, 2, 3], 4)
+    assert l.tolist() == [17, 1, 1]
+    assert slots[:, 0].tolist() == [t[0, 1] * 16, t[1, 0] * 16, t[2, 0] * 16]
+    pa.pa_free_pool(pool)
+
+
 def test_alloc_pool_rejects_bad_geometry():
     assert make_pool(10, 12)[0] == pa.PA_ERR_UNSUPPORTED       # block_size 12
     assert make_pool(10, 16, d=96)[0] == pa.PA_ERR_UNSUPPORTED  # head_dim 96
@@ -220,6 +256,8 @@ def _driver_input(nb, bs, order, ops):
     for op in ops:
         if op[0] == "append":
             lines.append(f"a {op[1]} {op[2]}")
+        elif op[0] == "batch":
+            lines.append(f"b {op[1]} {len(op[2])} " + " ".join(map(str, op[2])))
         elif op[0] == "fork":
             lines.append(f"f {op[1]} {op[2]}")
         elif op[0] == "free":
@@ -234,7 +272,7 @@ def _model_lines(nb, bs, order, ops):
     res = run_model(nb, bs, order, ops)
     lines = []
     for op, r, s in zip(ops, res[0::2], res[1::2]):
-        if op[0] == "append":
+        if op[0] in ("append", "batch"):
             lines.append(" ".join([str(r[0])] + [str(x) for x in r[1]]))
         elif op[0] in ("fork", "free"):
             lines.append(str(r[0]))

@@ -46,7 +46,7 @@ __all__ = [
 ]
 
 # Tags that separate the independent random streams of one workload.
-_TAG_LENS, _TAG_PERM, _TAG_KV, _TAG_Q, _TAG_PREFIX = 0, 1, 2, 3, 4
+_TAG_LENS, _TAG_PERM, _TAG_KV, _TAG_Q, _TAG_PREFIX, _TAG_STEP = 0, 1, 2, 3, 4, 5
 
 
 def _rng(seed: int, tag: int, index: int = 0) -> np.random.Generator:
@@ -177,6 +177,16 @@ class Workload:
     def queries(self) -> np.ndarray:
         """Decode: [B, Hq, D]; prefill: [sum(q_lens), Hq, D] (sequence-major)."""
         return draw_values(_rng(self.seed, _TAG_Q, 0), (self.num_q_rows, self.Hq, self.D), self.dtype)
+
+    def decode_step_inputs(self, step: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Inputs of decode step ``step`` after the cache is built: the new
+        token's K and V rows of every sequence ([B, Hkv, D] each) and the
+        step's queries ([B, Hq, D])."""
+        rng = _rng(self.seed, _TAG_STEP, step)
+        k = draw_values(rng, (self.B, self.Hkv, self.D), self.dtype)
+        v = draw_values(rng, (self.B, self.Hkv, self.D), self.dtype)
+        q = draw_values(rng, (self.B, self.Hq, self.D), self.dtype)
+        return k, v, q
 
     def cu_q_lens(self) -> np.ndarray:
         assert self.q_lens is not None
