@@ -17,7 +17,9 @@ Readings where the pages are silent (each listed in the design doc):
 * K and V are two pools with the same layout, indexed by the same block id;
 * softmax is the exact two-pass form (max, then sum) in fp64;
 * chunked prefill: query row i of a chunk of length n over a cache of length
-  L sits at absolute position L - n + i and attends to tokens 0..L-n+i;
+  L sits at absolute position L - n + i and attends to tokens 0..L-n+i
+  (none when that position is negative, i.e. the chunk is longer than the
+  cache: zero output);
 * an empty sequence (L = 0) yields a zero output and log-sum-exp -inf.
 """
 from __future__ import annotations
@@ -143,7 +145,8 @@ def paged_prefill(q: np.ndarray, cu_q_lens: np.ndarray, k_cache: np.ndarray, v_c
             qi = widen(q[r0 + i], dtype)
             for h in range(Hq):
                 g = h // G
-                out[r0 + i, h], lse[r0 + i, h] = attend(qi[h], K[:pos + 1, g, :], V[:pos + 1, g, :], scale)
+                kv = max(pos + 1, 0)   # a row before the cache start sees no keys
+                out[r0 + i, h], lse[r0 + i, h] = attend(qi[h], K[:kv, g, :], V[:kv, g, :], scale)
     return out, lse
 
 

@@ -325,6 +325,21 @@ def test_prefill_last_row_equals_decode():
         np.testing.assert_allclose(out[cu[b + 1] - 1], dout[b], rtol=0, atol=TOL)
 
 
+def test_prefill_rows_before_cache_start_are_empty():
+    # A chunk of 6 rows over a cache of 4 tokens: rows 0 and 1 sit at
+    # positions -2 and -1 and see no keys; row 2 sees token 0 only, so its
+    # output is V[0] exactly; the last row sees all 4 tokens.
+    rng = np.random.default_rng(11)
+    Ks, Vs, q, kp, vp, tables, lens, cu = prefill_case(rng, [0], [4], 2, 1, 8, 8)   # L = 4
+    q6 = rng.standard_normal((6, 2, 8)).astype(np.float32)
+    out, lse = OA.paged_prefill(q6, np.array([0, 6]), kp, vp, tables, lens, 0.5, "f32")
+    assert np.array_equal(out[:2], np.zeros((2, 2, 8))) and np.all(lse[:2] == -np.inf)
+    np.testing.assert_array_equal(out[2, :, :], np.repeat(Vs[0][0:1, 0, :].astype(np.float64), 2, 0))
+    ref = sdpa_masked(q6[5:6].astype(np.float64), Ks[0].astype(np.float64), Vs[0].astype(np.float64),
+                      0.5, np.ones((1, 4), bool))
+    np.testing.assert_allclose(out[5], ref[0], rtol=0, atol=TOL)
+
+
 def test_prefill_rows_subset_matches_full():
     rng = np.random.default_rng(10)
     Ks, Vs, q, kp, vp, tables, lens, cu = prefill_case(rng, [10, 4], [6, 9], 4, 2, 16, 16)
