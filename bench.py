@@ -120,7 +120,7 @@ def run_decode(args):
     max_blocks = -(-max_len // bs)
     pt = args.partition_tokens
     ws_bytes = pa_decode_workspace_bytes(B, Hq, D, max_len, pt)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     # Packed per-step metadata: slots int64 [B] | seq_lens int32 [B] | tables int32 [B, max_blocks].
     off_lens = 8 * B

@@ -163,10 +163,12 @@ pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
 pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value,
                       const int64_t* slot_mapping, int32_t T, void* stream);
 
-/* Bytes of device workspace pa_decode needs for this shape: fp32 partial
- * states of ceil(max_seq_len / partition_tokens) KV partitions per (sequence,
- * q head). 0 when a single partition covers max_seq_len. partition_tokens 0
- * means the default (512). Returns 0 for invalid arguments. */
+/* Bytes of device workspace pa_decode needs for this shape: long contexts
+ * are split into KV partitions of partition_tokens tokens, and when a
+ * sequence spans more than one, the workspace holds the fp32 partial state
+ * (max, sum, Σ weight·V) of every (sequence, q head, partition). 0 when one
+ * partition covers max_seq_len. partition_tokens 0 means the default (512).
+ * Returns 0 for invalid arguments. */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_seq_len, int32_t partition_tokens);
 
@@ -183,10 +185,13 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
  *   max_seq_len ≤ max_blocks × block_size.
  * partition_tokens: long contexts are split into KV partitions of this many
  *   tokens, each reduced to (max, sum, Σ weight·V), then merged by
- *   log-sum-exp. 0 = 512. Must be a multiple of 64, at most 2048, with
- *   partition_tokens × G ≤ 8192 (else PA_ERR_UNSUPPORTED).
- * workspace (device) of workspace_bytes ≥ pa_decode_workspace_bytes(...);
- *   may be NULL when that is 0.
+ *   log-sum-exp (a second launch, only when some sequence spans more than
+ *   one partition). 0 = 512. Must be a multiple of 64, at most 2048 (else
+ *   PA_ERR_UNSUPPORTED).
+ * workspace (device, 16-byte aligned, contents irrelevant) of
+ *   workspace_bytes ≥ pa_decode_workspace_bytes(...); may be NULL when that
+ *   is 0. Calls that may run concurrently (different streams) need separate
+ *   workspaces.
  * L = 0 gives a zero output row.
  * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
 pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* block_tables,

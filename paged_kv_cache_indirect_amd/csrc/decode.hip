@@ -8,33 +8,41 @@
 // §3.3). Grouped-query heads: q head h reads kv head h / G.
 //
 // How (MI355X-first; the pages' own kernel design is CUDA prior art):
-//  * Decode is a GEMV per head group: every K/V byte is used for G FMAs. It is
-//    HBM-bound, so it runs on VALU (no MFMA) and is organised around bytes in
-//    flight, not flops.
-//  * Pass 1 (PartitionKernel): one workgroup per (sequence, kv head, KV
-//    partition of partition_tokens tokens). The G q heads of the group share
-//    every K/V row read. 4 waves split the partition into 4 token ranges.
-//    Within a wave, 8 lanes cover one 256-byte K/V row with 16-byte loads (8
-//    rows per load instruction, each half-row a full 128-byte line), so each
-//    load instruction is fully coalesced. The wave's block ids are fetched
-//    once (one lane per table entry) and broadcast per 8-row step with
-//    v_readlane into SGPRs, keeping the table lookup off the per-row chain.
-//  * q·k: v_dot2_f32_bf16 (bf16 pairs, fp32 accumulate) then a 3-step DPP sum
-//    over the 8 lanes of a row. Scores (in log2 units) go to LDS; the wave
-//    takes the exact max of its range, turns scores into weights
-//    2^(s - m) with one exp per (token, head), and sums them.
-//  * P·V: fp32 FMAs of the weights into per-lane accumulators, reduced
-//    across the wave's row groups (DPP + shuffles), then across the 4 waves
-//    with a log-sum-exp rescale through LDS.
-//  * A sequence that fits in one partition writes its normalised output
-//    directly. Longer ones write fp32 partial states (max, sum, Σ w·V) and
-//    pass 2 (MergeKernel) combines them: out = Σ 2^(m_p - M) acc_p /
-//    Σ 2^(m_p - M) l_p.
-//  * Work items are mapped XCD-major: consecutive hardware workgroup ids go to
-//    different XCDs, so item = (wg % 8) * per_xcd + wg / 8 gives each XCD a
-//    contiguous run of items ordered (kv head, sequence, partition). With
-//    Hkv = 8 each XCD owns one kv head; shared prefix blocks of a head are
-//    then re-read from one XCD's L2 instead of eight.
+//  * Decode is a GEMV per head group: each K/V byte feeds G multiply-adds. It
+//    is bandwidth-shaped, so it runs on VALU (no MFMA). Measured on MI355X, a
+//    read-only gather of this access pattern reaches ~5.3 TB/s while the math
+//    of a straightforward kernel costs more than the loads: the design is
+//    about VALU instructions per byte as much as about bytes in flight.
+//  * A workgroup of 4 waves owns one KV partition (partition_tokens tokens)
+//    of one (sequence, kv head); each wave streams a quarter of it, K and V
+//    together in a single pass. Eight lanes cover one D-element row with
+//    16-byte loads (one load instruction fetches 8 whole rows); the loads of
+//    a batch of steps are issued together, then consumed.
+//  * The block ids of the wave's range (at most 64) are loaded once, one per
+//    lane, and broadcast per step with v_readlane (an SGPR), so the table
+//    lookup is off the per-row dependency chain — the extra indirection
+//    paging adds ("LLM推理优化", §2.2) costs one readlane per 8 rows.
+//  * Each 8-lane row group keeps its own online-softmax state (running max,
+//    sum, Σ w·V for the G heads). q·k: v_dot2_f32_bf16 plus a 3-step DPP sum.
+//    Weights: one exp2 per (token, head) on scores pre-scaled to log2 units;
+//    the running max is raised lazily (only when exceeded by more than 8),
+//    so rescaling the accumulators is rare and weights stay ≤ 2^8.
+//  * w·V for bf16 caches: two consecutive rows of a lane are interleaved per
+//    element with v_perm and contracted with v_dot2_f32_bf16 against the two
+//    weights rounded to bf16 (fp32 accumulate) — half the instructions of
+//    unpack + FMA. fp32 caches use plain FMAs.
+//  * At the end the 8 row groups of a wave merge by DPP/shuffles and the 4
+//    waves through LDS, by log-sum-exp. A sequence that fits in one partition
+//    writes its output directly; otherwise every partition writes its partial
+//    state (max, sum, Σ w·V) and a second, small kernel merges them by
+//    log-sum-exp, one wave per (sequence, q head). (Merging inside the first
+//    kernel through an arrival counter needs an agent-scope release/acquire
+//    per partition — an L2 writeback and invalidate per workgroup on this
+//    chip — which measured far slower than one extra launch.)
+//  * Work items are mapped XCD-major with the kv head outermost: consecutive
+//    hardware workgroup ids go to different XCDs, so each XCD owns a
+//    contiguous range (one kv head when Hkv = 8) and a shared prefix block of
+//    that head is re-read from one XCD's L2.
 #include "device_common.h"
 #include "launch.h"
 
@@ -42,17 +50,25 @@ namespace pa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                 // waves per workgroup (one partition)
+constexpr int kThreads = 64 * kWaves;
 constexpr int kLanesPerRow = 8;
-constexpr int kRowsPerStep = 64 / kLanesPerRow;  // tokens per wave per load step
+constexpr int kRowsPerStep = 64 / kLanesPerRow;
+constexpr float kLazyMax = 8.f;
+// Running-max start value: finite, so exp2(x - m) needs no -inf guard, and
+// far below any score, so the first real score always raises it.
+constexpr float kMaxInit = -1.0e30f;
 
 template <typename T, int D>
 struct RowGeom {
   static constexpr int kElemPerChunk = 16 / static_cast<int>(sizeof(T));
-  static constexpr int kChunks = D * static_cast<int>(sizeof(T)) / 16;
-  static constexpr int kChunksPerLane = kChunks / kLanesPerRow;  // 1, 2 or 4
+  static constexpr int kChunks = D * static_cast<int>(sizeof(T)) / 16;     // 16-byte chunks per row
+  static constexpr int kChunksPerLane = kChunks / kLanesPerRow;            // 1, 2 or 4
   static constexpr int kElemPerLane = kChunksPerLane * kElemPerChunk;
+  // Steps (8 rows each) whose loads are issued together: 8 KiB of K+V per
+  // wave at 256-byte rows. The kernel is bound by VALU issue rather than by
+  // bytes in flight, so 3 waves per SIMD beat deeper batches at 2 waves.
+  static constexpr int kStepsInFlight = kChunksPerLane == 1 ? 4 : 2;
   static_assert(kChunks % kLanesPerRow == 0, "row must split into 8 lanes of 16-byte chunks");
 };
 
@@ -79,16 +95,38 @@ __device__ __forceinline__ float chunk_dot(const uint4& k, const uint4& q, float
   return acc;
 }
 
-// Unpack one 16-byte chunk of V to fp32.
-__device__ __forceinline__ void chunk_unpack(const uint4& v, float* o, uint16_t) {
-  o[0] = bf16lo(v.x); o[1] = bf16hi(v.x);
-  o[2] = bf16lo(v.y); o[3] = bf16hi(v.y);
-  o[4] = bf16lo(v.z); o[5] = bf16hi(v.z);
-  o[6] = bf16lo(v.w); o[7] = bf16hi(v.w);
+__device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) {  // (x.lo, y.lo)
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
 }
-__device__ __forceinline__ void chunk_unpack(const uint4& v, float* o, float) {
-  o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
-  o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+__device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {  // (x.hi, y.hi)
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t r;
+  r.x = static_cast<__bf16>(lo);
+  r.y = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// acc[e] += w0 * V0[e] + w1 * V1[e] over one 16-byte chunk of two V rows.
+// bf16: the two rows are interleaved per element with v_perm and contracted
+// with v_dot2_f32_bf16 against (w0, w1) rounded to bf16; fp32: two FMAs.
+__device__ __forceinline__ void pv_pair(const uint4& v0, const uint4& v1, uint32_t wpk, float, float,
+                                        float* acc, uint16_t) {
+  const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w};
+  const uint32_t b[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    acc[2 * k] = dot2_bf16(perm_lo(a[k], b[k]), wpk, acc[2 * k]);
+    acc[2 * k + 1] = dot2_bf16(perm_hi(a[k], b[k]), wpk, acc[2 * k + 1]);
+  }
+}
+__device__ __forceinline__ void pv_pair(const uint4& v0, const uint4& v1, uint32_t, float w0, float w1,
+                                        float* acc, float) {
+  const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w};
+  const uint32_t b[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = fmaf(w1, __uint_as_float(b[k]), fmaf(w0, __uint_as_float(a[k]), acc[k]));
 }
 
 __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
@@ -96,51 +134,49 @@ __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void PartitionKernel(
+__global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ kc,
     const T* __restrict__ vc, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ ws, int32_t B, int32_t Hkv,
-    int32_t max_blocks, int32_t bs, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml, int32_t B, int32_t Hkv,
+    int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
     int32_t P, int32_t per_xcd, float scale_log2) {
   using RG = RowGeom<T, D>;
   constexpr int CPL = RG::kChunksPerLane;
   constexpr int EPC = RG::kElemPerChunk;
   constexpr int EPL = RG::kElemPerLane;
-  extern __shared__ float lds[];
+  constexpr int U = RG::kStepsInFlight;  // even: steps are consumed in pairs
+  static_assert(U % 2 == 0, "steps are consumed in pairs");
+  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float s_ml[kWaves][G][2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane >> 3;  // row within a load step
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int r = lane >> 3;  // row within a step
   const int j = lane & 7;   // lane within the row
 
-  // XCD-major work mapping.
+  // ---- work item (XCD-major; kv head, then sequence, then partition)
   const int wg = blockIdx.x;
   const int item = (wg & 7) * per_xcd + (wg >> 3);
-  if (item >= P * B * Hkv) return;
+  if (item >= Hkv * B * P) return;
   const int p = item % P;
   const int bg = item / P;
   const int b = bg % B;
   const int g = bg / B;
+  const int Hq = Hkv * G;
 
   int L = seq_lens[b];
   L = min(max(L, 0), max_seq_len);
-  const int p0 = p * PT;
-  if (p > 0 && p0 >= L) return;
-  const int p1 = min(p0 + PT, L);
-  const int Pb = max(1, (L + PT - 1) / PT);
-  const int Hq = Hkv * G;
+  const int Pb = max(1, (L + PT - 1) / PT);  // partitions of this sequence
+  if (p >= Pb) return;
 
-  const int TPW = PT / kWaves;  // tokens per wave (multiple of 16)
-  const int w0 = p0 + w * TPW;
-  const int ntok = max(0, min(w0 + TPW, p1) - w0);
+  const int TPW = PT / kWaves;               // tokens per wave (a multiple of 16)
+  const int w0 = p * PT + w * TPW;
+  const int ntok = max(0, min(w0 + TPW, L) - w0);
   const int nsteps = (ntok + kRowsPerStep - 1) / kRowsPerStep;
 
-  float* s_lds = lds + w * TPW * G;                   // [TPW][G] this wave's scores / weights
-  float* m_acc = lds + PT * G;                         // [4][G][D]
-  float* m_ml = m_acc + kWaves * G * D;                // [4][G][2]
-
-  // q fragments: this lane's chunks (j, j+8, ...) of the G heads.
+  // q fragments: this lane's chunks (j, j + 8, ...) of the G heads.
   uint4 qf[G][CPL];
   {
     const T* qb = q + (static_cast<int64_t>(b) * Hq + g * G) * D;
@@ -151,148 +187,124 @@ __global__ __launch_bounds__(kThreads) void PartitionKernel(
         qf[h][i] = *reinterpret_cast<const uint4*>(qb + h * D + (j + kLanesPerRow * i) * EPC);
   }
 
-  // Block ids of this wave's token range: lane x holds logical block lb0 + x.
-  const int lb0 = w0 / bs;
+  // Block ids of the wave's range (at most 64): lane x holds logical block lb0 + x.
+  // Steps start on multiples of 8 tokens and block sizes are multiples of 8,
+  // so the 8 rows of one step always sit in one block.
+  const int bs = 1 << bs_shift;
+  const int32_t* trow = tables + static_cast<int64_t>(b) * max_blocks;
+  const int lb0 = w0 >> bs_shift;
+  const int lb_end = (w0 + ntok + bs - 1) >> bs_shift;
   int my_blk = 0;
-  {
-    const int nlb = (TPW + bs - 1) / bs + 1;
-    const int lb = lb0 + lane;
-    if (lane < nlb && lb < max_blocks)
-      my_blk = clamp_block(tables[static_cast<int64_t>(b) * max_blocks + lb], num_blocks);
-  }
+  if (lb0 + lane < lb_end) my_blk = clamp_block(trow[lb0 + lane], num_blocks);
 
   const int64_t row_stride = static_cast<int64_t>(Hkv) * D;  // elements between slots
-  const T* kbase = kc + static_cast<int64_t>(g) * D;
-  const T* vbase = vc + static_cast<int64_t>(g) * D;
+  const T* kbase = kc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
+  const T* vbase = vc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
 
-  // ---------------- pass over K: scores (log2 units) to LDS, running max.
-  float mrun[G];
+  float m[G], l[G], acc[G][EPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) mrun[h] = -INFINITY;
-
-  constexpr int U = 4;  // load steps in flight per lane
-  for (int st0 = 0; st0 < nsteps; st0 += U) {
-    uint4 kf[U][CPL];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int st = st0 + u;
-      if (st < nsteps) {
-        const int tok = w0 + st * kRowsPerStep;
-        const int blk = __builtin_amdgcn_readlane(my_blk, tok / bs - lb0);
-        const int64_t slot = static_cast<int64_t>(blk) * bs + (tok % bs) + r;
-        const T* row = kbase + slot * row_stride;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-          kf[u][i] = *reinterpret_cast<const uint4*>(row + (j + kLanesPerRow * i) * EPC);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int st = st0 + u;
-      if (st < nsteps) {
-        const int t = st * kRowsPerStep + r;  // token index within the wave range
-        float s[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float a = 0.f;
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) a = chunk_dot(kf[u][i], qf[h][i], a, T{});
-          s[h] = sum8(a);
-        }
-        const bool valid = t < ntok;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          s[h] = valid ? s[h] * scale_log2 : -INFINITY;
-          mrun[h] = fmaxf(mrun[h], s[h]);
-        }
-        if (j == 0) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) s_lds[t * G + h] = s[h];
-        }
-      }
-    }
-  }
-
-  // Wave max per head; an all-empty range keeps m = -inf and uses 0 as shift.
-  float m[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) m[h] = max_over_groups8(mrun[h]);
-
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // ---------------- weights: one exp per (token, head); lane handles head lane % G.
-  float msel = m[0];
-#pragma unroll
-  for (int h = 1; h < G; ++h) msel = (lane % G == h) ? m[h] : msel;
-  const float mshift = (msel == -INFINITY) ? 0.f : msel;
-  float lsum = 0.f;
-  const int nent = nsteps * kRowsPerStep * G;
-  for (int e = lane; e < nent; e += 64) {
-    const float pw = fast_exp2(s_lds[e] - mshift);
-    s_lds[e] = pw;
-    lsum += pw;
-  }
-#pragma unroll
-  for (int x = G; x < 64; x <<= 1) lsum += __shfl_xor(lsum, x);  // lane l: sum of head l % G
-
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // ---------------- pass over V: acc[h][e] += w[t][h] * V[t][e].
-  float acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    m[h] = kMaxInit;
+    l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-
-  for (int st0 = 0; st0 < nsteps; st0 += U) {
-    uint4 vf[U][CPL];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int st = st0 + u;
-      if (st < nsteps) {
-        const int tok = w0 + st * kRowsPerStep;
-        const int blk = __builtin_amdgcn_readlane(my_blk, tok / bs - lb0);
-        const int64_t slot = static_cast<int64_t>(blk) * bs + (tok % bs) + r;
-        const T* row = vbase + slot * row_stride;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-          vf[u][i] = *reinterpret_cast<const uint4*>(row + (j + kLanesPerRow * i) * EPC);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int st = st0 + u;
-      if (st < nsteps) {
-        const int t = st * kRowsPerStep + r;
-        float pw[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) pw[h] = s_lds[t * G + h];
-        float v[EPL];
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) chunk_unpack(vf[u][i], v + i * EPC, T{});
-        if ((st + 1) * kRowsPerStep > ntok && t >= ntok) {
-          // Rows past the sequence end in its last block hold stale data.
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) v[e] = 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pw[h], v[e], acc[h][e]);
-      }
-    }
   }
 
-  // Reduce the 8 row groups of the wave; lanes 0..7 keep the wave's result.
+  uint4 kb[U][CPL];
+  uint4 vb[U][CPL];
+  auto issue = [&](int st, int u) {
+    const int tok = w0 + st * kRowsPerStep;
+    const int lb = tok >> bs_shift;
+    const int blk = __builtin_amdgcn_readlane(my_blk, lb - lb0);
+    const int64_t slot0 = (static_cast<int64_t>(blk) << bs_shift) + (tok & (bs - 1));
+    const T* krow = kbase + slot0 * row_stride;
+    const T* vrow = vbase + slot0 * row_stride;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = sum_over_groups8(acc[h][e]);
+    for (int i = 0; i < CPL; ++i) {
+      kb[u][i] = *reinterpret_cast<const uint4*>(krow + (j + kLanesPerRow * i) * EPC);
+      vb[u][i] = *reinterpret_cast<const uint4*>(vrow + (j + kLanesPerRow * i) * EPC);
+    }
+  };
 
+  // Two consecutive steps (rows t and t + 8 for this lane) at a time.
+  auto consume_pair = [&](int st, int u) {
+    float x0[G], x1[G];  // scores in log2 units
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        a0 = chunk_dot(kb[u][i], qf[h][i], a0, T{});
+        a1 = chunk_dot(kb[u + 1][i], qf[h][i], a1, T{});
+      }
+      x0[h] = sum8(a0) * scale_log2;
+      x1[h] = sum8(a1) * scale_log2;
+    }
+    if ((st + 2) * kRowsPerStep > ntok) {  // rows past the end hold stale data (maybe NaN)
+      const bool bad0 = st * kRowsPerStep + r >= ntok;
+      const bool bad1 = (st + 1) * kRowsPerStep + r >= ntok;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        x0[h] = bad0 ? -INFINITY : x0[h];
+        x1[h] = bad1 ? -INFINITY : x1[h];
+      }
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        if (bad0) vb[u][i] = make_uint4(0, 0, 0, 0);
+        if (bad1) vb[u + 1][i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    // Lazy running max: raise it only when a score exceeds it by > kLazyMax.
+    float over = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < G; ++h) over = fmaxf(over, fmaxf(x0[h], x1[h]) - m[h]);
+    if (__builtin_amdgcn_ballot_w64(over > kLazyMax)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float top = fmaxf(x0[h], x1[h]);
+        const float mn = top > m[h] + kLazyMax ? top : m[h];
+        const float f = fast_exp2(m[h] - mn);
+        l[h] *= f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+        m[h] = mn;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float w0v = fast_exp2(x0[h] - m[h]);
+      const float w1v = fast_exp2(x1[h] - m[h]);
+      l[h] += w0v + w1v;
+      const uint32_t wpk = sizeof(T) == 2 ? pack_bf16(w0v, w1v) : 0u;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) pv_pair(vb[u][i], vb[u + 1][i], wpk, w0v, w1v, &acc[h][i * EPC], T{});
+    }
+  };
+
+  // Batches of U steps: all U steps' loads are issued (a step past the end
+  // re-reads the last one, a cache hit, so the count of loads in flight is
+  // the same on every path), then consumed in pairs.
+  for (int st0 = 0; st0 < nsteps; st0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) issue(min(st0 + u, nsteps - 1), u);
+    // Keep all U steps' loads ahead of the math (the scheduler would sink
+    // each load next to its first use, exposing memory latency per step).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; u += 2)
+      if (st0 + u < nsteps) consume_pair(st0 + u, u);
+  }
+
+  // ---- merge the 8 row groups of the wave (lanes that differ in bits 3..5)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = max_over_groups8(m[h]);
+    const float f = fast_exp2(m[h] - M);
+    l[h] = sum_over_groups8(l[h] * f);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = sum_over_groups8(acc[h][e] * f);
+    m[h] = M;
+  }
   if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -300,87 +312,118 @@ __global__ __launch_bounds__(kThreads) void PartitionKernel(
       for (int i = 0; i < CPL; ++i)
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
-          m_acc[(w * G + h) * D + (j + kLanesPerRow * i) * EPC + e] = acc[h][i * EPC + e];
+          s_acc[w][h][(j + kLanesPerRow * i) * EPC + e] = acc[h][i * EPC + e];
   }
   if (lane < G) {
-    m_ml[(w * G + lane) * 2 + 0] = msel;  // lane < G: msel = m[lane]
-    m_ml[(w * G + lane) * 2 + 1] = lsum;
+    float mm = m[0], ll = l[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) {
+      mm = lane == h ? m[h] : mm;
+      ll = lane == h ? l[h] : ll;
+    }
+    s_ml[w][lane][0] = mm;
+    s_ml[w][lane][1] = ll;
   }
   __syncthreads();
 
-  // ---------------- merge the 4 waves and write.
+  // ---- merge the 4 waves; write the output, or this partition's partial state
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
-    float M = -INFINITY;
+    float M = kMaxInit;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, m_ml[(ww * G + h) * 2]);
-    float a = 0.f, l = 0.f;
-    if (M != -INFINITY) {
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_ml[ww][h][0]);
+    float a = 0.f, lsum = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float mw = m_ml[(ww * G + h) * 2];
-        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        a = fmaf(f, m_acc[(ww * G + h) * D + d], a);
-        l = fmaf(f, m_ml[(ww * G + h) * 2 + 1], l);
-      }
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = fast_exp2(s_ml[ww][h][0] - M);
+      a = fmaf(f, s_acc[ww][h][d], a);
+      lsum = fmaf(f, s_ml[ww][h][1], lsum);
     }
-    const int hq = g * G + h;
     if (Pb == 1) {
-      out[(static_cast<int64_t>(b) * Hq + hq) * D + d] = from_f32<T>(l > 0.f ? a / l : 0.f);
+      out[(static_cast<int64_t>(b) * Hq + g * G + h) * D + d] = from_f32<T>(lsum > 0.f ? a / lsum : 0.f);
     } else {
-      float* st = ws + ((static_cast<int64_t>(b) * Hq + hq) * P + p) * (D + 2);
-      st[2 + d] = a;
+      const int64_t row = (static_cast<int64_t>(b) * Hq + g * G + h) * P + p;  // (b, q head, p)
+      ws_acc[row * D + d] = a;
       if (d == 0) {
-        st[0] = M;
-        st[1] = l;
+        ws_ml[row * 2 + 0] = M;
+        ws_ml[row * 2 + 1] = lsum;
       }
     }
   }
 }
 
 // Pass 2: log-sum-exp merge of the partitions of each (sequence, q head).
+// One wave; lanes first take the partitions' maxima in parallel, then each
+// lane accumulates D/64 output dims over the partitions with the weights
+// broadcast from the lane that computed them.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void MergeKernel(T* __restrict__ out, const float* __restrict__ ws,
-                                                 const int32_t* __restrict__ seq_lens, int32_t Hq,
-                                                 int32_t max_seq_len, int32_t PT, int32_t P) {
+__global__ __launch_bounds__(64) void MergeKernel(T* __restrict__ out, const float* __restrict__ ws_acc,
+                                                  const float* __restrict__ ws_ml,
+                                                  const int32_t* __restrict__ seq_lens, int32_t Hq,
+                                                  int32_t max_seq_len, int32_t PT, int32_t P) {
+  constexpr int EPL = D / 64;
   const int bh = blockIdx.x;
   const int b = bh / Hq;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
   int L = seq_lens[b];
   L = min(max(L, 0), max_seq_len);
   const int Pb = (L + PT - 1) / PT;
   if (Pb <= 1) return;  // written by pass 1
-  const float* st = ws + static_cast<int64_t>(bh) * P * (D + 2);
-  float M = -INFINITY;
-  for (int p = 0; p < Pb; ++p) M = fmaxf(M, st[p * (D + 2)]);
-  float a = 0.f, l = 0.f;
-  for (int p = 0; p < Pb; ++p) {
-    const float* s = st + p * (D + 2);
-    const float f = (s[0] == -INFINITY) ? 0.f : fast_exp2(s[0] - M);
-    a = fmaf(f, s[2 + d], a);
-    l = fmaf(f, s[1], l);
+  const float* ml = ws_ml + static_cast<int64_t>(bh) * P * 2;
+  const float* acc = ws_acc + static_cast<int64_t>(bh) * P * D;
+
+  float M = kMaxInit;
+  for (int x = lane; x < Pb; x += 64) M = fmaxf(M, ml[2 * x]);
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) M = fmaxf(M, __shfl_xor(M, s));
+
+  float a[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a[e] = 0.f;
+  float lsum = 0.f;
+  for (int x0 = 0; x0 < Pb; x0 += 64) {
+    const int x = x0 + lane;
+    float wgt = 0.f, lx = 0.f;
+    if (x < Pb) {
+      wgt = fast_exp2(ml[2 * x] - M);
+      lx = ml[2 * x + 1];
+    }
+    lsum += wgt * lx;
+    const int n = min(64, Pb - x0);
+#pragma unroll 8
+    for (int k = 0; k < n; ++k) {
+      const float wk = __shfl(wgt, k);
+      const float* src = acc + static_cast<int64_t>(x0 + k) * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a[e] = fmaf(wk, src[e], a[e]);
+    }
   }
-  out[static_cast<int64_t>(bh) * D + d] = from_f32<T>(l > 0.f ? a / l : 0.f);
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) lsum += __shfl_xor(lsum, s);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    out[static_cast<int64_t>(bh) * D + lane * EPL + e] = from_f32<T>(a[e] * inv);
 }
 
 template <typename T, int D, int G>
 hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   const int P = a.num_partitions;
-  const int items = P * a.B * a.Hkv;
-  const int per_xcd = (items + 7) / 8;
-  const size_t lds = (static_cast<size_t>(a.partition_tokens) * G + kWaves * G * D +
-                      kWaves * G * 2) * sizeof(float);
+  const int64_t items = static_cast<int64_t>(P) * a.B * a.Hkv;
+  const int per_xcd = static_cast<int>((items + 7) / 8);
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((PartitionKernel<T, D, G>), dim3(per_xcd * 8), dim3(kThreads), lds, stream,
+  DecodeWorkspace ws = DecodeWorkspaceLayout(a.ws, a.B, a.Hq, a.D, P);
+  hipLaunchKernelGGL((DecodeKernel<T, D, G>), dim3(per_xcd * 8), dim3(kThreads), 0, stream,
                      static_cast<T*>(a.out), static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k_cache), static_cast<const T*>(a.v_cache),
-                     a.block_tables, a.seq_lens, a.ws, a.B, a.Hkv, a.max_blocks, a.block_size,
-                     a.num_blocks, a.max_seq_len, a.partition_tokens, P, per_xcd, scale_log2);
+                     a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
+                     __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
+                     P, per_xcd, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
-  hipLaunchKernelGGL((MergeKernel<T, D>), dim3(a.B * a.Hq), dim3(D), 0, stream,
-                     static_cast<T*>(a.out), a.ws, a.seq_lens, a.Hq, a.max_seq_len,
+  hipLaunchKernelGGL((MergeKernel<T, D>), dim3(a.B * a.Hq), dim3(64), 0, stream,
+                     static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, a.Hq, a.max_seq_len,
                      a.partition_tokens, P);
   return hipGetLastError();
 }

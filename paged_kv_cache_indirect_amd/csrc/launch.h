@@ -19,7 +19,7 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* ws;          // partial states; null when num_partitions == 1
+  void* ws;           // workspace (DecodeWorkspaceLayout); null when num_partitions == 1
   int32_t B, Hq, Hkv, D, G;
   int32_t block_size, num_blocks, max_blocks;
   int32_t max_seq_len, partition_tokens, num_partitions;
@@ -48,10 +48,23 @@ inline int32_t DecodePartitions(int32_t max_seq_len, int32_t partition_tokens) {
   int32_t p = (max_seq_len + partition_tokens - 1) / partition_tokens;
   return p < 1 ? 1 : p;
 }
-// Partial state per (sequence, q head, partition): D accumulators + (max, sum).
+// Workspace of a decode call with more than one partition: the fp32 partial
+// state of every (sequence, q head, partition):
+//   [acc: B*Hq*P*D f32][max, sum: B*Hq*P*2 f32]
 inline size_t DecodeWorkspaceBytes(int32_t B, int32_t Hq, int32_t D, int32_t P) {
   if (P <= 1) return 0;
   return static_cast<size_t>(B) * Hq * P * (static_cast<size_t>(D) + 2) * sizeof(float);
+}
+struct DecodeWorkspace {
+  float* acc;
+  float* ml;
+};
+inline DecodeWorkspace DecodeWorkspaceLayout(void* ws, int32_t B, int32_t Hq, int32_t D, int32_t P) {
+  DecodeWorkspace w{nullptr, nullptr};
+  if (!ws || P <= 1) return w;
+  w.acc = static_cast<float*>(ws);
+  w.ml = w.acc + static_cast<size_t>(B) * Hq * P * D;
+  return w;
 }
 
 }  // namespace pa

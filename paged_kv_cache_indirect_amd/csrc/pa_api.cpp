@@ -206,15 +206,15 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
     if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * l.block_size)
       return Fail(PA_ERR_INVALID, "max_seq_len exceeds max_blocks * block_size");
     const int32_t pt = partition_tokens == 0 ? 512 : partition_tokens;
-    if (pt % 64 || pt > 2048 || static_cast<int64_t>(pt) * G > 8192)
-      return Fail(PA_ERR_UNSUPPORTED,
-                  "partition_tokens must be a multiple of 64, at most 2048, with partition_tokens * G <= 8192");
+    if (pt % 64 || pt > 2048)
+      return Fail(PA_ERR_UNSUPPORTED, "partition_tokens must be a multiple of 64, at most 2048");
     const int32_t P = pa::DecodePartitions(max_seq_len, pt);
     if (static_cast<int64_t>(P) * B * l.num_kv_heads >= (int64_t{1} << 31) - 8)
       return Fail(PA_ERR_UNSUPPORTED, "grid too large");
     const size_t need = pa::DecodeWorkspaceBytes(B, num_q_heads, l.head_dim, P);
     if (need && (!workspace || workspace_bytes < need))
       return Fail(PA_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+    if (need && !Aligned16(workspace)) return Fail(PA_ERR_INVALID, "workspace must be 16-byte aligned");
     pa::DecodeArgs a{};
     a.out = out;
     a.q = q;
@@ -222,7 +222,7 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
     a.v_cache = pool->v_cache;
     a.block_tables = block_tables;
     a.seq_lens = seq_lens;
-    a.ws = static_cast<float*>(workspace);
+    a.ws = workspace;
     a.B = B;
     a.Hq = num_q_heads;
     a.Hkv = l.num_kv_heads;

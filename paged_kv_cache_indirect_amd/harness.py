@@ -94,7 +94,7 @@ class GpuCache:
     def workspace_for(self, partition_tokens: int = 0, max_seq_len: Optional[int] = None):
         msl = self.wl.max_seq_len if max_seq_len is None else max_seq_len
         need = pa_decode_workspace_bytes(self.wl.B, self.wl.Hq, self.wl.D, msl, partition_tokens)
-        return torch.empty(max(need, 1), dtype=torch.uint8, device=self.device) if need else None
+        return torch.empty(need, dtype=torch.uint8, device=self.device) if need else None
 
     def decode(self, partition_tokens: int = 0, workspace=None, out=None, max_seq_len=None, stream=None):
         out = self.out if out is None else out

@@ -214,9 +214,9 @@ def test_device_entry_points_validate_before_launch():
     st, pool = make_pool(64, 16, hkv=8, d=128)
     assert st == 0
     dummy = 0x40000
-    ws = pa.lib.pa_decode_workspace_bytes(64, 32, 128, 4096, 512)
-    assert ws == 64 * 32 * 8 * 130 * 4
-    assert pa.lib.pa_decode_workspace_bytes(64, 32, 128, 512, 512) == 0
+    ws = pa.lib.pa_decode_workspace_bytes(64, 32, 128, 4097, 512)   # 9 partitions
+    assert ws == 64 * 32 * 9 * 130 * 4
+    assert pa.lib.pa_decode_workspace_bytes(64, 32, 128, 512, 512) == 0   # one partition covers it
     # G = 3 is outside the supported set
     assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 24, 0.1, 4096, 0, dummy, ws, None) \
         == pa.PA_ERR_UNSUPPORTED
@@ -226,14 +226,14 @@ def test_device_entry_points_validate_before_launch():
     # max_seq_len beyond the table width
     assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 16, dummy, 4, 32, 0.1, 4096, 0, dummy, ws, None) \
         == pa.PA_ERR_INVALID
-    # workspace missing / too small
-    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 32, 0.1, 4096, 0, None, 0, None) \
+    # workspace missing / too small / misaligned
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 257, dummy, 4, 32, 0.1, 4097, 0, None, 0, None) \
         == pa.PA_ERR_INVALID
     assert "workspace too small" in pa.pa_last_error()
     # partition size rules
     assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 32, 0.1, 4096, 100, dummy, 1 << 30, None) \
         == pa.PA_ERR_UNSUPPORTED
-    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 64, 0.1, 4096, 2048, dummy, 1 << 30, None) \
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 64, 0.1, 4096, 4096, dummy, 1 << 30, None) \
         == pa.PA_ERR_UNSUPPORTED
     # misaligned q
     assert pa.lib.pa_decode(pool, dummy, dummy + 2, dummy, 256, dummy, 4, 32, 0.1, 4096, 0, dummy, ws, None) \
