@@ -12,10 +12,10 @@
 // [num_blocks, block_size, Hkv, D] ("LLM推理优化", §3.3).
 //
 // How (MI355X-first; FlashAttention-2 on the pages is Ampere prior art):
-//  * One workgroup = 4 waves = 128 query rows of one (sequence, kv head): the
+//  * One workgroup = 8 waves = 256 query rows of one (sequence, kv head): the
 //    G q heads that share the kv head are packed into the row dimension
-//    (128 / G positions x G heads), so every K/V tile staged in LDS feeds
-//    all of them.
+//    (256 / G positions x G heads), so every K/V tile staged in LDS feeds all
+//    of them. Each wave owns 32 rows.
 //  * The contraction runs on v_mfma_f32_32x32x16_bf16 in transposed form:
 //    S^T = K · Q^T and O^T = V^T · P^T. In the accumulator layout a lane then
 //    owns one query row (lane % 32) and 16 keys (or 16 dims) of it, so the
@@ -24,14 +24,21 @@
 //    into the B operand of the second product with no data movement: the key
 //    order inside each 16-key step is permuted consistently on both sides
 //    (V^T is written to LDS in that permuted order).
-//  * KV tiles of 64 tokens: K as [token][dim], V transposed to [dim][token]
-//    (the transpose is done in registers with v_perm before the LDS write),
-//    double-buffered; the next tile's global loads are in flight while the
-//    current one is multiplied. Tokens past the causal end of the workgroup
-//    are staged as zeros (stale slots of the last block may hold anything).
-//  * Online softmax in base 2 with a lazily updated running max: the max is
-//    only raised when a tile's max exceeds it by more than 8, so most tiles
-//    skip the O rescale; weights stay ≤ 2^8, exact up to rounding.
+//  * KV tiles of kKT tokens: K as [token][dim], V transposed to [dim][token]
+//    (transposed in registers with v_perm before the LDS write), both with
+//    padded rows so that every MFMA operand read is one ds_read_b128 at a
+//    per-lane base plus an immediate offset, free of bank conflicts;
+//    double-buffered (70 KiB of LDS; gfx950 allows 160 KiB per workgroup).
+//    Half the threads stage K, half V. Global loads run two tiles ahead of
+//    the multiply (two register staging sets) and block ids three, so the
+//    latency of a load is covered by two tiles of MFMA work and no load
+//    waits on a table lookup.
+//    Tokens past the causal end of the workgroup are staged as zeros (stale
+//    slots of the last block may hold anything).
+//  * Online softmax in base 2: the tile max is taken on raw scores, the
+//    scale is folded into one FMA ahead of exp2, and the running max is
+//    raised lazily (only when a tile exceeds it by more than 8), so most
+//    tiles skip the O rescale; weights stay ≤ 2^8, exact up to rounding.
 //  * Causal mask only on tiles that reach past the smallest position of the
 //    workgroup. Work items are mapped XCD-major with the kv head outermost,
 //    so all query tiles of one (sequence, kv head) share one XCD's L2.
@@ -42,9 +49,10 @@ namespace pa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;   // query rows (positions x heads) per workgroup
-constexpr int kKT = 64;      // KV tokens per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;  // query rows (positions x heads) per workgroup
+constexpr int kKT = 64;             // KV tokens per tile
 constexpr float kLazyMax = 8.f;
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -55,16 +63,23 @@ struct PGeom {
   static constexpr int kKSteps = D / 16;      // MFMA k-steps for S^T = K Q^T
   static constexpr int kDBlocks = D / 32;     // 32-dim output blocks
   static constexpr int kChunks = D / 8;       // 16-byte chunks per K/V row
-  static constexpr int kKPitch = D;           // K tile row pitch (elements)
-  static constexpr int kVPitch = kKT;         // V^T tile row pitch (elements)
+  static constexpr int kKPitch = D + 8;       // K tile row pitch (elements): 16 B pad
+  static constexpr int kVPitch = kKT + 8;     // V^T tile row pitch (elements): 16 B pad
   static constexpr int kKElems = kKT * kKPitch;
   static constexpr int kVElems = D * kVPitch;
   static constexpr int kBufElems = kKElems + kVElems;
-  static constexpr int kKLoads = kKT * kChunks / kThreads;   // 16-byte K chunks per thread
-  static constexpr int kVPairs = (kKT / 4) * kChunks;        // (4-token group, chunk) pairs
+  static constexpr int kSBlocks = kKT / 32;   // 32-key S^T accumulator blocks per tile
+  static constexpr int kPSteps = kKT / 16;    // 16-key MFMA k-steps of O^T += V^T P^T
+  static constexpr int kStageThreads = kThreads / 2;                 // K stagers, then V stagers
+  static constexpr int kKLoads = kKT * kChunks / kStageThreads;      // 16-byte K chunks per K stager
+  static constexpr int kVPairs = (kKT / 4) * kChunks;                // (4-token group, chunk) pairs
+  static constexpr int kVGroups = (kVPairs + kStageThreads - 1) / kStageThreads;  // per V stager
+  static constexpr int kSRegs = kKLoads > 4 * kVGroups ? kKLoads : 4 * kVGroups;
+  static constexpr int kIds = kKLoads > kVGroups ? kKLoads : kVGroups;
+  static_assert(kKT % 32 == 0 && kKLoads >= 1, "tile geometry");
 };
 
-// Position of key t (0..63) inside a V^T row: within each 16-key MFMA step,
+// Position of key t (0..kKT-1) inside a V^T row: within each 16-key MFMA step,
 // half-wave h takes keys {4h..4h+3, 8+4h..8+4h+3}, which are the keys its
 // S^T accumulators hold; they are stored contiguously so one 16-byte read
 // fetches them.
@@ -74,20 +89,6 @@ __device__ __forceinline__ int vt_pos(int t) {
   return (blk << 5) | (s << 4) | (h << 3) | e;
 }
 
-// LDS tiles are unpadded (two K + V^T tiles fit in 64 KB); 16-byte slots are
-// XOR-swizzled per row instead, so that the MFMA operand reads (32 rows at one
-// column) and the staging writes spread over all 64 banks.
-// V^T rows: 8 slots of 8 keys.
-__device__ __forceinline__ int vt_swz(int d, int pos) {
-  return (((pos >> 3) ^ (((d >> 1) ^ (d >> 4)) & 7)) << 3) | (pos & 7);
-}
-// K rows: D / 8 slots of 8 dims.
-template <int D>
-__device__ __forceinline__ int k_swz(int row, int col) {
-  const int f = D == 128 ? (row & 15) : ((row >> 1) & 7);
-  return (((col >> 3) ^ f) << 3) | (col & 7);
-}
-
 __device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) {  // (x.lo, y.lo)
   return __builtin_amdgcn_perm(y, x, 0x05040100u);
 }
@@ -95,12 +96,16 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {  // (x.hi,
   return __builtin_amdgcn_perm(y, x, 0x07060302u);
 }
 
+__device__ __forceinline__ int clamp_blk(int blk, int num_blocks) {
+  return (static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks)) ? blk : 0;
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void PrefillKernel(
+__global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens, int32_t B,
-    int32_t Hkv, int32_t max_blocks, int32_t bs, int32_t num_blocks, int32_t n_qtiles,
+    int32_t Hkv, int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t n_qtiles,
     int32_t per_xcd, float scale_log2) {
   using PG = PGeom<D>;
   constexpr int QP = kRows / G;  // positions per workgroup
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 2) void PrefillKernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;   // query row within the wave (accumulator column)
   const int h2 = lane >> 5;  // half-wave
 
@@ -125,6 +130,7 @@ __global__ __launch_bounds__(kThreads, 2) void PrefillKernel(
   const int nq = cu_q_lens[b + 1] - qbeg;
   const int q0 = tile * QP;
   if (q0 >= nq) return;
+  const int bs = 1 << bs_shift;
   int L = seq_lens[b];
   L = min(max(L, 0), max_blocks * bs);
   const int ctx = L - nq;
@@ -156,71 +162,106 @@ __global__ __launch_bounds__(kThreads, 2) void PrefillKernel(
   const uint16_t* kbase = kc + static_cast<int64_t>(g) * D;
   const uint16_t* vbase = vc + static_cast<int64_t>(g) * D;
 
-  // ---- staging: K chunks (token, chunk) and V 4-token groups
-  uint4 kreg[PG::kKLoads];
-  uint4 vreg[4];
-  const bool v_active = tid < PG::kVPairs;
-  const int v_c = tid % PG::kChunks;
-  const int v_tg = tid / PG::kChunks;
+  // ---- staging roles: threads [0, 256) stage K chunks, [256, 512) stage V groups.
+  // A K stager moves chunks (token, c) with c fastest across lanes (a 256-byte
+  // row per 16 lanes). A V stager moves 4-token groups (tg, c) with tg fastest
+  // across lanes, so the transposed LDS writes of one instruction spread over
+  // the banks.
+  const bool k_stager = tid < PG::kStageThreads;
+  const int st_id = k_stager ? tid : tid - PG::kStageThreads;
+  const int k_c = st_id % PG::kChunks;
+  constexpr int kKTokStride = PG::kStageThreads / PG::kChunks;
+  constexpr int kGroupsPerTile = kKT / 4;
 
-  auto block_of = [&](int t) -> int {
-    int blk = trow[t / bs];
-    return (static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks)) ? blk : 0;
+  using StageRegs = uint4[PG::kSRegs];  // K: kKLoads chunks; V: 4 tokens per group
+  struct TileIds {
+    int id[PG::kIds];
+  };
+  // Block ids for one tile, fetched a tile ahead of its K/V loads.
+  auto fetch_ids = [&](int jt) {
+    TileIds ids;
+    const int t0 = jt * kKT;
+#pragma unroll
+    for (int i = 0; i < PG::kIds; ++i) ids.id[i] = 0;
+    if (k_stager) {
+#pragma unroll
+      for (int i = 0; i < PG::kKLoads; ++i) {
+        const int tok = t0 + st_id / PG::kChunks + i * kKTokStride;
+        if (tok < kv_end) ids.id[i] = clamp_blk(trow[tok >> bs_shift], num_blocks);
+      }
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < PG::kVGroups; ++gi) {
+        const int pair = st_id + gi * PG::kStageThreads;
+        const int tok0 = t0 + 4 * (pair % kGroupsPerTile);  // 4 aligned tokens share a block
+        if (pair < PG::kVPairs && tok0 < kv_end) ids.id[gi] = clamp_blk(trow[tok0 >> bs_shift], num_blocks);
+      }
+    }
+    return ids;
   };
 
-  auto load_tile = [&](int j) {
-    const int t0 = j * kKT;
+  auto load_tile = [&](int jt, const TileIds& ids, StageRegs& sreg) {
+    const int t0 = jt * kKT;
+    if (k_stager) {
 #pragma unroll
-    for (int i = 0; i < PG::kKLoads; ++i) {
-      const int c = tid % PG::kChunks;
-      const int t = tid / PG::kChunks + i * (kThreads / PG::kChunks);
-      const int tok = t0 + t;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tok < kv_end) {
-        const int64_t slot = static_cast<int64_t>(block_of(tok)) * bs + tok % bs;
-        v = *reinterpret_cast<const uint4*>(kbase + slot * slot_stride + 8 * c);
-      }
-      kreg[i] = v;
-    }
-    if (v_active) {
-      const int tok0 = t0 + 4 * v_tg;
-      const int blk = tok0 < kv_end ? block_of(tok0) : 0;  // 4 aligned tokens share a block
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = tok0 + r;
+      for (int i = 0; i < PG::kKLoads; ++i) {
+        const int tok = t0 + st_id / PG::kChunks + i * kKTokStride;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (tok < kv_end) {
-          const int64_t slot = static_cast<int64_t>(blk) * bs + tok % bs;
-          v = *reinterpret_cast<const uint4*>(vbase + slot * slot_stride + 8 * v_c);
+          const int64_t slot = (static_cast<int64_t>(ids.id[i]) << bs_shift) + (tok & (bs - 1));
+          v = *reinterpret_cast<const uint4*>(kbase + slot * slot_stride + 8 * k_c);
         }
-        vreg[r] = v;
+        sreg[i] = v;
+      }
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < PG::kVGroups; ++gi) {
+        const int pair = st_id + gi * PG::kStageThreads;
+        const int c = pair / kGroupsPerTile;
+        const int tok0 = t0 + 4 * (pair % kGroupsPerTile);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = tok0 + r;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (pair < PG::kVPairs && tok < kv_end) {
+            const int64_t slot = (static_cast<int64_t>(ids.id[gi]) << bs_shift) + (tok & (bs - 1));
+            v = *reinterpret_cast<const uint4*>(vbase + slot * slot_stride + 8 * c);
+          }
+          sreg[4 * gi + r] = v;
+        }
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const StageRegs& sreg) {
     uint16_t* ks = smem + buf * PG::kBufElems;
     uint16_t* vt = ks + PG::kKElems;
+    if (k_stager) {
 #pragma unroll
-    for (int i = 0; i < PG::kKLoads; ++i) {
-      const int c = tid % PG::kChunks;
-      const int t = tid / PG::kChunks + i * (kThreads / PG::kChunks);
-      *reinterpret_cast<uint4*>(ks + t * PG::kKPitch + k_swz<D>(t, 8 * c)) = kreg[i];
-    }
-    if (v_active) {
-      // Transpose 4 tokens x 8 dims into 8 dims x 4 tokens.
-      const uint32_t* a = reinterpret_cast<const uint32_t*>(&vreg[0]);
-      const uint32_t* bq = reinterpret_cast<const uint32_t*>(&vreg[1]);
-      const uint32_t* cq = reinterpret_cast<const uint32_t*>(&vreg[2]);
-      const uint32_t* dq = reinterpret_cast<const uint32_t*>(&vreg[3]);
-      const int pos = vt_pos(4 * v_tg);
+      for (int i = 0; i < PG::kKLoads; ++i) {
+        const int t = st_id / PG::kChunks + i * kKTokStride;
+        *reinterpret_cast<uint4*>(ks + t * PG::kKPitch + 8 * k_c) = sreg[i];
+      }
+    } else {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int d0 = 8 * v_c + 2 * k;
-        uint2 lo = make_uint2(perm_lo(a[k], bq[k]), perm_lo(cq[k], dq[k]));
-        uint2 hi = make_uint2(perm_hi(a[k], bq[k]), perm_hi(cq[k], dq[k]));
-        *reinterpret_cast<uint2*>(vt + d0 * PG::kVPitch + vt_swz(d0, pos)) = lo;
-        *reinterpret_cast<uint2*>(vt + (d0 + 1) * PG::kVPitch + vt_swz(d0 + 1, pos)) = hi;
+      for (int gi = 0; gi < PG::kVGroups; ++gi) {
+        const int pair = st_id + gi * PG::kStageThreads;
+        if (pair >= PG::kVPairs) continue;
+        const int c = pair / kGroupsPerTile;
+        // Transpose 4 tokens x 8 dims into 8 dims x 4 tokens.
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(&sreg[4 * gi + 0]);
+        const uint32_t* bq = reinterpret_cast<const uint32_t*>(&sreg[4 * gi + 1]);
+        const uint32_t* cq = reinterpret_cast<const uint32_t*>(&sreg[4 * gi + 2]);
+        const uint32_t* dq = reinterpret_cast<const uint32_t*>(&sreg[4 * gi + 3]);
+        const int pos = vt_pos(4 * (pair % kGroupsPerTile));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int d0 = 8 * c + 2 * k;
+          uint2 lo = make_uint2(perm_lo(a[k], bq[k]), perm_lo(cq[k], dq[k]));
+          uint2 hi = make_uint2(perm_hi(a[k], bq[k]), perm_hi(cq[k], dq[k]));
+          *reinterpret_cast<uint2*>(vt + d0 * PG::kVPitch + pos) = lo;
+          *reinterpret_cast<uint2*>(vt + (d0 + 1) * PG::kVPitch + pos) = hi;
+        }
       }
     }
   };
@@ -234,58 +275,51 @@ __global__ __launch_bounds__(kThreads, 2) void PrefillKernel(
   float m = -INFINITY;  // running max (log2 units), lazily raised
   float l = 0.f;        // this half-wave's share of the softmax denominator
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // Per-lane LDS bases: MFMA operand reads then differ only by immediates.
+  const int k_lane = n * PG::kKPitch + (D / 2) * h2;   // + (32*tb)*pitch + 8*st
+  const int v_lane = n * PG::kVPitch + 8 * h2;         // + (32*db)*pitch + 16*ks
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // Pipeline, two tiles deep: while tile j is multiplied out of LDS buffer
+  // j % 2, tile j + 1 sits in registers (its loads were issued an iteration
+  // ago) and tile j + 2's loads are in flight into the other register set;
+  // block ids run one tile further ahead. The loop is unrolled by two so the
+  // two register sets keep fixed registers.
+  auto compute_tile = [&](int j) {
     const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
-
     const uint16_t* ks = smem + buf * PG::kBufElems;
     const uint16_t* vt = ks + PG::kKElems;
 
-    // S^T = K · Q^T for the two 32-key halves of the tile.
-    f32x16v s[2];
+    // S^T = K · Q^T, one 32-key accumulator block at a time.
+    f32x16v s[PG::kSBlocks];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tb = 0; tb < PG::kSBlocks; ++tb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[tb][v] = 0.f;
-      const int kr = 32 * tb + n;
-      const uint16_t* krow = ks + kr * PG::kKPitch;
+      const uint16_t* krow = ks + k_lane + 32 * tb * PG::kKPitch;
 #pragma unroll
       for (int st = 0; st < PG::kKSteps; ++st) {
-        const bf16x8v a = __builtin_bit_cast(
-            bf16x8v, *reinterpret_cast<const uint4*>(krow + k_swz<D>(kr, (D / 2) * h2 + 8 * st)));
+        const bf16x8v a = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(krow + 8 * st));
         s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[tb], 0, 0, 0);
       }
     }
 
-    // Scores in log2 units; causal mask where the tile reaches past min_apos.
+    // Causal mask where the tile reaches past min_apos; tile max on raw scores.
     const int t0 = j * kKT;
-    float tmax = -INFINITY;
     if (t0 + kKT - 1 > min_apos) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < PG::kSBlocks; ++tb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int t = t0 + 32 * tb + 8 * (v >> 2) + 4 * h2 + (v & 3);
-          const float x = s[tb][v] * scale_log2;
-          s[tb][v] = t <= apos ? x : -INFINITY;
-          tmax = fmaxf(tmax, s[tb][v]);
-        }
-    } else {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[tb][v] *= scale_log2;
-          tmax = fmaxf(tmax, s[tb][v]);
+          s[tb][v] = t <= apos ? s[tb][v] : -INFINITY;
         }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < PG::kSBlocks; ++tb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[tb][v]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;  // scale > 0 keeps the argmax
 
     // Lazy max: raise m only when the tile exceeds it by more than kLazyMax.
     const bool raise = tmax > m + kLazyMax;
@@ -299,17 +333,17 @@ __global__ __launch_bounds__(kThreads, 2) void PrefillKernel(
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
       m = mn;
     }
-    const float msafe = (m == -INFINITY) ? 0.f : m;
+    const float nm = (m == -INFINITY) ? 0.f : -m;
 
-    // P = 2^(s - m) as bf16, packed per 16-key MFMA step.
-    bf16x8v p[4];
+    // P = 2^(scale·s - m) as bf16, packed per 16-key MFMA step.
+    bf16x8v p[PG::kPSteps];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < PG::kSBlocks; ++tb)
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = fast_exp2(s[tb][8 * hs + e] - msafe);
+          const float pe = fast_exp2(fmaf(s[tb][8 * hs + e], scale_log2, nm));
           l += pe;
           p[2 * tb + hs][e] = static_cast<__bf16>(pe);
         }
@@ -317,19 +351,37 @@ __global__ __launch_bounds__(kThreads, 2) void PrefillKernel(
     // O^T += V^T · P^T.
 #pragma unroll
     for (int db = 0; db < PG::kDBlocks; ++db) {
-      const int d = 32 * db + n;
-      const uint16_t* vrow = vt + d * PG::kVPitch;
+      const uint16_t* vrow = vt + v_lane + 32 * db * PG::kVPitch;
 #pragma unroll
-      for (int ks4 = 0; ks4 < 4; ++ks4) {
-        const int pos = 16 * ks4 + 8 * h2;
-        const bf16x8v a =
-            __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(vrow + vt_swz(d, pos)));
+      for (int ks4 = 0; ks4 < PG::kPSteps; ++ks4) {
+        const bf16x8v a = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(vrow + 16 * ks4));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[ks4], o[db], 0, 0, 0);
       }
     }
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+  };
+  auto iteration = [&](int j, StageRegs& in_flight, const StageRegs& arrived, TileIds& ids_next) {
+    TileIds ids_after{};
+    if (j + 3 < n_tiles) ids_after = fetch_ids(j + 3);
+    if (j + 2 < n_tiles) load_tile(j + 2, ids_next, in_flight);
+    compute_tile(j);
+    if (j + 1 < n_tiles) store_tile((j + 1) & 1, arrived);
+    ids_next = ids_after;
     __syncthreads();
+  };
+
+  StageRegs sreg_a, sreg_b;
+  TileIds ids_next{};
+  if (n_tiles > 0) {
+    load_tile(0, fetch_ids(0), sreg_a);
+    store_tile(0, sreg_a);
+    if (n_tiles > 1) load_tile(1, fetch_ids(1), sreg_a);
+    if (n_tiles > 2) ids_next = fetch_ids(2);
+  }
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    iteration(j, sreg_b, sreg_a, ids_next);
+    if (j + 1 < n_tiles) iteration(j + 1, sreg_a, sreg_b, ids_next);
   }
 
   // ---- normalise and store (bf16, round to nearest even)
@@ -359,12 +411,17 @@ hipError_t LaunchTyped(const PrefillArgs& a, hipStream_t stream) {
   if (items >= (int64_t{1} << 31) - 8) return hipErrorInvalidValue;
   const int per_xcd = static_cast<int>((items + 7) / 8);
   const size_t lds = 2 * PGeom<D>::kBufElems * sizeof(uint16_t);
+  // More than 64 KiB of dynamic LDS: raise the kernel's limit once.
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&PrefillKernel<D, G>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((PrefillKernel<D, G>), dim3(per_xcd * 8), dim3(kThreads), lds, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k_cache), static_cast<const uint16_t*>(a.v_cache),
-                     a.cu_q_lens, a.block_tables, a.seq_lens, a.B, a.Hkv, a.max_blocks, a.block_size,
-                     a.num_blocks, n_qtiles, per_xcd, scale_log2);
+                     a.cu_q_lens, a.block_tables, a.seq_lens, a.B, a.Hkv, a.max_blocks,
+                     __builtin_ctz(a.block_size), a.num_blocks, n_qtiles, per_xcd, scale_log2);
   return hipGetLastError();
 }
 
