@@ -307,6 +307,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the decode steps, run one plain 1 GiB device-to-device copy: "
+                         "the reference that scales hardware byte counters (FETCH_SIZE, WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -322,6 +325,16 @@ def main() -> int:
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         return 2
     import paged_kv_cache_indirect_amd  # noqa: F401  (fails loudly if libpa.so is missing)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 1073741824 bytes read, 1073741824 bytes written")
+        del src, dst
+        torch.cuda.empty_cache()
 
     wl, dec = run_decode(args)
     frac = dec["achieved_gbps"] / HBM_PEAK_GBPS
