@@ -74,7 +74,7 @@ typedef struct {
   int32_t free_blocks;
   int32_t used_blocks;
   int32_t shared_blocks;
-  int32_t reserved;
+  int32_t pending_copies;  /* copy-on-write block copies not yet run (see pa_write_kv) */
   int64_t filled_slots;
   int64_t allocated_slots;
 } pa_pool_stats_t;
@@ -124,10 +124,18 @@ pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seq_ids, int32_t n, 
 
 /* Make dst a new sequence that shares all of src's blocks (prefix sharing:
  * same physical blocks, each block's refcount + 1; "vLLM的'内存分页'到底多神奇",
- * §2 and §3 phase 3). Only whole blocks are shared: src's length must be a
- * multiple of block_size, else PA_ERR_UNSUPPORTED (no copy-on-write of a
- * partly filled shared block). Errors: PA_ERR_UNKNOWN_SEQ (src unknown),
- * PA_ERR_INVALID (dst exists or dst == src). */
+ * §2 and §3 phase 3), a partly filled last block included. Sharing is
+ * copy-on-write (same page, §3 phase 3): when a sequence appends into a
+ * partly filled last block that other sequences still share, the append
+ * takes a fresh block for it first (before any new tail block; it counts
+ * toward the all-or-nothing admission), drops one reference of the shared
+ * block, and records a pending copy shared -> fresh. The next pa_write_kv on
+ * this pool performs the pending copies, in the order recorded, on its
+ * stream before its scatter; a copy sees the block as the device holds it
+ * then, so write the rows of an append (pa_write_kv) before forking that
+ * sequence. Pending copies are kept across frees of their blocks.
+ * Errors: PA_ERR_UNKNOWN_SEQ (src unknown), PA_ERR_INVALID (dst exists or
+ * dst == src). */
 pa_status pa_seq_fork(pa_pool* pool, int64_t src_seq_id, int64_t dst_seq_id);
 
 /* End a sequence: each of its blocks loses one reference; a block whose count
@@ -148,17 +156,25 @@ pa_status pa_block_tables(const pa_pool* pool, const int64_t* seq_ids, int32_t n
 /* Current block accounting into *out (host). */
 pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
 
+/* The pending copy-on-write block copies, in the order they will run:
+ * src_out[i] -> dst_out[i] (host, capacity entries each); *n_out receives the
+ * count. Errors: PA_ERR_INVALID (null pointers, capacity below the count). */
+pa_status pa_pool_pending_copies(const pa_pool* pool, int32_t* src_out, int32_t* dst_out, int32_t capacity,
+                                 int32_t* n_out);
+
 /* ------------------------------------------------------------------------ */
 /* Device operations                                                          */
 /* ------------------------------------------------------------------------ */
 
 /* KV append scatter (paging's O(1) append: "LLM推理优化：技术原理解析总览", §2.2).
+ * First performs, in order, the pool's pending copy-on-write block copies
+ * (see pa_seq_fork), then the scatter, all on `stream`.
  * key, value (device): [T, num_kv_heads, head_dim] of the pool dtype,
  * contiguous. slot_mapping (device): T int64 flat slots from pa_seq_append.
  * Row t is copied bit for bit to k_cache/v_cache[slot / block_size][slot %
  * block_size]. A negative slot is padding and is skipped; a slot ≥
  * num_blocks × block_size is also skipped (no fault). Two rows with the same
- * slot race (undefined which lands). T == 0 launches nothing.
+ * slot race (undefined which lands). T == 0 launches only pending copies.
  * Errors: PA_ERR_INVALID (T < 0, null pointers with T > 0), PA_ERR_HIP. */
 pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value,
                       const int64_t* slot_mapping, int32_t T, void* stream);

@@ -10,7 +10,8 @@ Sources:
   each time the current page fills (with 8-token pages, token 9 opens page 2).
 * same page, §3 phase 3: a finished sequence's pages go back to the free
   list; pages shared through prefix caching carry a reference count and are
-  returned only when the last sharer ends.
+  returned only when the last sharer ends; the sharing works like
+  copy-on-write (a writer gets its own copy of a shared page).
 * same page, §4: admission control refuses (or queues) a request when not
   enough free pages exist, instead of risking an out-of-memory failure;
   aborting a request frees all of its pages.
@@ -21,8 +22,12 @@ Policy choices the pages leave open (listed in the design doc):
   pushed back on top, and a sequence's blocks are pushed in table order;
 * ``append`` is all-or-nothing: if the free list cannot cover the new blocks
   it fails with NO_BLOCKS and changes nothing;
-* ``fork`` shares whole blocks only: the source length must be a multiple of
-  block_size (copy-on-write of a partly filled shared block is not modelled);
+* ``fork`` shares every block, a partly filled last block included;
+* appending into a partly filled last block that is shared first takes a
+  fresh block for it (before any new tail block, counted in the
+  all-or-nothing admission), drops one reference of the shared block and
+  records a pending copy (shared, fresh); pending copies are kept in order
+  until the device performs them, frees included;
 * block ids are int32; tables export padded with -1.
 """
 from __future__ import annotations
@@ -46,6 +51,7 @@ class BlockManagerModel:
         self.ref: List[int] = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
+        self.pending: List[tuple] = []   # copy-on-write block copies (src, dst), in order
 
     # ---------------------------------------------------------------- ops
     def append(self, seq: int, n: int):
@@ -56,11 +62,18 @@ class BlockManagerModel:
         L = self.lens.get(seq, 0)
         bs = self.block_size
         have = len(table)
-        need = -(-(L + n) // bs) - have
-        if need > len(self.free):
+        cow = n > 0 and have > 0 and L % bs != 0 and self.ref[table[-1]] > 1
+        tail = -(-(L + n) // bs) - have
+        if tail + cow > len(self.free):
             return ERR_NO_BLOCKS, []
         table = list(table)
-        for _ in range(need):
+        if cow:
+            old, blk = table[-1], self.free.pop()
+            self.ref[blk] += 1
+            self.ref[old] -= 1
+            table[-1] = blk
+            self.pending.append((old, blk))
+        for _ in range(tail):
             blk = self.free.pop()
             self.ref[blk] += 1
             table.append(blk)
@@ -77,7 +90,14 @@ class BlockManagerModel:
         if n < 0 or len(set(seqs)) != len(seqs):
             return ERR_INVALID, []
         bs = self.block_size
-        need = sum(-(-(self.lens.get(s, 0) + n) // bs) - len(self.tables.get(s, [])) for s in seqs)
+        need = 0
+        dropped: Dict[int, int] = {}
+        for s in seqs:
+            L, t = self.lens.get(s, 0), self.tables.get(s, [])
+            need += -(-(L + n) // bs) - len(t)
+            if n > 0 and t and L % bs != 0 and self.ref[t[-1]] - dropped.get(t[-1], 0) > 1:
+                need += 1
+                dropped[t[-1]] = dropped.get(t[-1], 0) + 1
         if need > len(self.free):
             return ERR_NO_BLOCKS, []
         out = []
@@ -92,8 +112,6 @@ class BlockManagerModel:
             return ERR_UNKNOWN_SEQ
         if dst in self.tables or dst == src:
             return ERR_INVALID
-        if self.lens[src] % self.block_size:
-            return ERR_UNSUPPORTED
         self.tables[dst] = list(self.tables[src])
         self.lens[dst] = self.lens[src]
         for blk in self.tables[dst]:
@@ -137,6 +155,7 @@ class BlockManagerModel:
             "shared_blocks": sum(1 for r in self.ref if r > 1),
             "filled_slots": sum(fill),
             "allocated_slots": used * bs,
+            "pending_copies": len(self.pending),
         }
 
     # -------------------------------------------------------------- checks

@@ -38,6 +38,11 @@ class OracleCache:
                 st, slots = self.bm.append(seq, n)
                 if st != 0:
                     raise RuntimeError(f"oracle block manager refused {op}: status {st}")
+                # Copy-on-write copies recorded by the append run before its rows land.
+                for src, dst in self.bm.pending:
+                    self.k_cache[dst] = self.k_cache[src]
+                    self.v_cache[dst] = self.v_cache[src]
+                self.bm.pending = []
                 if only is None or seq in only:
                     k, v = wl.kv_rows(seq, start, n)
                     self._scatter(k, v, np.asarray(slots, dtype=np.int64))

@@ -23,7 +23,7 @@ __all__ = [
     "PaError", "PA_OK", "PA_ERR_INVALID", "PA_ERR_NO_BLOCKS", "PA_ERR_UNSUPPORTED", "PA_ERR_HIP",
     "PA_ERR_UNKNOWN_SEQ", "PA_F32", "PA_BF16", "LIB_PATH", "lib",
     "pa_alloc_pool", "pa_free_pool", "pa_seq_append", "pa_seq_append_batch", "pa_seq_fork", "pa_seq_free",
-    "pa_block_tables", "pa_pool_stats", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
+    "pa_block_tables", "pa_pool_stats", "pa_pool_pending_copies", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
     "pa_prefill", "pa_last_error",
 ]
 
@@ -52,7 +52,7 @@ class _Layout(ctypes.Structure):
 
 class _Stats(ctypes.Structure):
     _fields_ = [("free_blocks", ctypes.c_int32), ("used_blocks", ctypes.c_int32),
-                ("shared_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("shared_blocks", ctypes.c_int32), ("pending_copies", ctypes.c_int32),
                 ("filled_slots", ctypes.c_int64), ("allocated_slots", ctypes.c_int64)]
 
 
@@ -66,6 +66,7 @@ _SIGS = {
     "pa_seq_free": (_i32, [_vp, _i64]),
     "pa_block_tables": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "pa_pool_stats": (_i32, [_vp, ctypes.POINTER(_Stats)]),
+    "pa_pool_pending_copies": (_i32, [_vp, _vp, _vp, _i32, _vp]),
     "pa_write_kv": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
@@ -193,7 +194,18 @@ def pa_pool_stats(pool: int) -> dict:
     _check(lib.pa_pool_stats(pool, ctypes.byref(s)), "pa_pool_stats")
     return {"free_blocks": s.free_blocks, "used_blocks": s.used_blocks,
             "shared_blocks": s.shared_blocks, "filled_slots": s.filled_slots,
-            "allocated_slots": s.allocated_slots}
+            "allocated_slots": s.allocated_slots, "pending_copies": s.pending_copies}
+
+
+def pa_pool_pending_copies(pool: int) -> list:
+    """Pending copy-on-write block copies [(src, dst), ...] in run order."""
+    n = ctypes.c_int32()
+    cap = pa_pool_stats(pool)["pending_copies"]
+    src = np.empty(max(cap, 1), dtype=np.int32)
+    dst = np.empty(max(cap, 1), dtype=np.int32)
+    _check(lib.pa_pool_pending_copies(pool, src.ctypes.data, dst.ctypes.data, cap, ctypes.byref(n)),
+           "pa_pool_pending_copies")
+    return list(zip(src[:n.value].tolist(), dst[:n.value].tolist()))
 
 
 def pa_last_error() -> str:

@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstddef>
 #include <unordered_set>
 
 namespace pa {
@@ -57,17 +58,30 @@ Status BlockManager::Append(int64_t seq, int32_t n, int64_t* slots_out, std::str
     return kErrInvalid;
   }
   const int64_t have = it == seqs_.end() ? 0 : static_cast<int64_t>(it->second.table.size());
-  const int64_t need = CeilDiv(new_len, block_size_) - have;
+  const bool cow = n > 0 && have > 0 && old_len % block_size_ != 0 &&
+                   ref_[static_cast<size_t>(it->second.table.back())] > 1;
+  const int64_t tail = CeilDiv(new_len, block_size_) - have;
+  const int64_t need = tail + (cow ? 1 : 0);
   if (need > static_cast<int64_t>(free_.size())) {
     *err = "not enough free blocks: need " + std::to_string(need) + ", have " +
            std::to_string(free_.size());
     return kErrNoBlocks;
   }
   // Everything that can throw happens before the first mutation.
+  if (cow) pending_.reserve(pending_.size() + 1);
   if (it == seqs_.end()) it = seqs_.emplace(seq, Seq{}).first;
   Seq& s = it->second;
-  s.table.reserve(static_cast<size_t>(have + need));
-  for (int64_t i = 0; i < need; ++i) {
+  s.table.reserve(static_cast<size_t>(have + tail));
+  if (cow) {  // the shared, partly filled last block: this sequence writes into its own copy
+    const int32_t old_blk = s.table.back();
+    const int32_t blk = free_.back();
+    free_.pop_back();
+    ++ref_[static_cast<size_t>(blk)];
+    --ref_[static_cast<size_t>(old_blk)];
+    s.table.back() = blk;
+    pending_.emplace_back(old_blk, blk);
+  }
+  for (int64_t i = 0; i < tail; ++i) {
     int32_t blk = free_.back();
     free_.pop_back();
     ++ref_[static_cast<size_t>(blk)];
@@ -94,6 +108,7 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
   // Validate the whole batch and count its new blocks before any mutation.
   std::unordered_set<int64_t> seen;
   seen.reserve(static_cast<size_t>(n));
+  std::unordered_map<int32_t, int32_t> cow_drops;  // references dropped by copies earlier in the batch
   int64_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (!seen.insert(seqs[i]).second) {
@@ -108,6 +123,16 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
       return kErrInvalid;
     }
     need += CeilDiv(old_len + n_tokens, block_size_) - have;
+    // A copy-on-write of a shared partial last block needs one more block;
+    // an earlier copy in the same batch may have left it with one user.
+    if (n_tokens > 0 && have > 0 && old_len % block_size_ != 0) {
+      const int32_t last = it->second.table.back();
+      int32_t& dropped = cow_drops[last];
+      if (ref_[static_cast<size_t>(last)] - dropped > 1) {
+        ++need;
+        ++dropped;
+      }
+    }
   }
   if (need > static_cast<int64_t>(free_.size())) {
     *err = "not enough free blocks for the batch: need " + std::to_string(need) + ", have " +
@@ -125,6 +150,7 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
       Seq& s = seqs_.find(seqs[i])->second;
       s.table.reserve(static_cast<size_t>(CeilDiv(s.len + n_tokens, block_size_)));
     }
+    pending_.reserve(pending_.size() + static_cast<size_t>(n));
   } catch (...) {
     for (int64_t id : created) seqs_.erase(id);
     throw;
@@ -147,10 +173,6 @@ Status BlockManager::Fork(int64_t src, int64_t dst, std::string* err) {
     *err = "destination sequence " + std::to_string(dst) + " already exists";
     return kErrInvalid;
   }
-  if (it->second.len % block_size_) {
-    *err = "fork shares whole blocks only: source length is not a multiple of block_size";
-    return kErrUnsupported;
-  }
   Seq copy = it->second;  // may throw before any mutation
   for (int32_t blk : copy.table) ++ref_[static_cast<size_t>(blk)];
   seqs_.emplace(dst, std::move(copy));
@@ -166,7 +188,12 @@ Status BlockManager::Free(int64_t seq, std::string* err) {
   // free_ never exceeds num_blocks_ entries: reserve once so push_back cannot throw.
   free_.reserve(static_cast<size_t>(num_blocks_));
   for (int32_t blk : it->second.table) {
-    if (--ref_[static_cast<size_t>(blk)] == 0) free_.push_back(blk);
+    if (--ref_[static_cast<size_t>(blk)] == 0) {
+      // A pending copy into this block stays: a later copy may read the
+      // block, and the scatter that follows the copies overwrites whatever
+      // rows a new owner gets.
+      free_.push_back(blk);
+    }
   }
   seqs_.erase(it);
   return kOk;

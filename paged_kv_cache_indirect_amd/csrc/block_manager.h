@@ -8,13 +8,22 @@
 //      prompt prefix may point at the same physical pages.
 //  §3  phase 1: pages are taken on demand, one more each time the current
 //      page fills; phase 3: a finished sequence's pages return to the free
-//      list, a shared page only when its last user ends (reference count).
+//      list, a shared page only when its last user ends (reference count);
+//      sharing is copy-on-write: a sequence about to write into a page it
+//      shares gets its own copy first.
 //  §4  admission control: refuse a request that cannot get its pages rather
 //      than run out of memory; abort frees every page of a request.
 //
 // Policy choices where the page is silent: the free list is a LIFO stack
 // seeded from a caller-given order; freed blocks are pushed in table order;
-// append is all-or-nothing; fork shares whole blocks only.
+// append is all-or-nothing; fork shares every block, a partly filled last
+// one included. Appending into a partly filled last block that is shared
+// takes a fresh block first (before any new tail block), records a pending
+// copy old -> new of that block, and drops one reference of the old block.
+// The device copy is the caller's: pa_write_kv performs the pending copies,
+// in the order they were recorded, before its scatter, so a copy sees the
+// block as the device holds it then. Pending copies survive frees of
+// their blocks (a later copy in the list may read one).
 //
 // Plain C++ (no HIP): it is built into the device library and, on its own,
 // into host-only test drivers.
@@ -23,6 +32,7 @@
 #include <cstdint>
 #include <string>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 namespace pa {
@@ -70,6 +80,10 @@ class BlockManager {
   int32_t refcount(int32_t blk) const { return ref_[blk]; }
   int32_t free_count() const { return static_cast<int32_t>(free_.size()); }
 
+  // Block copies (src, dst) recorded by copy-on-write appends, in order.
+  const std::vector<std::pair<int32_t, int32_t>>& pending_copies() const { return pending_; }
+  void ClearPendingCopies() { pending_.clear(); }
+
  private:
   struct Seq {
     std::vector<int32_t> table;
@@ -80,6 +94,7 @@ class BlockManager {
   std::vector<int32_t> free_;  // stack: back() is the next block handed out
   std::vector<int32_t> ref_;
   std::unordered_map<int64_t, Seq> seqs_;
+  std::vector<std::pair<int32_t, int32_t>> pending_;
 };
 
 }  // namespace pa

@@ -12,6 +12,20 @@ hipError_t LaunchWriteKv(const void* key, const void* value, const int64_t* slot
                          void* v_cache, int32_t T, int64_t row_bytes, int64_t num_slots,
                          hipStream_t stream);
 
+// Up to kMaxCopiesPerLaunch independent block copies (no pair reads or
+// writes a block another pair of the list writes), passed by value.
+constexpr int kMaxCopiesPerLaunch = 64;
+struct BlockCopyList {
+  int32_t src[kMaxCopiesPerLaunch];
+  int32_t dst[kMaxCopiesPerLaunch];
+  int32_t n;
+};
+
+// Copy block src[p] to block dst[p] in both pools for every pair of the list
+// (copy-on-write of shared blocks).
+hipError_t LaunchCopyBlocks(void* k_cache, void* v_cache, const BlockCopyList& list, int64_t block_bytes,
+                            hipStream_t stream);
+
 struct DecodeArgs {
   void* out;
   const void* q;

@@ -154,9 +154,26 @@ pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out) {
     out->free_blocks = s.free_blocks;
     out->used_blocks = s.used_blocks;
     out->shared_blocks = s.shared_blocks;
-    out->reserved = 0;
+    out->pending_copies = static_cast<int32_t>(pool->bm.pending_copies().size());
     out->filled_slots = s.filled_slots;
     out->allocated_slots = s.allocated_slots;
+    return PA_OK;
+  });
+}
+
+pa_status pa_pool_pending_copies(const pa_pool* pool, int32_t* src_out, int32_t* dst_out, int32_t capacity,
+                                 int32_t* n_out) {
+  return Guard([&]() -> pa_status {
+    if (!pool || !n_out) return Fail(PA_ERR_INVALID, "null argument");
+    const auto& pend = pool->bm.pending_copies();
+    const int32_t n = static_cast<int32_t>(pend.size());
+    if (capacity < n) return Fail(PA_ERR_INVALID, "capacity smaller than the pending copy count");
+    if (n > 0 && (!src_out || !dst_out)) return Fail(PA_ERR_INVALID, "null argument");
+    for (int32_t i = 0; i < n; ++i) {
+      src_out[i] = pend[static_cast<size_t>(i)].first;
+      dst_out[i] = pend[static_cast<size_t>(i)].second;
+    }
+    *n_out = n;
     return PA_OK;
   });
 }
@@ -166,11 +183,39 @@ pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value, const i
   return Guard([&]() -> pa_status {
     if (!pool) return Fail(PA_ERR_INVALID, "null pool");
     if (T < 0) return Fail(PA_ERR_INVALID, "T must be >= 0");
-    if (T == 0) return PA_OK;
-    if (!key || !value || !slot_mapping) return Fail(PA_ERR_INVALID, "null argument");
-    if (!Aligned16(key) || !Aligned16(value))
+    if (T > 0 && (!key || !value || !slot_mapping)) return Fail(PA_ERR_INVALID, "null argument");
+    if (T > 0 && (!Aligned16(key) || !Aligned16(value)))
       return Fail(PA_ERR_INVALID, "key and value must be 16-byte aligned");
+    // Copy-on-write copies recorded by earlier appends run first, in order.
+    // Consecutive copies share a launch until one touches a block that an
+    // earlier copy of the launch writes, or writes a block it reads.
     const pa_kv_layout& l = pool->layout;
+    const int64_t block_bytes =
+        static_cast<int64_t>(l.block_size) * l.num_kv_heads * l.head_dim * ElemBytes(l.dtype);
+    pa::BlockCopyList list{};
+    auto flush = [&]() -> pa_status {
+      const pa_status st = FromHip(pa::LaunchCopyBlocks(pool->k_cache, pool->v_cache, list, block_bytes,
+                                                        static_cast<hipStream_t>(stream)),
+                                   "copy-on-write block copy launch");
+      list.n = 0;
+      return st;
+    };
+    for (const auto& cp : pool->bm.pending_copies()) {
+      bool depends = list.n == pa::kMaxCopiesPerLaunch;
+      for (int32_t i = 0; i < list.n && !depends; ++i)
+        depends = cp.first == list.dst[i] || cp.second == list.dst[i] || cp.second == list.src[i];
+      if (depends) {
+        const pa_status st = flush();
+        if (st != PA_OK) return st;
+      }
+      list.src[list.n] = cp.first;
+      list.dst[list.n] = cp.second;
+      ++list.n;
+    }
+    const pa_status st = flush();
+    if (st != PA_OK) return st;
+    pool->bm.ClearPendingCopies();
+    if (T == 0) return PA_OK;
     const int64_t row_bytes = static_cast<int64_t>(l.num_kv_heads) * l.head_dim * ElemBytes(l.dtype);
     const int64_t chunks = static_cast<int64_t>(T) * (row_bytes / 16);
     if ((chunks + 255) / 256 >= (int64_t{1} << 31)) return Fail(PA_ERR_UNSUPPORTED, "T too large");

@@ -12,6 +12,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace pa {
 
 __global__ __launch_bounds__(256) void WriteKvKernel(const uint4* __restrict__ key,
@@ -29,6 +31,32 @@ __global__ __launch_bounds__(256) void WriteKvKernel(const uint4* __restrict__ k
   const int64_t dst = s * chunks_per_row + c;
   kc[dst] = key[idx];
   vc[dst] = value[idx];
+}
+
+// Copy-on-write of shared blocks: for each pair p of the list, block
+// src[p] of both pools to block dst[p] (block_bytes each, a multiple of 16).
+// The pairs of one launch run concurrently, so the host puts a pair whose
+// blocks an earlier pair of the list writes or reads (a chain a->b, b->c)
+// into a later launch. blockIdx.y picks the pair.
+__global__ __launch_bounds__(256) void CopyBlocksKernel(uint4* __restrict__ kc, uint4* __restrict__ vc,
+                                                        BlockCopyList list, int64_t chunks) {
+  const int64_t src = list.src[blockIdx.y], dst = list.dst[blockIdx.y];
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < chunks;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    kc[dst * chunks + i] = kc[src * chunks + i];
+    vc[dst * chunks + i] = vc[src * chunks + i];
+  }
+}
+
+hipError_t LaunchCopyBlocks(void* k_cache, void* v_cache, const BlockCopyList& list, int64_t block_bytes,
+                            hipStream_t stream) {
+  if (list.n <= 0) return hipSuccess;
+  const int64_t chunks = block_bytes / 16;
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 64);
+  hipLaunchKernelGGL(CopyBlocksKernel, dim3(static_cast<uint32_t>(blocks), static_cast<uint32_t>(list.n)),
+                     dim3(256), 0, stream, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), list,
+                     chunks);
+  return hipGetLastError();
 }
 
 hipError_t LaunchWriteKv(const void* key, const void* value, const int64_t* slots, void* k_cache,

@@ -77,8 +77,10 @@ int main() {
       std::printf("\n");
     } else if (op[0] == 's') {
       pa::PoolStats s = bm.Stats();
-      std::printf("%d %d %d %lld %lld\n", s.free_blocks, s.used_blocks, s.shared_blocks,
+      std::printf("%d %d %d %lld %lld", s.free_blocks, s.used_blocks, s.shared_blocks,
                   static_cast<long long>(s.filled_slots), static_cast<long long>(s.allocated_slots));
+      for (const auto& c : bm.pending_copies()) std::printf(" %d %d", c.first, c.second);
+      std::printf("\n");
     }
   }
   return 0;

@@ -90,7 +90,7 @@ def run_model(nb, bs, order, ops):
             out.append((st, l, t))
         s = m.stats()
         out.append(tuple(s[k] for k in ("free_blocks", "used_blocks", "shared_blocks", "filled_slots",
-                                        "allocated_slots")))
+                                        "allocated_slots")) + tuple(x for c in m.pending for x in c))
     return out
 
 
@@ -118,7 +118,8 @@ def run_abi(pool, ops):
             out.append((st, l.tolist(), t[:, :mb].tolist()) if st == 0 else (st, None, None))
         s = pa.pa_pool_stats(pool)
         out.append(tuple(s[k] for k in ("free_blocks", "used_blocks", "shared_blocks", "filled_slots",
-                                        "allocated_slots")))
+                                        "allocated_slots")) + tuple(x for c in pa.pa_pool_pending_copies(pool)
+                                                                   for x in c))
     return out
 
 

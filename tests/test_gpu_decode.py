@@ -73,7 +73,7 @@ def small(lens, Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", seed=5, **kw):
 
 
 # ------------------------------------------------------------------ scatter
-@pytest.mark.parametrize("name", ["tiny", "gqa8b", "prefix"])
+@pytest.mark.parametrize("name", ["tiny", "gqa8b", "prefix", "prefix_cow"])
 def test_write_kv_bit_exact(name):
     wl = W.config(name)
     gpu, ora = build_both(wl)
@@ -160,6 +160,66 @@ def test_decode_prefix_sharing_full():
     got = widen_out(gpu.decode(512, gpu.workspace_for(512)), wl.dtype)
     assert_close(got, oracle_out(wl, ora), wl.dtype, "prefix")
     gpu.close()
+
+
+def test_decode_copy_on_write_prefix_full():
+    """32 sequences forked from a prefix whose last block is half full: the
+    appends copy that block (HIP block copy before the scatter) and decode
+    reads each sequence's own copy."""
+    wl = W.config("prefix_cow")
+    gpu, ora = build_both(wl)
+    from paged_kv_cache_indirect_amd import pa_pool_stats
+    st = pa_pool_stats(gpu.pool)
+    model = ora.bm.stats()
+    for key in ("free_blocks", "used_blocks", "shared_blocks", "filled_slots", "allocated_slots"):
+        assert st[key] == model[key], key
+    assert st["pending_copies"] == 0
+    got = widen_out(gpu.decode(512, gpu.workspace_for(512)), wl.dtype)
+    assert_close(got, oracle_out(wl, ora), wl.dtype, "prefix_cow")
+    gpu.close()
+
+
+def test_write_kv_with_no_rows_runs_pending_copies():
+    """T == 0 performs the pending copy-on-write copies and nothing else."""
+    import paged_kv_cache_indirect_amd as pa
+    h = _harness()
+    nb, bs, hkv, d = 6, 8, 2, 64
+    kc = torch.zeros((nb, bs, hkv, d), dtype=torch.float32, device="cuda")
+    vc = torch.zeros_like(kc)
+    pool = pa.pa_alloc_pool(kc, vc, np.arange(nb, dtype=np.int32))
+    try:
+        slots = pa.pa_seq_append(pool, 0, 5)
+        rows = torch.arange(5 * hkv * d, dtype=torch.float32, device="cuda").reshape(5, hkv, d) + 1
+        pa.pa_write_kv(pool, rows, -rows, torch.from_numpy(np.asarray(slots, np.int64)).cuda())
+        pa.pa_seq_fork(pool, 0, 1)
+        pa.pa_seq_append(pool, 1, 2)
+        (src, dst), = pa.pa_pool_pending_copies(pool)
+        e = torch.empty((0, hkv, d), dtype=torch.float32, device="cuda")
+        pa.pa_write_kv(pool, e, e, torch.empty(0, dtype=torch.int64, device="cuda"))
+        torch.cuda.synchronize()
+        assert pa.pa_pool_pending_copies(pool) == []
+        k = h.to_host(kc, "f32")
+        v = h.to_host(vc, "f32")
+        assert np.array_equal(k[dst], k[src]) and np.array_equal(v[dst], v[src])
+        assert np.array_equal(k[src][:5], rows.cpu().numpy())
+        untouched = [b for b in range(nb) if b not in (src, dst)]
+        assert not k[untouched].any() and not v[untouched].any()
+        # A chain in one flush: 3 copies 0's block into b, 4 (a fork of 3)
+        # copies b into c. b -> c must run after src -> b (separate launches).
+        pa.pa_seq_fork(pool, 0, 3)
+        pa.pa_seq_append(pool, 3, 1)
+        pa.pa_seq_fork(pool, 3, 4)
+        pa.pa_seq_append(pool, 4, 1)
+        (s1, b), (s2, c) = pa.pa_pool_pending_copies(pool)
+        assert s1 == src and s2 == b
+        kc[b].fill_(7.0)
+        kc[c].fill_(9.0)
+        pa.pa_write_kv(pool, e, e, torch.empty(0, dtype=torch.int64, device="cuda"))
+        torch.cuda.synchronize()
+        k = h.to_host(kc, "f32")
+        assert np.array_equal(k[b], k[src]) and np.array_equal(k[c], k[src])
+    finally:
+        pa.pa_free_pool(pool)
 
 
 def test_decode_partition_invariance_and_max_seq_len_slack():

@@ -79,17 +79,31 @@ def test_lifo_worked_example():
     assert bm.free_seq(10) == OK        # pushes 4, 1, 0 in table order: top is 0
     st, s = bm.append(12, 5)            # pops 0, then 1
     assert bm.tables[12] == [0, 1]
-    st = bm.fork(12, 13)
-    assert st == ERR_UNSUPPORTED        # 5 tokens is not block-aligned
-    st, s = bm.append(12, 3)            # len 8, fills block 1 — no new block
-    assert bm.tables[12] == [0, 1] and s == [5, 6, 7]
-    assert bm.fork(12, 13) == OK
+    # Free stack now, top first: 4, 3, 2.
+    assert bm.fork(12, 13) == OK        # 5 tokens: the partly filled block 1 is shared too
     assert bm.ref[0] == 2 and bm.ref[1] == 2
-    st, s = bm.append(13, 1)            # child opens its own block: pops 4
-    assert bm.tables[13] == [0, 1, 4] and s == [16]
-    assert bm.free_seq(12) == OK        # shared blocks stay allocated
-    assert bm.ref[0] == 1 and 0 not in bm.free
-    assert bm.free_seq(13) == OK and bm.free_seq(11) == OK
+    st, s = bm.append(13, 2)            # child writes into shared block 1: copy-on-write pops 4
+    assert st == OK and bm.tables[13] == [0, 4] and s == [17, 18]
+    assert bm.pending == [(1, 4)] and bm.ref[1] == 1 and bm.ref[4] == 1
+    st, s = bm.append(12, 3)            # parent now owns block 1 alone: no copy, fills it
+    assert bm.tables[12] == [0, 1] and s == [5, 6, 7] and bm.pending == [(1, 4)]
+    assert bm.free_seq(13) == OK        # block 4 is free again; its copy stays recorded
+    assert bm.pending == [(1, 4)] and bm.free == [2, 3, 4]
+    bm.pending = []                     # the device performed the copy
+    assert bm.fork(12, 14) == OK        # len 8, aligned
+    st, s = bm.append(14, 1)            # opens its own block: pops 4
+    assert bm.tables[14] == [0, 1, 4] and s == [16]
+    assert bm.fork(14, 15) == OK        # len 9: shares 0, 1 and the partly filled 4
+    # 15 grows 9 -> 17: one copy block plus two tail blocks, only 3 and 2 free.
+    assert bm.append(15, 8) == (ERR_NO_BLOCKS, [])
+    assert bm.tables[15] == [0, 1, 4] and bm.pending == [] and bm.free == [2, 3]
+    st, s = bm.append(15, 7)            # 9 -> 16: copy pops 3, tail pops 2
+    assert st == OK and bm.tables[15] == [0, 1, 3, 2]
+    assert s == [13, 14, 15, 8, 9, 10, 11] and bm.pending == [(4, 3)]
+    assert bm.ref[4] == 1 and bm.ref[0] == 3
+    for q in (12, 14, 15):
+        assert bm.free_seq(q) == OK
+    assert bm.free_seq(11) == OK
     assert sorted(bm.free) == list(range(6))
 
 
@@ -216,3 +230,50 @@ def test_scatter_mutant_off_by_one_is_caught():
     for t, s in enumerate([0, 1, 2]):
         flat[s + 1] = key[t]
     assert not np.array_equal(OA.gather_sequence(kc, [0], 3, 4), key)
+
+
+# ------------------------------------------------- copy-on-write round trip
+def _round_trip_mismatches(wl):
+    from oracle.cache import OracleCache
+    c = OracleCache(wl)
+    bad = []
+    for s in range(wl.B):
+        L = int(c.seq_lens[s])
+        k, v = wl.seq_kv(s)
+        gk = OA.gather_sequence(c.k_cache, c.block_tables[s], L, wl.block_size)
+        gv = OA.gather_sequence(c.v_cache, c.block_tables[s], L, wl.block_size)
+        if not (np.array_equal(gk.view(np.uint8), k.view(np.uint8)) and
+                np.array_equal(gv.view(np.uint8), v.view(np.uint8))):
+            bad.append(s)
+    return c, bad
+
+
+def test_cache_round_trip_with_copy_on_write():
+    """A 1000-token prefix (last block half full) forked 32 ways: every
+    sequence reads back exactly its logical rows through its table, and the
+    partial block was copied once per writer that still found it shared."""
+    import workloads as W
+    wl = W.config("prefix_cow")
+    c, bad = _round_trip_mismatches(wl)
+    assert bad == []
+    part = [int(c.block_tables[s][62]) for s in range(wl.B)]
+    writers = [s for s in range(wl.B) if wl.seq_lens[s] > 1000]
+    # all writers but the last get private copies; non-writers and the last writer keep the original
+    original = part[writers[-1]]
+    assert all(part[s] == original for s in range(wl.B) if s not in writers[:-1])
+    assert len({part[s] for s in writers[:-1]} | {original}) == len(writers)
+
+
+def test_round_trip_catches_a_dropped_copy(monkeypatch):
+    """Mutation: an append that forgets its copy-on-write copy must fail the round trip."""
+    import workloads as W
+    real = BlockManagerModel.append
+
+    def forgetful(self, seq, n):
+        r = real(self, seq, n)
+        self.pending = []
+        return r
+
+    monkeypatch.setattr(BlockManagerModel, "append", forgetful)
+    _, bad = _round_trip_mismatches(W.config("prefix_cow"))
+    assert bad

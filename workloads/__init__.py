@@ -31,6 +31,13 @@ num_heads, head_dim] pool layout and block_size 16):
                bf16, bs 16.
 * ``prefill``- 16 seqs, each a 512-token causal query chunk over existing
                paged context of length U[0,7680], 32/8, D 128, bf16, bs 32.
+
+One more case exercises copy-on-write of a partly filled shared block (it is
+a parity case, not a benchmark configuration):
+
+* ``prefix_cow`` - 32 seqs forked from one 1000-token prefix (1000 = 62·16
+               + 8: the last prefix block is half full) plus suffixes
+               U[0,300], 32/8, D 128, bf16, bs 16.
 """
 from __future__ import annotations
 
@@ -230,14 +237,19 @@ def make_prefix_share(name: str, B: int, prefix_len: int, suffix_lens: Sequence[
                       pool_factor: float = 1.1, partition_tokens: int = 512) -> Workload:
     """B sequences whose first ``prefix_len`` tokens live in the same physical blocks.
 
-    Sequence 0 appends the prefix; sequences 1..B-1 fork it (sharing whole
-    blocks, so every prefix block ends with refcount B); then every sequence
-    appends its own suffix.
+    Sequence 0 appends the prefix; sequences 1..B-1 fork it (every prefix
+    block ends with refcount B); then every sequence appends its own suffix,
+    in order 0..B-1. When ``prefix_len`` is not a multiple of ``block_size``
+    the last prefix block is only partly filled, so each suffix append that
+    still finds it shared takes a private copy of it first (copy-on-write).
     """
-    assert prefix_len % block_size == 0, "shared prefix must be block-aligned"
     suffix_lens = np.asarray(suffix_lens, dtype=np.int32)
     lens = (suffix_lens + prefix_len).astype(np.int32)
-    need = prefix_len // block_size + int(sum(-(-int(s) // block_size) for s in suffix_lens))
+    # Upper bound on blocks: the prefix, plus for each non-empty suffix every
+    # block past the prefix's full blocks (its copy of a partial block included).
+    full = prefix_len // block_size
+    need = -(-prefix_len // block_size) + int(sum(-(-(prefix_len + int(s)) // block_size) - full
+                                                  for s in suffix_lens if s > 0))
     nb, perm = _pool(seed, need, pool_factor, None)
     ops: List[tuple] = [("append", 0, prefix_len)]
     ops += [("fork", 0, b) for b in range(1, B)]
@@ -287,6 +299,10 @@ def config(name: str) -> Workload:
     if name == "prefix":
         s = 1003
         return make_prefix_share("prefix", 128, 2048, _uniform_ints(s, 0, 1024, 128), Hq=32,
+                                 Hkv=8, D=128, block_size=16, dtype="bf16", seed=s)
+    if name == "prefix_cow":
+        s = 1005
+        return make_prefix_share("prefix_cow", 32, 1000, _uniform_ints(s, 0, 300, 32), Hq=32,
                                  Hkv=8, D=128, block_size=16, dtype="bf16", seed=s)
     if name == "prefill":
         s = 1004
