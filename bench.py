@@ -26,7 +26,8 @@ against 8 TB/s HBM. ``cpu_baseline`` is the CPU oracle
 (fp64 gather + softmax attention) timed on this host on the same workload.
 ``prefill`` is the chunked causal prefill workload (16 x 512-token chunks
 over U[0, 7680] cached tokens, bs 32) timed the same way against the bf16
-MFMA peak.
+MFMA peak. ``decode_fp8`` times pa_decode over an FP8 (E4M3) pool of the same
+batch shape (seed 1006), with the bytes it must read (1-byte K/V codes).
 """
 from __future__ import annotations
 
@@ -83,7 +84,7 @@ def decode_bytes(wl, lens) -> int:
     q and out, the ceil(L / bs) table entries in use, and seq_lens."""
     import numpy as np
     L = np.asarray(lens, dtype=np.int64)
-    kv = int(L.sum()) * wl.Hkv * wl.D * 2 * wl.elem_bytes
+    kv = int(L.sum()) * wl.Hkv * wl.D * 2 * wl.kv_elem_bytes
     qo = 2 * wl.B * wl.Hq * wl.D * wl.elem_bytes
     tables = int(((L + wl.block_size - 1) // wl.block_size).sum()) * 4
     return kv + qo + tables + 4 * wl.B
@@ -199,6 +200,51 @@ def run_decode(args):
     return wl, res
 
 
+# ----------------------------------------------------------------- FP8 decode
+def run_decode_fp8(args):
+    """pa_decode over an FP8 (E4M3) pool of the 8B-shaped batch: back-to-back
+    launches bracketed by HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_indirect_amd import harness
+
+    dev = torch.device("cuda:0")
+    wl = W.config("gqa8b_fp8")
+    log(f"[bench] building gqa8b_fp8 cache: B={wl.B} nb={wl.num_blocks}")
+    cache = harness.GpuCache(wl, device=dev, poison=False)
+    pt = args.partition_tokens
+    ws = cache.workspace_for(pt)
+    for _ in range(3):
+        cache.decode(pt, ws)
+    n = args.steps
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    for i in range(n):
+        e0[i].record(stream)
+        cache.decode(pt, ws)
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in zip(e0, e1)]
+    t = float(np.mean(ms)) * 1e-3
+    nbytes = decode_bytes(wl, wl.seq_lens)
+    gbps = nbytes / t / 1e9
+    cache.close()
+    log(f"[bench] fp8 decode: {t * 1e6:.1f} us, {gbps:.0f} GB/s")
+    return {
+        "workload": "8B-shaped GQA decode over an FP8 (OCP E4M3) pool: batch 64, 32 q / 8 kv heads, "
+                    "head_dim 128, bf16 q/out, block_size 16, lengths U[512,4096] (seed 1006), "
+                    "per-tensor scales k 0.0137 / v 0.0129",
+        "us_mean": t * 1e6, "us_median": float(np.median(ms)) * 1e3, "us_min": float(np.min(ms)) * 1e3,
+        "tok_per_s": wl.B / t,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "bytes_per_launch": nbytes},
+    }
+
+
 # -------------------------------------------------------------------- prefill
 def causal_flops(wl) -> float:
     """4 * D * Hq * sum_b sum_i (ctx_b + i + 1): QK^T and PV over the
@@ -305,6 +351,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache decode leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the decode steps, run one plain 1 GiB device-to-device copy: "
                          "the reference that scales hardware byte counters (FETCH_SIZE, WRITE_SIZE)")
@@ -339,6 +386,7 @@ def main() -> int:
     log(f"[bench] decode: {dec['decode_us_mean']:.1f} us/launch, {dec['achieved_gbps']:.0f} GB/s "
         f"({100 * frac:.1f}% of HBM peak); step {dec['ms_per_step'] * 1e3:.1f} us")
     pre = None if args.no_prefill else run_prefill(args)[1]
+    fp8 = None if args.no_fp8 else run_decode_fp8(args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, wl)
 
     line = {
@@ -382,6 +430,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "prefill": pre,
+        "decode_fp8": fp8,
     }
     print(json.dumps(line), flush=True)
     return 0

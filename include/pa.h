@@ -25,9 +25,12 @@
  *    calls are asynchronous: they enqueue work and return.
  *  - Threads: a pool is not thread-safe; callers serialise calls on one pool.
  *  - Supported set: head_dim ∈ {64, 128}; block_size ∈ {8, 16, 32};
- *    dtype ∈ {PA_F32, PA_BF16}; num_q_heads a multiple of num_kv_heads with
- *    group G = num_q_heads / num_kv_heads ∈ {1, 2, 4, 8}. q, out and the pools
- *    share one dtype. Anything else returns PA_ERR_UNSUPPORTED.
+ *    dtype ∈ {PA_F32, PA_BF16, PA_FP8_E4M3}; num_q_heads a multiple of
+ *    num_kv_heads with group G = num_q_heads / num_kv_heads ∈ {1, 2, 4, 8}.
+ *    q, out and the pools share one dtype, except that an FP8 pool takes
+ *    bf16 q, out and K/V rows (PA_FP8_E4M3 needs head_dim 128 and is served
+ *    by pa_write_kv and pa_decode; pa_prefill returns PA_ERR_UNSUPPORTED).
+ *    Anything else returns PA_ERR_UNSUPPORTED.
  *  - Grouped-query attention: q head h reads kv head h / G.
  *  - Block ids in tables are int32. Table contents are not validated on the
  *    device: an id outside [0, num_blocks) is undefined (the kernels clamp it
@@ -52,7 +55,13 @@ typedef enum {
   PA_ERR_UNKNOWN_SEQ = -5  /* sequence id not known to the pool                        */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* PA_FP8_E4M3: the pools hold 8-bit OCP E4M3 codes (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; 0x7F/0xFF NaN, no infinity, largest finite
+ * 448), one code per element, with one scale per pool for K and one for V
+ * (pa_pool_set_kv_scales): a code c stands for value(c) · scale. The FP8 KV
+ * cache is the remedy "LLM推理优化：技术原理解析总览" (dpshk.com) §5.1 gives
+ * for a 16-bit cache next to a quantised model; the page names no format. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 /* Geometry of the two pools. dtype holds a pa_dtype value. */
 typedef struct {
@@ -162,6 +171,13 @@ pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
 pa_status pa_pool_pending_copies(const pa_pool* pool, int32_t* src_out, int32_t* dst_out, int32_t capacity,
                                  int32_t* n_out);
 
+/* Per-tensor scales of an FP8 pool: a K code c stands for value(c) · k_scale,
+ * a V code for value(c) · v_scale. Both default to 1. pa_write_kv quantises
+ * with the scales current at the call, so set them before the first write.
+ * Errors: PA_ERR_INVALID (a scale not finite or not > 0),
+ * PA_ERR_UNSUPPORTED (the pool is not PA_FP8_E4M3). */
+pa_status pa_pool_set_kv_scales(pa_pool* pool, float k_scale, float v_scale);
+
 /* ------------------------------------------------------------------------ */
 /* Device operations                                                          */
 /* ------------------------------------------------------------------------ */
@@ -175,6 +191,10 @@ pa_status pa_pool_pending_copies(const pa_pool* pool, int32_t* src_out, int32_t*
  * block_size]. A negative slot is padding and is skipped; a slot ≥
  * num_blocks × block_size is also skipped (no fault). Two rows with the same
  * slot race (undefined which lands). T == 0 launches only pending copies.
+ * FP8 pools: key and value are bf16 rows; each element x is stored as the
+ * E4M3 code nearest to x / scale (the quotient rounded to fp32 first, then
+ * clamped to ±448, ties to the code with an even mantissa; NaN inputs give
+ * an unspecified code).
  * Errors: PA_ERR_INVALID (T < 0, null pointers with T > 0), PA_ERR_HIP. */
 pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value,
                       const int64_t* slot_mapping, int32_t T, void* stream);
@@ -189,8 +209,11 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
                                  int32_t max_seq_len, int32_t partition_tokens);
 
 /* Decode attention: one query token per sequence over its paged cache.
- * out (device): [B, num_q_heads, head_dim], pool dtype, written.
- * q (device): [B, num_q_heads, head_dim], pool dtype.
+ * out (device): [B, num_q_heads, head_dim], pool dtype (bf16 for an FP8
+ *   pool), written.
+ * q (device): [B, num_q_heads, head_dim], pool dtype (bf16 for an FP8 pool).
+ *   An FP8 pool's codes are read as value(code) · k_scale for keys and
+ *   value(code) · v_scale for values.
  * block_tables (device): [B, max_blocks] int32, row b = sequence b's table.
  * seq_lens (device): [B] int32, valid cache entries of each sequence at call
  *   time (the new token included, i.e. after pa_write_kv). Entries past

@@ -20,14 +20,18 @@ Readings where the pages are silent (each listed in the design doc):
   L sits at absolute position L - n + i and attends to tokens 0..L-n+i
   (none when that position is negative, i.e. the chunk is longer than the
   cache: zero output);
-* an empty sequence (L = 0) yields a zero output and log-sum-exp -inf.
+* an empty sequence (L = 0) yields a zero output and log-sum-exp -inf;
+* an FP8 cache holds E4M3 codes; a K code c is read as value(c)·k_scale and
+  a V code as value(c)·v_scale (``oracle.fp8``), exactly, before attention.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from .fp8 import decode_e4m3
+
 __all__ = [
-    "widen", "gather_sequence", "attend", "paged_decode", "paged_decode_one",
+    "widen", "widen_kv", "gather_sequence", "attend", "paged_decode", "paged_decode_one",
     "paged_prefill", "partial_state", "merge_partials",
 ]
 
@@ -41,6 +45,15 @@ def widen(a: np.ndarray, dtype: str) -> np.ndarray:
         u = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(np.float32).astype(np.float64)
     raise ValueError(dtype)
+
+
+def widen_kv(a: np.ndarray, kv_dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Stored cache elements -> fp64 values: fp32 / bf16 as ``widen``; FP8
+    codes decoded from the E4M3 definition and multiplied by the pool scale
+    (exact in fp64: a 4-bit by 24-bit significand product)."""
+    if kv_dtype == "fp8":
+        return decode_e4m3(a) * np.float64(np.float32(scale))
+    return widen(a, kv_dtype)
 
 
 def gather_sequence(cache: np.ndarray, table_row: np.ndarray, L: int, block_size: int) -> np.ndarray:
@@ -88,13 +101,16 @@ def paged_decode_one(q_bh: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
 
 
 def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
-                 block_tables: np.ndarray, seq_lens: np.ndarray, scale: float, dtype: str):
+                 block_tables: np.ndarray, seq_lens: np.ndarray, scale: float, dtype: str,
+                 kv_dtype: str = "", k_scale: float = 1.0, v_scale: float = 1.0):
     """Decode attention for every (sequence, q head).
 
     q [B, Hq, D]; k_cache/v_cache [num_blocks, block_size, Hkv, D];
-    block_tables int [B, max_blocks]; seq_lens int [B].
+    block_tables int [B, max_blocks]; seq_lens int [B]. ``kv_dtype`` is the
+    cache element type ("" = ``dtype``); FP8 caches use the pool scales.
     Returns (out [B, Hq, D] fp64, lse [B, Hq] fp64).
     """
+    kvd = kv_dtype or dtype
     B, Hq, D = q.shape
     block_size, Hkv = k_cache.shape[1], k_cache.shape[2]
     G = _gqa_group(Hq, Hkv)
@@ -102,8 +118,8 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     lse = np.full((B, Hq), -np.inf, dtype=np.float64)
     for b in range(B):
         L = int(seq_lens[b])
-        K = widen(gather_sequence(k_cache, block_tables[b], L, block_size), dtype)
-        V = widen(gather_sequence(v_cache, block_tables[b], L, block_size), dtype)
+        K = widen_kv(gather_sequence(k_cache, block_tables[b], L, block_size), kvd, k_scale)
+        V = widen_kv(gather_sequence(v_cache, block_tables[b], L, block_size), kvd, v_scale)
         qb = widen(q[b], dtype)
         for h in range(Hq):
             g = h // G

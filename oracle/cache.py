@@ -1,7 +1,8 @@
 """Build a workload's paged cache on the CPU with the oracle's own pieces.  (Test infrastructure.)
 
 Replays the workload's op stream through the Python block-manager model,
-scatters each appended row with the scatter oracle, and exports the tables.
+scatters each appended row with the scatter oracle (FP8 caches store the
+rows' E4M3 codes, quantised by ``oracle.fp8``), and exports the tables.
 Shares nothing with the HIP path: only the seeded workload description comes
 from the common generator module.
 """
@@ -9,7 +10,9 @@ from __future__ import annotations
 
 import numpy as np
 
+from .attention import widen
 from .block_manager import BlockManagerModel
+from .fp8 import NAN_CODE, quantize_e4m3
 from .scatter import write_kv
 
 SENTINEL_BF16 = 0x7FC1          # NaN patterns for never-written slots
@@ -25,7 +28,9 @@ class OracleCache:
         self.wl = wl
         only = None if only is None else set(int(s) for s in only) | ({0} if wl.prefix_len else set())
         shape = (wl.num_blocks, wl.block_size, wl.Hkv, wl.D)
-        if wl.dtype == "bf16":
+        if wl.cache_dtype == "fp8":
+            self.k_cache = np.full(shape, NAN_CODE if poison else 0, dtype=np.uint8)
+        elif wl.dtype == "bf16":
             self.k_cache = np.full(shape, SENTINEL_BF16 if poison else 0, dtype=np.uint16)
         else:
             self.k_cache = np.full(shape, SENTINEL_F32 if poison else 0, dtype=np.float32)
@@ -56,6 +61,9 @@ class OracleCache:
         self.seq_lens = np.asarray(lens, dtype=np.int32)
 
     def _scatter(self, k, v, slots):
+        if self.wl.cache_dtype == "fp8":
+            k = quantize_e4m3(widen(k, self.wl.dtype).astype(np.float32), self.wl.k_scale)
+            v = quantize_e4m3(widen(v, self.wl.dtype).astype(np.float32), self.wl.v_scale)
         if len(slots) <= 4096:
             write_kv(self.k_cache, self.v_cache, k, v, slots)
             return

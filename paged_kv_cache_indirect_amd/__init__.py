@@ -21,14 +21,14 @@ import numpy as np
 
 __all__ = [
     "PaError", "PA_OK", "PA_ERR_INVALID", "PA_ERR_NO_BLOCKS", "PA_ERR_UNSUPPORTED", "PA_ERR_HIP",
-    "PA_ERR_UNKNOWN_SEQ", "PA_F32", "PA_BF16", "LIB_PATH", "lib",
+    "PA_ERR_UNKNOWN_SEQ", "PA_F32", "PA_BF16", "PA_FP8_E4M3", "LIB_PATH", "lib",
     "pa_alloc_pool", "pa_free_pool", "pa_seq_append", "pa_seq_append_batch", "pa_seq_fork", "pa_seq_free",
-    "pa_block_tables", "pa_pool_stats", "pa_pool_pending_copies", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
-    "pa_prefill", "pa_last_error",
+    "pa_block_tables", "pa_pool_stats", "pa_pool_pending_copies", "pa_pool_set_kv_scales", "pa_write_kv",
+    "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
@@ -60,6 +60,7 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 _SIGS = {
     "pa_alloc_pool": (_i32, [ctypes.POINTER(_Layout), _vp, _vp, _vp, ctypes.POINTER(_vp)]),
     "pa_free_pool": (None, [_vp]),
+    "pa_pool_set_kv_scales": (_i32, [_vp, ctypes.c_float, ctypes.c_float]),
     "pa_seq_append": (_i32, [_vp, _i64, _i32, _vp]),
     "pa_seq_append_batch": (_i32, [_vp, _vp, _i32, _i32, _vp]),
     "pa_seq_fork": (_i32, [_vp, _i64, _i64]),
@@ -113,6 +114,8 @@ def _dtype_code(t) -> int:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return PA_FP8_E4M3
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
@@ -213,6 +216,11 @@ def pa_last_error() -> str:
 
 
 # ------------------------------------------------------------ device ops
+def pa_pool_set_kv_scales(pool: int, k_scale: float, v_scale: float) -> None:
+    """Per-tensor scales of an FP8 pool (a code c stands for value(c) * scale)."""
+    _check(lib.pa_pool_set_kv_scales(pool, float(k_scale), float(v_scale)), "pa_pool_set_kv_scales")
+
+
 def pa_write_kv(pool: int, key, value, slot_mapping, stream=None) -> None:
     """key/value: device [T, Hkv, D]; slot_mapping: device int64 [T]."""
     T = int(slot_mapping.shape[0])

@@ -59,10 +59,15 @@ constexpr float kLazyMax = 8.f;
 // far below any score, so the first real score always raises it.
 constexpr float kMaxInit = -1.0e30f;
 
-template <typename T, int D>
+// 8-bit OCP E4M3 cache element (a code; its value is decoded on load).
+struct Fp8E4M3 {
+  uint8_t bits;
+};
+
+template <typename KV, int D>
 struct RowGeom {
-  static constexpr int kElemPerChunk = 16 / static_cast<int>(sizeof(T));
-  static constexpr int kChunks = D * static_cast<int>(sizeof(T)) / 16;     // 16-byte chunks per row
+  static constexpr int kElemPerChunk = 16 / static_cast<int>(sizeof(KV));
+  static constexpr int kChunks = D * static_cast<int>(sizeof(KV)) / 16;    // 16-byte chunks per row
   static constexpr int kChunksPerLane = kChunks / kLanesPerRow;            // 1, 2 or 4
   static constexpr int kElemPerLane = kChunksPerLane * kElemPerChunk;
   // Steps (8 rows each) whose loads are issued together: 8 KiB of K+V per
@@ -129,22 +134,53 @@ __device__ __forceinline__ void pv_pair(const uint4& v0, const uint4& v1, uint32
   for (int k = 0; k < 4; ++k) acc[k] = fmaf(w1, __uint_as_float(b[k]), fmaf(w0, __uint_as_float(a[k]), acc[k]));
 }
 
+// A 16-byte chunk of cache elements as 16-byte chunks of the compute type:
+// the same chunk for fp32 / bf16 caches; for E4M3 codes, 16 codes become 16
+// bf16 values (exact: every E4M3 value is a bf16 value) in two chunks.
+template <typename KV>
+struct Widen {
+  static constexpr int kOut = 1;
+  __device__ __forceinline__ static void run(const uint4& c, uint4* o) { o[0] = c; }
+};
+template <>
+struct Widen<Fp8E4M3> {
+  static constexpr int kOut = 2;
+  // Codes 0, 1 (lo) or 2, 3 (hi) of a 32-bit word -> two bf16 in one word.
+  __device__ __forceinline__ static uint32_t lo(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  }
+  __device__ __forceinline__ static uint32_t hi(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  }
+  __device__ __forceinline__ static void run(const uint4& c, uint4* o) {
+    o[0] = make_uint4(lo(c.x), hi(c.x), lo(c.y), hi(c.y));
+    o[1] = make_uint4(lo(c.z), hi(c.z), lo(c.w), hi(c.w));
+  }
+};
+
 __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
   return (static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks)) ? blk : 0;
 }
 
-template <typename T, int D, int G>
+// T: q / out / arithmetic type (float or bf16 bits); KV: cache element type
+// (T itself, or Fp8E4M3 with bf16 T). v_scale multiplies the output (the
+// FP8 value scale; 1 otherwise); the key scale is folded into scale_log2.
+template <typename T, typename KV, int D, int G>
 __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
-    T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ kc,
-    const T* __restrict__ vc, const int32_t* __restrict__ tables,
+    T* __restrict__ out, const T* __restrict__ q, const KV* __restrict__ kc,
+    const KV* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int32_t B, int32_t Hkv,
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
-    int32_t P, int32_t per_xcd, float scale_log2) {
-  using RG = RowGeom<T, D>;
+    int32_t P, int32_t per_xcd, float scale_log2, float v_scale) {
+  using RG = RowGeom<KV, D>;
+  using WD = Widen<KV>;
   constexpr int CPL = RG::kChunksPerLane;
   constexpr int EPC = RG::kElemPerChunk;
   constexpr int EPL = RG::kElemPerLane;
+  constexpr int QPC = WD::kOut;        // compute-type chunks per cache chunk
+  constexpr int EPQ = EPC / QPC;       // elements per compute-type chunk
+  static_assert(EPQ * static_cast<int>(sizeof(T)) == 16, "compute chunks are 16 bytes");
   constexpr int U = RG::kStepsInFlight;  // even: steps are consumed in pairs
   static_assert(U % 2 == 0, "steps are consumed in pairs");
   __shared__ float s_acc[kWaves][G][D];
@@ -177,14 +213,16 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
   const int nsteps = (ntok + kRowsPerStep - 1) / kRowsPerStep;
 
   // q fragments: this lane's chunks (j, j + 8, ...) of the G heads.
-  uint4 qf[G][CPL];
+  uint4 qf[G][CPL][QPC];
   {
     const T* qb = q + (static_cast<int64_t>(b) * Hq + g * G) * D;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int i = 0; i < CPL; ++i)
-        qf[h][i] = *reinterpret_cast<const uint4*>(qb + h * D + (j + kLanesPerRow * i) * EPC);
+#pragma unroll
+        for (int qq = 0; qq < QPC; ++qq)
+          qf[h][i][qq] = *reinterpret_cast<const uint4*>(qb + h * D + (j + kLanesPerRow * i) * EPC + qq * EPQ);
   }
 
   // Block ids of the wave's range (at most 64): lane x holds logical block lb0 + x.
@@ -198,8 +236,8 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
   if (lb0 + lane < lb_end) my_blk = clamp_block(trow[lb0 + lane], num_blocks);
 
   const int64_t row_stride = static_cast<int64_t>(Hkv) * D;  // elements between slots
-  const T* kbase = kc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
-  const T* vbase = vc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
+  const KV* kbase = kc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
+  const KV* vbase = vc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -217,8 +255,8 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
     const int lb = tok >> bs_shift;
     const int blk = __builtin_amdgcn_readlane(my_blk, lb - lb0);
     const int64_t slot0 = (static_cast<int64_t>(blk) << bs_shift) + (tok & (bs - 1));
-    const T* krow = kbase + slot0 * row_stride;
-    const T* vrow = vbase + slot0 * row_stride;
+    const KV* krow = kbase + slot0 * row_stride;
+    const KV* vrow = vbase + slot0 * row_stride;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       kb[u][i] = *reinterpret_cast<const uint4*>(krow + (j + kLanesPerRow * i) * EPC);
@@ -229,14 +267,22 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
   // Two consecutive steps (rows t and t + 8 for this lane) at a time.
   auto consume_pair = [&](int st, int u) {
     float x0[G], x1[G];  // scores in log2 units
+    uint4 k0[CPL][QPC], k1[CPL][QPC];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      WD::run(kb[u][i], k0[i]);
+      WD::run(kb[u + 1][i], k1[i]);
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        a0 = chunk_dot(kb[u][i], qf[h][i], a0, T{});
-        a1 = chunk_dot(kb[u + 1][i], qf[h][i], a1, T{});
-      }
+      for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int qq = 0; qq < QPC; ++qq) {
+          a0 = chunk_dot(k0[i][qq], qf[h][i][qq], a0, T{});
+          a1 = chunk_dot(k1[i][qq], qf[h][i][qq], a1, T{});
+        }
       x0[h] = sum8(a0) * scale_log2;
       x1[h] = sum8(a1) * scale_log2;
     }
@@ -270,6 +316,12 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
         m[h] = mn;
       }
     }
+    uint4 v0[CPL][QPC], v1[CPL][QPC];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      WD::run(vb[u][i], v0[i]);
+      WD::run(vb[u + 1][i], v1[i]);
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float w0v = fast_exp2(x0[h] - m[h]);
@@ -277,7 +329,10 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
       l[h] += w0v + w1v;
       const uint32_t wpk = sizeof(T) == 2 ? pack_bf16(w0v, w1v) : 0u;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) pv_pair(vb[u][i], vb[u + 1][i], wpk, w0v, w1v, &acc[h][i * EPC], T{});
+      for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int qq = 0; qq < QPC; ++qq)
+          pv_pair(v0[i][qq], v1[i][qq], wpk, w0v, w1v, &acc[h][i * EPC + qq * EPQ], T{});
     }
   };
 
@@ -340,6 +395,7 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
       a = fmaf(f, s_acc[ww][h][d], a);
       lsum = fmaf(f, s_ml[ww][h][1], lsum);
     }
+    a *= v_scale;
     if (Pb == 1) {
       out[(static_cast<int64_t>(b) * Hq + g * G + h) * D + d] = from_f32<T>(lsum > 0.f ? a / lsum : 0.f);
     } else {
@@ -407,19 +463,21 @@ __global__ __launch_bounds__(64) void MergeKernel(T* __restrict__ out, const flo
     out[static_cast<int64_t>(bh) * D + lane * EPL + e] = from_f32<T>(a[e] * inv);
 }
 
-template <typename T, int D, int G>
+template <typename T, typename KV, int D, int G>
 hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   const int P = a.num_partitions;
   const int64_t items = static_cast<int64_t>(P) * a.B * a.Hkv;
   const int per_xcd = static_cast<int>((items + 7) / 8);
-  const float scale_log2 = a.scale * 1.4426950408889634f;
+  const bool fp8 = sizeof(KV) == 1;
+  const float scale_log2 = a.scale * (fp8 ? a.k_scale : 1.f) * 1.4426950408889634f;
+  const float v_scale = fp8 ? a.v_scale : 1.f;
   DecodeWorkspace ws = DecodeWorkspaceLayout(a.ws, a.B, a.Hq, a.D, P);
-  hipLaunchKernelGGL((DecodeKernel<T, D, G>), dim3(per_xcd * 8), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((DecodeKernel<T, KV, D, G>), dim3(per_xcd * 8), dim3(kThreads), 0, stream,
                      static_cast<T*>(a.out), static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.k_cache), static_cast<const T*>(a.v_cache),
+                     static_cast<const KV*>(a.k_cache), static_cast<const KV*>(a.v_cache),
                      a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
                      __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
-                     P, per_xcd, scale_log2);
+                     P, per_xcd, scale_log2, v_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
   hipLaunchKernelGGL((MergeKernel<T, D>), dim3(a.B * a.Hq), dim3(64), 0, stream,
@@ -428,27 +486,32 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename KV, int D>
 hipError_t DispatchG(const DecodeArgs& a, hipStream_t s) {
   switch (a.G) {
-    case 1: return LaunchTyped<T, D, 1>(a, s);
-    case 2: return LaunchTyped<T, D, 2>(a, s);
-    case 4: return LaunchTyped<T, D, 4>(a, s);
-    case 8: return LaunchTyped<T, D, 8>(a, s);
+    case 1: return LaunchTyped<T, KV, D, 1>(a, s);
+    case 2: return LaunchTyped<T, KV, D, 2>(a, s);
+    case 4: return LaunchTyped<T, KV, D, 4>(a, s);
+    case 8: return LaunchTyped<T, KV, D, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T>
 hipError_t DispatchD(const DecodeArgs& a, hipStream_t s) {
-  return a.D == 64 ? DispatchG<T, 64>(a, s) : DispatchG<T, 128>(a, s);
+  return a.D == 64 ? DispatchG<T, T, 64>(a, s) : DispatchG<T, T, 128>(a, s);
 }
 
 }  // namespace
 
 hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  return a.dtype == 0 ? DispatchD<float>(a, stream) : DispatchD<uint16_t>(a, stream);
+  switch (a.dtype) {
+    case 0: return DispatchD<float>(a, stream);
+    case 1: return DispatchD<uint16_t>(a, stream);
+    case 2: return a.D == 128 ? DispatchG<uint16_t, Fp8E4M3, 128>(a, stream) : hipErrorNotSupported;
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pa

@@ -12,6 +12,12 @@ hipError_t LaunchWriteKv(const void* key, const void* value, const int64_t* slot
                          void* v_cache, int32_t T, int64_t row_bytes, int64_t num_slots,
                          hipStream_t stream);
 
+// KV append scatter into FP8 (E4M3) pools: bf16 rows of `row_elems` elements
+// (a multiple of 16) are quantised with the pool's per-tensor scales.
+hipError_t LaunchWriteKvFp8(const void* key, const void* value, const int64_t* slots, void* k_cache,
+                            void* v_cache, int32_t T, int64_t row_elems, int64_t num_slots, float k_scale,
+                            float v_scale, hipStream_t stream);
+
 // Up to kMaxCopiesPerLaunch independent block copies (no pair reads or
 // writes a block another pair of the list writes), passed by value.
 constexpr int kMaxCopiesPerLaunch = 64;
@@ -38,6 +44,7 @@ struct DecodeArgs {
   int32_t block_size, num_blocks, max_blocks;
   int32_t max_seq_len, partition_tokens, num_partitions;
   float scale;
+  float k_scale, v_scale;  // FP8 pools: code value multipliers (1 otherwise)
   int dtype;          // pa_dtype
 };
 hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream);

@@ -19,6 +19,8 @@ struct pa_pool {
   void* k_cache;
   void* v_cache;
   pa::BlockManager bm;
+  float k_scale = 1.f;  // FP8 pools: a code c stands for value(c) * scale
+  float v_scale = 1.f;
   pa_pool(const pa_kv_layout& l, void* k, void* v, const int32_t* order)
       : layout(l), k_cache(k), v_cache(v), bm(l.num_blocks, l.block_size, order) {}
 };
@@ -37,15 +39,18 @@ pa_status FromHip(hipError_t e, const char* what) {
   return Fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int ElemBytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+int ElemBytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
 
 bool Aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 pa_status CheckLayout(const pa_kv_layout& l) {
   if (l.num_blocks <= 0 || l.block_size <= 0 || l.num_kv_heads <= 0 || l.head_dim <= 0)
     return Fail(PA_ERR_INVALID, "layout sizes must be positive");
-  if (l.dtype != PA_F32 && l.dtype != PA_BF16) return Fail(PA_ERR_UNSUPPORTED, "dtype must be PA_F32 or PA_BF16");
+  if (l.dtype != PA_F32 && l.dtype != PA_BF16 && l.dtype != PA_FP8_E4M3)
+    return Fail(PA_ERR_UNSUPPORTED, "dtype must be PA_F32, PA_BF16 or PA_FP8_E4M3");
   if (l.head_dim != 64 && l.head_dim != 128) return Fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (l.dtype == PA_FP8_E4M3 && l.head_dim != 128)
+    return Fail(PA_ERR_UNSUPPORTED, "PA_FP8_E4M3 pools need head_dim 128");
   if (l.block_size != 8 && l.block_size != 16 && l.block_size != 32)
     return Fail(PA_ERR_UNSUPPORTED, "block_size must be 8, 16 or 32");
   const int64_t slots = static_cast<int64_t>(l.num_blocks) * l.block_size;
@@ -178,6 +183,18 @@ pa_status pa_pool_pending_copies(const pa_pool* pool, int32_t* src_out, int32_t*
   });
 }
 
+pa_status pa_pool_set_kv_scales(pa_pool* pool, float k_scale, float v_scale) {
+  return Guard([&]() -> pa_status {
+    if (!pool) return Fail(PA_ERR_INVALID, "null pool");
+    if (pool->layout.dtype != PA_FP8_E4M3) return Fail(PA_ERR_UNSUPPORTED, "kv scales apply to FP8 pools only");
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale > 3.0e38f || v_scale > 3.0e38f)
+      return Fail(PA_ERR_INVALID, "scales must be finite and > 0");
+    pool->k_scale = k_scale;
+    pool->v_scale = v_scale;
+    return PA_OK;
+  });
+}
+
 pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value, const int64_t* slot_mapping,
                       int32_t T, void* stream) {
   return Guard([&]() -> pa_status {
@@ -216,12 +233,21 @@ pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value, const i
     if (st != PA_OK) return st;
     pool->bm.ClearPendingCopies();
     if (T == 0) return PA_OK;
-    const int64_t row_bytes = static_cast<int64_t>(l.num_kv_heads) * l.head_dim * ElemBytes(l.dtype);
+    const int64_t row_elems = static_cast<int64_t>(l.num_kv_heads) * l.head_dim;
+    const int64_t num_slots = static_cast<int64_t>(l.num_blocks) * l.block_size;
+    const hipStream_t st_ = static_cast<hipStream_t>(stream);
+    if (l.dtype == PA_FP8_E4M3) {
+      const int64_t chunks = static_cast<int64_t>(T) * (row_elems / 16);
+      if ((chunks + 255) / 256 >= (int64_t{1} << 31)) return Fail(PA_ERR_UNSUPPORTED, "T too large");
+      return FromHip(pa::LaunchWriteKvFp8(key, value, slot_mapping, pool->k_cache, pool->v_cache, T, row_elems,
+                                          num_slots, pool->k_scale, pool->v_scale, st_),
+                     "write_kv launch");
+    }
+    const int64_t row_bytes = row_elems * ElemBytes(l.dtype);
     const int64_t chunks = static_cast<int64_t>(T) * (row_bytes / 16);
     if ((chunks + 255) / 256 >= (int64_t{1} << 31)) return Fail(PA_ERR_UNSUPPORTED, "T too large");
-    const int64_t num_slots = static_cast<int64_t>(l.num_blocks) * l.block_size;
     return FromHip(pa::LaunchWriteKv(key, value, slot_mapping, pool->k_cache, pool->v_cache, T,
-                                     row_bytes, num_slots, static_cast<hipStream_t>(stream)),
+                                     row_bytes, num_slots, st_),
                    "write_kv launch");
   });
 }
@@ -280,6 +306,8 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
     a.partition_tokens = pt;
     a.num_partitions = P;
     a.scale = scale;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
     a.dtype = l.dtype;
     return FromHip(pa::LaunchDecode(a, static_cast<hipStream_t>(stream)), "decode launch");
   });

@@ -59,6 +59,63 @@ hipError_t LaunchCopyBlocks(void* k_cache, void* v_cache, const BlockCopyList& l
   return hipGetLastError();
 }
 
+// FP8 scatter: one thread quantises 16 elements (two 16-byte bf16 chunks of
+// the input row) into one 16-byte chunk of E4M3 codes, for K and for V.
+// Per element: fp32 quotient x / scale (IEEE division, round to nearest
+// even), clamp to ±448, then the hardware conversion (round to nearest even).
+__device__ __forceinline__ uint32_t quantize4_e4m3(uint32_t w0, uint32_t w1, float scale) {
+  const float x0 = __uint_as_float(w0 << 16), x1 = __uint_as_float(w0 & 0xFFFF0000u);
+  const float x2 = __uint_as_float(w1 << 16), x3 = __uint_as_float(w1 & 0xFFFF0000u);
+  const float lim = 448.f;
+  const float q0 = fminf(fmaxf(x0 / scale, -lim), lim);
+  const float q1 = fminf(fmaxf(x1 / scale, -lim), lim);
+  const float q2 = fminf(fmaxf(x2 / scale, -lim), lim);
+  const float q3 = fminf(fmaxf(x3 / scale, -lim), lim);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);  // bytes 0, 1
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, r, true);        // bytes 2, 3
+  return static_cast<uint32_t>(r);
+}
+
+__device__ __forceinline__ uint4 quantize16_e4m3(const uint4& a, const uint4& b, float scale) {
+  uint4 o;
+  o.x = quantize4_e4m3(a.x, a.y, scale);
+  o.y = quantize4_e4m3(a.z, a.w, scale);
+  o.z = quantize4_e4m3(b.x, b.y, scale);
+  o.w = quantize4_e4m3(b.z, b.w, scale);
+  return o;
+}
+
+__global__ __launch_bounds__(256) void WriteKvFp8Kernel(const uint4* __restrict__ key,
+                                                        const uint4* __restrict__ value,
+                                                        const int64_t* __restrict__ slots,
+                                                        uint4* __restrict__ kc, uint4* __restrict__ vc,
+                                                        int64_t total_chunks, int64_t chunks_per_row,
+                                                        int64_t num_slots, float k_scale, float v_scale) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total_chunks) return;
+  const int64_t t = idx / chunks_per_row;
+  const int64_t c = idx - t * chunks_per_row;
+  const int64_t s = slots[t];
+  if (s < 0 || s >= num_slots) return;  // padding / out of range: skipped
+  const int64_t dst = s * chunks_per_row + c;
+  kc[dst] = quantize16_e4m3(key[2 * idx], key[2 * idx + 1], k_scale);
+  vc[dst] = quantize16_e4m3(value[2 * idx], value[2 * idx + 1], v_scale);
+}
+
+hipError_t LaunchWriteKvFp8(const void* key, const void* value, const int64_t* slots, void* k_cache,
+                            void* v_cache, int32_t T, int64_t row_elems, int64_t num_slots, float k_scale,
+                            float v_scale, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int64_t cpr = row_elems / 16;
+  const int64_t total = static_cast<int64_t>(T) * cpr;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(WriteKvFp8Kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint4*>(key), static_cast<const uint4*>(value), slots,
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), total, cpr, num_slots,
+                     k_scale, v_scale);
+  return hipGetLastError();
+}
+
 hipError_t LaunchWriteKv(const void* key, const void* value, const int64_t* slots, void* k_cache,
                          void* v_cache, int32_t T, int64_t row_bytes, int64_t num_slots,
                          hipStream_t stream) {

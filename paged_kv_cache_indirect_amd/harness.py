@@ -13,11 +13,12 @@ import numpy as np
 import torch
 
 from . import (pa_alloc_pool, pa_block_tables, pa_decode, pa_decode_workspace_bytes, pa_free_pool,
-               pa_prefill, pa_seq_append, pa_seq_fork, pa_seq_free, pa_write_kv)
+               pa_pool_set_kv_scales, pa_prefill, pa_seq_append, pa_seq_fork, pa_seq_free, pa_write_kv)
 
 # NaN bit patterns used to poison never-written cache slots.
 SENTINEL_BF16 = 0x7FC1
 SENTINEL_F32 = 0x7FC00001
+SENTINEL_FP8 = 0x7F
 
 
 def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -28,9 +29,11 @@ def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
-    """Device tensor -> host float32 array, or uint16 bf16 bits."""
+    """Device tensor -> host float32 array, uint16 bf16 bits, or uint8 E4M3 codes."""
     if dtype == "bf16":
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if dtype == "fp8":
+        return t.view(torch.uint8).cpu().numpy()
     return t.cpu().numpy()
 
 
@@ -40,18 +43,23 @@ class GpuCache:
     def __init__(self, wl, device="cuda", poison: bool = True, chunk_tokens: int = 1 << 16):
         self.wl = wl
         self.device = device
-        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}[wl.cache_dtype]
         shape = (wl.num_blocks, wl.block_size, wl.Hkv, wl.D)
         self.k_cache = torch.empty(shape, dtype=tdt, device=device)
         self.v_cache = torch.empty(shape, dtype=tdt, device=device)
         if poison:
-            if wl.dtype == "bf16":
+            if wl.cache_dtype == "fp8":
+                self.k_cache.view(torch.uint8).fill_(SENTINEL_FP8)
+                self.v_cache.view(torch.uint8).fill_(SENTINEL_FP8)
+            elif wl.dtype == "bf16":
                 self.k_cache.view(torch.int16).fill_(SENTINEL_BF16)
                 self.v_cache.view(torch.int16).fill_(SENTINEL_BF16)
             else:
                 self.k_cache.view(torch.int32).fill_(SENTINEL_F32)
                 self.v_cache.view(torch.int32).fill_(SENTINEL_F32)
         self.pool = pa_alloc_pool(self.k_cache, self.v_cache, wl.free_order)
+        if wl.cache_dtype == "fp8":
+            pa_pool_set_kv_scales(self.pool, wl.k_scale, wl.v_scale)
         self.slots = {}
         for op in wl.ops:
             if op[0] == "append":

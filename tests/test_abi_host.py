@@ -306,3 +306,20 @@ def test_block_manager_under_asan_ubsan(tmp_path):
                            env=env, timeout=120)
         assert p.returncode == 0, p.stderr[-3000:]
         assert p.stdout.strip().splitlines() == _model_lines(nb, bs, order, ops)
+
+
+def test_fp8_pool_rules():
+    assert make_pool(16, 16, hkv=2, d=64, dtype=pa.PA_FP8_E4M3)[0] == pa.PA_ERR_UNSUPPORTED   # needs D 128
+    st, pool = make_pool(16, 16, hkv=2, d=128, dtype=pa.PA_FP8_E4M3)
+    assert st == 0
+    assert pa.lib.pa_pool_set_kv_scales(pool, 0.5, 0.25) == pa.PA_OK
+    for bad in ((0.0, 1.0), (1.0, -1.0), (float("nan"), 1.0), (float("inf"), 1.0)):
+        assert pa.lib.pa_pool_set_kv_scales(pool, *bad) == pa.PA_ERR_INVALID, bad
+    dummy = 0x40000
+    # prefill is bf16-only; an FP8 pool is refused before any launch
+    assert pa.lib.pa_prefill(pool, dummy, dummy, dummy, dummy, 4, dummy, 2, 4, 16, 0.1, None) \
+        == pa.PA_ERR_UNSUPPORTED
+    pa.pa_free_pool(pool)
+    st, bpool = make_pool(16, 16, hkv=2, d=128, dtype=pa.PA_BF16)
+    assert pa.lib.pa_pool_set_kv_scales(bpool, 0.5, 0.5) == pa.PA_ERR_UNSUPPORTED
+    pa.pa_free_pool(bpool)

@@ -38,6 +38,9 @@ a parity case, not a benchmark configuration):
 * ``prefix_cow`` - 32 seqs forked from one 1000-token prefix (1000 = 62·16
                + 8: the last prefix block is half full) plus suffixes
                U[0,300], 32/8, D 128, bf16, bs 16.
+* ``gqa8b_fp8`` - the ``gqa8b`` shape (seed 1006) with an FP8 (E4M3) cache:
+               bf16 rows quantised with per-tensor scales k 0.0137, v 0.0129
+               (N(0,1) values up to about 6 map inside ±448).
 """
 from __future__ import annotations
 
@@ -99,7 +102,7 @@ class Workload:
     Hkv: int
     D: int
     block_size: int
-    dtype: str                     # "f32" | "bf16"
+    dtype: str                     # "f32" | "bf16": q, out and the K/V rows handed to the scatter
     seed: int
     seq_lens: np.ndarray           # int32 [B], cache length at call time
     num_blocks: int
@@ -109,6 +112,9 @@ class Workload:
     q_lens: Optional[np.ndarray] = None     # prefill: int32 [B] query-chunk length
     partition_tokens: int = 512
     prefix_len: int = 0            # shared-prefix workloads
+    kv_dtype: str = ""             # cache element type: "" = dtype, or "fp8" (E4M3 codes, bf16 rows in)
+    k_scale: float = 1.0           # FP8 caches: per-tensor scales (code value * scale)
+    v_scale: float = 1.0
     _cache: Dict[int, Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict, repr=False)
     _prefix: Optional[Tuple[np.ndarray, np.ndarray]] = field(default=None, repr=False)
 
@@ -116,6 +122,14 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.cache_dtype == "fp8" else self.elem_bytes
 
     @property
     def G(self) -> int:
@@ -202,13 +216,13 @@ class Workload:
     # ---------------------------------------------------------- byte counts
     def kv_bytes(self) -> int:
         """Logical K+V bytes one call reads: sum_b L_b * Hkv * D * 2 * elem."""
-        return int(self.seq_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * self.elem_bytes
+        return int(self.seq_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * self.kv_elem_bytes
 
     def unique_kv_bytes(self) -> int:
         if not self.prefix_len:
             return self.kv_bytes()
         tok = int(self.seq_lens.astype(np.int64).sum()) - (self.B - 1) * self.prefix_len
-        return tok * self.Hkv * self.D * 2 * self.elem_bytes
+        return tok * self.Hkv * self.D * 2 * self.kv_elem_bytes
 
 
 def _pool(seed: int, need: int, factor: float, fixed: Optional[int]) -> Tuple[int, np.ndarray]:
@@ -219,8 +233,10 @@ def _pool(seed: int, need: int, factor: float, fixed: Optional[int]) -> Tuple[in
 
 def make_decode(name: str, lens: Sequence[int], Hq: int, Hkv: int, D: int, block_size: int,
                 dtype: str, seed: int, pool_factor: float = 1.1, num_blocks: Optional[int] = None,
-                partition_tokens: int = 512, scale: Optional[float] = None) -> Workload:
-    """Decode workload: one query token per sequence over a paged cache of ``lens``."""
+                partition_tokens: int = 512, scale: Optional[float] = None, kv_dtype: str = "",
+                k_scale: float = 1.0, v_scale: float = 1.0) -> Workload:
+    """Decode workload: one query token per sequence over a paged cache of ``lens``.
+    ``kv_dtype="fp8"`` stores the bf16 rows as E4M3 codes with the given scales."""
     lens = np.asarray(lens, dtype=np.int32)
     need = int(sum(-(-int(L) // block_size) for L in lens))
     nb, perm = _pool(seed, need, pool_factor, num_blocks)
@@ -229,7 +245,8 @@ def make_decode(name: str, lens: Sequence[int], Hq: int, Hkv: int, D: int, block
                     block_size=block_size, dtype=dtype, seed=seed, seq_lens=lens,
                     num_blocks=nb, free_order=perm, ops=ops,
                     scale=scale if scale is not None else 1.0 / math.sqrt(D),
-                    partition_tokens=partition_tokens)
+                    partition_tokens=partition_tokens, kv_dtype=kv_dtype, k_scale=k_scale,
+                    v_scale=v_scale)
 
 
 def make_prefix_share(name: str, B: int, prefix_len: int, suffix_lens: Sequence[int], Hq: int,
@@ -300,6 +317,11 @@ def config(name: str) -> Workload:
         s = 1003
         return make_prefix_share("prefix", 128, 2048, _uniform_ints(s, 0, 1024, 128), Hq=32,
                                  Hkv=8, D=128, block_size=16, dtype="bf16", seed=s)
+    if name == "gqa8b_fp8":
+        s = 1006
+        return make_decode("gqa8b_fp8", _uniform_ints(s, 512, 4096, 64), Hq=32, Hkv=8, D=128,
+                           block_size=16, dtype="bf16", seed=s, kv_dtype="fp8", k_scale=0.0137,
+                           v_scale=0.0129)
     if name == "prefix_cow":
         s = 1005
         return make_prefix_share("prefix_cow", 32, 1000, _uniform_ints(s, 0, 300, 32), Hq=32,
