@@ -28,6 +28,8 @@ against 8 TB/s HBM. ``cpu_baseline`` is the CPU oracle
 over U[0, 7680] cached tokens, bs 32) timed the same way against the bf16
 MFMA peak. ``decode_fp8`` times pa_decode over an FP8 (E4M3) pool of the same
 batch shape (seed 1006), with the bytes it must read (1-byte K/V codes).
+``mixed_step`` runs serving steps that mix decode and chunked prefill
+(pa_step eager, and the same step captured once as a HIP graph and replayed).
 """
 from __future__ import annotations
 
@@ -245,6 +247,62 @@ def run_decode_fp8(args):
     }
 
 
+# ----------------------------------------------------------------- mixed step
+def run_mixed(args):
+    """Mixed serving steps (decode + chunked prefill + the scatter of all new
+    rows) through pa_step (eager) and through a captured step graph, each on
+    its own pool; GPU time per step from HIP events around the launch, host
+    time per step (block manager appends, table export, metadata uploads,
+    launch) by clock; the steps' K/V rows and queries are staged in HBM first."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_indirect_amd import harness
+
+    wl = W.config("mixed")
+    p = wl.plan
+    res = {}
+    for mode in ("eager", "graph"):
+        log(f"[bench] mixed step ({mode}): Bd={p['Bd']} Bp={p['Bp']} chunk={p['chunk']} steps={p['steps']}")
+        run = harness.MixedRunner(wl, use_graph=(mode == "graph"))
+        run.stage_inputs()                           # step inputs resident in HBM before timing
+        stream = torch.cuda.current_stream()
+        gpu_ms, host_ms, steps_bytes, steps_flops = [], [], [], []
+        for s in range(p["steps"]):
+            t0 = time.perf_counter()
+            run.prepare(s)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run.launch()
+            e1.record(stream)
+            host_ms.append((time.perf_counter() - t0) * 1e3)
+            torch.cuda.synchronize()
+            gpu_ms.append(e0.elapsed_time(e1))
+            lens = run.host_lens
+            dl = lens[:p["Bd"]].astype(np.int64)
+            steps_bytes.append(int(dl.sum()) * wl.Hkv * wl.D * 2 * wl.elem_bytes + run.T * wl.Hkv * wl.D * 2 * 2 *
+                               wl.elem_bytes)
+            ctx = lens[p["Bd"]:].astype(np.int64) - p["chunk"]
+            n = p["chunk"]
+            steps_flops.append(4.0 * wl.D * wl.Hq * float(np.sum(n * ctx + n * (n + 1) // 2)))
+        run.close()
+        timed = slice(2, None)                       # the first two steps warm up (and capture)
+        t = float(np.mean(gpu_ms[timed])) * 1e-3
+        floor = float(np.mean(steps_bytes[timed])) / (HBM_PEAK_GBPS * 1e9) + \
+            float(np.mean(steps_flops[timed])) / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        res[mode] = {"gpu_us_per_step": t * 1e6, "host_us_per_step": float(np.mean(host_ms[timed])) * 1e3,
+                     "roofline_floor_us": floor * 1e6, "frac_of_floor": floor / t}
+    res["workload"] = ("mixed serving step: 56 decode sequences U[512,4096] + 8 chunked-prefill sequences "
+                       "(256-token chunks over cached context U[0,4096]), Hq 32 / Hkv 8, D 128, bf16, bs 16 "
+                       "(seed 1007); step = scatter of all new rows + decode + prefill")
+    res["floor"] = ("decode K/V + scatter bytes at 8 TB/s plus causal prefill flops at 2.5 PFLOP/s, "
+                    "per step")
+    log(f"[bench] mixed step: eager {res['eager']['gpu_us_per_step']:.1f} us, "
+        f"graph {res['graph']['gpu_us_per_step']:.1f} us")
+    return res
+
+
 # -------------------------------------------------------------------- prefill
 def causal_flops(wl) -> float:
     """4 * D * Hq * sum_b sum_i (ctx_b + i + 1): QK^T and PV over the
@@ -352,6 +410,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache decode leg")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-step (eager vs graph) leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the decode steps, run one plain 1 GiB device-to-device copy: "
                          "the reference that scales hardware byte counters (FETCH_SIZE, WRITE_SIZE)")
@@ -387,6 +446,7 @@ def main() -> int:
         f"({100 * frac:.1f}% of HBM peak); step {dec['ms_per_step'] * 1e3:.1f} us")
     pre = None if args.no_prefill else run_prefill(args)[1]
     fp8 = None if args.no_fp8 else run_decode_fp8(args)
+    mixed = None if args.no_mixed else run_mixed(args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, wl)
 
     line = {
@@ -431,6 +491,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "prefill": pre,
         "decode_fp8": fp8,
+        "mixed_step": mixed,
     }
     print(json.dumps(line), flush=True)
     return 0

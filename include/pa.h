@@ -257,6 +257,78 @@ pa_status pa_prefill(pa_pool* pool, void* out, const void* q, const int32_t* cu_
                      const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                      int32_t B, int32_t num_q_heads, int32_t max_q_len, float scale, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* One mixed step, eager or as a replayable HIP graph                         */
+/* ------------------------------------------------------------------------ */
+
+/* A serving step mixes the decode of running sequences with prefill chunks
+ * of new ones in one batch ("vLLM 生产级落地深剖", musen-ai.com, §2; chunked
+ * prefill: "LLM推理优化：技术原理解析总览", §2.3). One step is: the scatter of
+ * every new K/V row (decode tokens and prefill chunks together), then decode
+ * over the decode sequences, then prefill over the chunk sequences, all on
+ * one stream. The fields mean what the same-named arguments of
+ * pa_write_kv, pa_decode and pa_prefill mean; a part whose count is 0
+ * (num_new_tokens, dec_batch, pre_batch) is skipped and its pointers may be
+ * NULL. dec_out and pre_out must not overlap. */
+typedef struct {
+  /* scatter (pa_write_kv) */
+  const void* key;              /* device [num_new_tokens, Hkv, D] */
+  const void* value;            /* device [num_new_tokens, Hkv, D] */
+  const int64_t* slot_mapping;  /* device [num_new_tokens]; -1 rows are skipped */
+  int32_t num_new_tokens;
+  /* shared */
+  int32_t num_q_heads;
+  float scale;
+  int32_t max_blocks;           /* row width of both block-table arrays */
+  /* decode (pa_decode) */
+  void* dec_out;
+  const void* dec_q;
+  const int32_t* dec_block_tables;
+  const int32_t* dec_seq_lens;
+  int32_t dec_batch;
+  int32_t dec_max_seq_len;
+  int32_t partition_tokens;
+  void* workspace;
+  size_t workspace_bytes;
+  /* prefill (pa_prefill) */
+  void* pre_out;
+  const void* pre_q;
+  const int32_t* pre_cu_q_lens;
+  const int32_t* pre_block_tables;
+  const int32_t* pre_seq_lens;
+  int32_t pre_batch;
+  int32_t pre_max_q_len;
+} pa_step_desc;
+
+/* Enqueue one mixed step on `stream`: pending copy-on-write copies, the
+ * scatter, decode, prefill. Every part is validated before anything is
+ * launched. Errors: those of pa_write_kv, pa_decode and pa_prefill. */
+pa_status pa_step(pa_pool* pool, const pa_step_desc* desc, void* stream);
+
+typedef struct pa_step_graph pa_step_graph; /* opaque, library-owned */
+
+/* Capture the launches of one mixed step (pa_step without copies) into an
+ * instantiated HIP graph. Sizes, grid shapes and every pointer in `desc` are
+ * frozen; the device buffers they name are read when the graph runs, so the
+ * caller updates their contents (new rows, slots, tables, lengths, queries,
+ * cu_q_lens) between launches. Decode rows with length 0 give zero output and
+ * slots of -1 skip their rows, so a frozen batch can carry idle entries.
+ * The pool must have no pending copy-on-write copies at capture. The graph
+ * refers to the pool and to the caller's buffers: destroy it before freeing
+ * them. Nothing is launched by this call. Errors: those of pa_step;
+ * PA_ERR_INVALID when copies are pending; PA_ERR_HIP (capture or
+ * instantiation failed). */
+pa_status pa_step_graph_create(pa_pool* pool, const pa_step_desc* desc, pa_step_graph** out);
+
+/* Launch the captured step on `stream`, after enqueueing the pool's pending
+ * copy-on-write copies (they change from step to step, so they stay outside
+ * the graph). Errors: PA_ERR_INVALID (null graph), PA_ERR_HIP. */
+pa_status pa_step_graph_launch(pa_step_graph* graph, void* stream);
+
+/* Release the graph (NULL is ignored). Call it once the graph's launches
+ * have completed (synchronise their stream first). */
+void pa_step_graph_destroy(pa_step_graph* graph);
+
 /* Thread-local text describing the last non-OK status returned on this
  * thread ("" if none). Valid until the next call on this thread. */
 const char* pa_last_error(void);

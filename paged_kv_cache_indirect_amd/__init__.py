@@ -24,7 +24,8 @@ __all__ = [
     "PA_ERR_UNKNOWN_SEQ", "PA_F32", "PA_BF16", "PA_FP8_E4M3", "LIB_PATH", "lib",
     "pa_alloc_pool", "pa_free_pool", "pa_seq_append", "pa_seq_append_batch", "pa_seq_fork", "pa_seq_free",
     "pa_block_tables", "pa_pool_stats", "pa_pool_pending_copies", "pa_pool_set_kv_scales", "pa_write_kv",
-    "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error",
+    "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error", "StepDesc", "pa_step",
+    "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
@@ -56,10 +57,27 @@ class _Stats(ctypes.Structure):
                 ("filled_slots", ctypes.c_int64), ("allocated_slots", ctypes.c_int64)]
 
 
+class _StepDesc(ctypes.Structure):
+    _fields_ = [("key", ctypes.c_void_p), ("value", ctypes.c_void_p), ("slot_mapping", ctypes.c_void_p),
+                ("num_new_tokens", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("max_blocks", ctypes.c_int32),
+                ("dec_out", ctypes.c_void_p), ("dec_q", ctypes.c_void_p), ("dec_block_tables", ctypes.c_void_p),
+                ("dec_seq_lens", ctypes.c_void_p), ("dec_batch", ctypes.c_int32),
+                ("dec_max_seq_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("pre_out", ctypes.c_void_p), ("pre_q", ctypes.c_void_p), ("pre_cu_q_lens", ctypes.c_void_p),
+                ("pre_block_tables", ctypes.c_void_p), ("pre_seq_lens", ctypes.c_void_p),
+                ("pre_batch", ctypes.c_int32), ("pre_max_q_len", ctypes.c_int32)]
+
+
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "pa_alloc_pool": (_i32, [ctypes.POINTER(_Layout), _vp, _vp, _vp, ctypes.POINTER(_vp)]),
     "pa_free_pool": (None, [_vp]),
+    "pa_step": (_i32, [_vp, ctypes.POINTER(_StepDesc), _vp]),
+    "pa_step_graph_create": (_i32, [_vp, ctypes.POINTER(_StepDesc), ctypes.POINTER(_vp)]),
+    "pa_step_graph_launch": (_i32, [_vp, _vp]),
+    "pa_step_graph_destroy": (None, [_vp]),
     "pa_pool_set_kv_scales": (_i32, [_vp, ctypes.c_float, ctypes.c_float]),
     "pa_seq_append": (_i32, [_vp, _i64, _i32, _vp]),
     "pa_seq_append_batch": (_i32, [_vp, _vp, _i32, _i32, _vp]),
@@ -260,3 +278,56 @@ def pa_prefill(pool: int, out, q, cu_q_lens, block_tables, seq_lens, scale: floa
                           int(block_tables.shape[1]), _dptr(seq_lens), B, Hq, int(max_q_len),
                           float(scale), _stream(stream)),
            "pa_prefill")
+
+
+class StepDesc:
+    """One mixed step's buffers (torch device tensors, or None for a part
+    that is skipped), marshalled into the C struct ``pa_step_desc``.
+
+    key/value [T, Hkv, D] and slot_mapping int64 [T] feed the scatter;
+    dec_out/dec_q [Bd, Hq, D], dec_block_tables int32 [Bd, max_blocks] and
+    dec_seq_lens int32 [Bd] the decode; pre_out/pre_q [Tp, Hq, D],
+    pre_cu_q_lens int32 [Bp + 1], pre_block_tables int32 [Bp, max_blocks] and
+    pre_seq_lens int32 [Bp] the prefill. The tensors are kept referenced
+    here, so a graph captured from this description keeps valid pointers
+    while the object lives."""
+
+    def __init__(self, *, num_q_heads: int, scale: float, max_blocks: int, key=None, value=None,
+                 slot_mapping=None, dec_out=None, dec_q=None, dec_block_tables=None, dec_seq_lens=None,
+                 dec_max_seq_len: int = 0, partition_tokens: int = 0, workspace=None, pre_out=None, pre_q=None,
+                 pre_cu_q_lens=None, pre_block_tables=None, pre_seq_lens=None, pre_max_q_len: int = 0):
+        self.tensors = [key, value, slot_mapping, dec_out, dec_q, dec_block_tables, dec_seq_lens, workspace,
+                        pre_out, pre_q, pre_cu_q_lens, pre_block_tables, pre_seq_lens]
+        d = _StepDesc()
+        d.key, d.value, d.slot_mapping = _dptr(key), _dptr(value), _dptr(slot_mapping)
+        d.num_new_tokens = 0 if slot_mapping is None else int(slot_mapping.shape[0])
+        d.num_q_heads, d.scale, d.max_blocks = int(num_q_heads), float(scale), int(max_blocks)
+        d.dec_out, d.dec_q = _dptr(dec_out), _dptr(dec_q)
+        d.dec_block_tables, d.dec_seq_lens = _dptr(dec_block_tables), _dptr(dec_seq_lens)
+        d.dec_batch = 0 if dec_seq_lens is None else int(dec_seq_lens.shape[0])
+        d.dec_max_seq_len, d.partition_tokens = int(dec_max_seq_len), int(partition_tokens)
+        d.workspace = _dptr(workspace)
+        d.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        d.pre_out, d.pre_q, d.pre_cu_q_lens = _dptr(pre_out), _dptr(pre_q), _dptr(pre_cu_q_lens)
+        d.pre_block_tables, d.pre_seq_lens = _dptr(pre_block_tables), _dptr(pre_seq_lens)
+        d.pre_batch = 0 if pre_seq_lens is None else int(pre_seq_lens.shape[0])
+        d.pre_max_q_len = int(pre_max_q_len)
+        self.c = d
+
+
+def pa_step(pool: int, desc: StepDesc, stream=None) -> None:
+    _check(lib.pa_step(pool, ctypes.byref(desc.c), _stream(stream)), "pa_step")
+
+
+def pa_step_graph_create(pool: int, desc: StepDesc) -> int:
+    g = _vp()
+    _check(lib.pa_step_graph_create(pool, ctypes.byref(desc.c), ctypes.byref(g)), "pa_step_graph_create")
+    return g.value
+
+
+def pa_step_graph_launch(graph: int, stream=None) -> None:
+    _check(lib.pa_step_graph_launch(graph, _stream(stream)), "pa_step_graph_launch")
+
+
+def pa_step_graph_destroy(graph: int) -> None:
+    lib.pa_step_graph_destroy(graph)

@@ -64,6 +64,14 @@ struct PrefillArgs {
 };
 hipError_t LaunchPrefill(const PrefillArgs& a, hipStream_t stream);
 
+// Prefill work items: (kv head, tile of kPrefillRows query rows = positions x
+// G heads, sequence), for the grid-size check made before any launch.
+constexpr int kPrefillRows = 256;
+inline int64_t PrefillWorkItems(int32_t Hkv, int32_t G, int32_t B, int32_t max_q_len) {
+  const int32_t rows_per_tile = kPrefillRows / G;
+  return static_cast<int64_t>(Hkv) * ((max_q_len + rows_per_tile - 1) / rows_per_tile) * B;
+}
+
 // Grid / workspace geometry shared by the API layer and the launchers.
 inline int32_t DecodePartitions(int32_t max_seq_len, int32_t partition_tokens) {
   int32_t p = (max_seq_len + partition_tokens - 1) / partition_tokens;

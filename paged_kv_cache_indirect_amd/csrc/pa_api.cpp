@@ -25,6 +25,12 @@ struct pa_pool {
       : layout(l), k_cache(k), v_cache(v), bm(l.num_blocks, l.block_size, order) {}
 };
 
+struct pa_step_graph {
+  pa_pool* pool;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
 namespace {
 
 thread_local std::string g_error;
@@ -83,6 +89,199 @@ pa_status CheckHeads(const pa_pool* pool, int32_t Hq, int32_t* G) {
   *G = Hq / Hkv;
   if (*G != 1 && *G != 2 && *G != 4 && *G != 8)
     return Fail(PA_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads must be 1, 2, 4 or 8");
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------- device ops
+// Validation is kept apart from enqueueing, so that a composite call
+// (pa_step) checks every part before it launches anything.
+
+// Copy-on-write copies recorded by earlier appends, in recorded order.
+// Consecutive copies share a launch until one touches a block that an
+// earlier copy of the launch writes, or writes a block it reads.
+pa_status FlushCopies(pa_pool* pool, hipStream_t stream) {
+  const pa_kv_layout& l = pool->layout;
+  const int64_t block_bytes =
+      static_cast<int64_t>(l.block_size) * l.num_kv_heads * l.head_dim * ElemBytes(l.dtype);
+  pa::BlockCopyList list{};
+  auto flush = [&]() -> pa_status {
+    const pa_status st = FromHip(pa::LaunchCopyBlocks(pool->k_cache, pool->v_cache, list, block_bytes, stream),
+                                 "copy-on-write block copy launch");
+    list.n = 0;
+    return st;
+  };
+  for (const auto& cp : pool->bm.pending_copies()) {
+    bool depends = list.n == pa::kMaxCopiesPerLaunch;
+    for (int32_t i = 0; i < list.n && !depends; ++i)
+      depends = cp.first == list.dst[i] || cp.second == list.dst[i] || cp.second == list.src[i];
+    if (depends) {
+      const pa_status st = flush();
+      if (st != PA_OK) return st;
+    }
+    list.src[list.n] = cp.first;
+    list.dst[list.n] = cp.second;
+    ++list.n;
+  }
+  const pa_status st = flush();
+  if (st != PA_OK) return st;
+  pool->bm.ClearPendingCopies();
+  return PA_OK;
+}
+
+struct WriteCall {
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+  int32_t T;
+};
+
+pa_status CheckWrite(const pa_pool& pool, const WriteCall& w) {
+  if (w.T < 0) return Fail(PA_ERR_INVALID, "T must be >= 0");
+  if (w.T > 0 && (!w.key || !w.value || !w.slots)) return Fail(PA_ERR_INVALID, "null argument");
+  if (w.T > 0 && (!Aligned16(w.key) || !Aligned16(w.value)))
+    return Fail(PA_ERR_INVALID, "key and value must be 16-byte aligned");
+  const pa_kv_layout& l = pool.layout;
+  const int64_t row_elems = static_cast<int64_t>(l.num_kv_heads) * l.head_dim;
+  const int64_t chunks = static_cast<int64_t>(w.T) * (row_elems * ElemBytes(l.dtype) / 16);
+  if ((chunks + 255) / 256 >= (int64_t{1} << 31)) return Fail(PA_ERR_UNSUPPORTED, "T too large");
+  return PA_OK;
+}
+
+// The scatter itself (copies are flushed separately); arguments checked.
+pa_status EnqueueWrite(const pa_pool& pool, const WriteCall& w, hipStream_t st) {
+  if (w.T == 0) return PA_OK;
+  const pa_kv_layout& l = pool.layout;
+  const int64_t row_elems = static_cast<int64_t>(l.num_kv_heads) * l.head_dim;
+  const int64_t num_slots = static_cast<int64_t>(l.num_blocks) * l.block_size;
+  if (l.dtype == PA_FP8_E4M3)
+    return FromHip(pa::LaunchWriteKvFp8(w.key, w.value, w.slots, pool.k_cache, pool.v_cache, w.T, row_elems,
+                                        num_slots, pool.k_scale, pool.v_scale, st),
+                   "write_kv launch");
+  return FromHip(pa::LaunchWriteKv(w.key, w.value, w.slots, pool.k_cache, pool.v_cache, w.T,
+                                   row_elems * ElemBytes(l.dtype), num_slots, st),
+                 "write_kv launch");
+}
+
+// Checks a decode call and fills its launch arguments; *run stays false for
+// an empty batch (nothing to launch).
+pa_status PrepareDecode(const pa_pool& pool, void* out, const void* q, const int32_t* block_tables,
+                        int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t num_q_heads, float scale,
+                        int32_t max_seq_len, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                        pa::DecodeArgs* a, bool* run) {
+  *run = false;
+  if (B < 0 || max_blocks < 0 || max_seq_len < 0 || partition_tokens < 0)
+    return Fail(PA_ERR_INVALID, "negative size argument");
+  int32_t G = 0;
+  pa_status s = CheckHeads(&pool, num_q_heads, &G);
+  if (s != PA_OK) return s;
+  if (B == 0) return PA_OK;
+  if (!out || !q || !block_tables || !seq_lens) return Fail(PA_ERR_INVALID, "null argument");
+  if (!Aligned16(out) || !Aligned16(q)) return Fail(PA_ERR_INVALID, "q and out must be 16-byte aligned");
+  const pa_kv_layout& l = pool.layout;
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * l.block_size)
+    return Fail(PA_ERR_INVALID, "max_seq_len exceeds max_blocks * block_size");
+  const int32_t pt = partition_tokens == 0 ? 512 : partition_tokens;
+  if (pt % 64 || pt > 2048)
+    return Fail(PA_ERR_UNSUPPORTED, "partition_tokens must be a multiple of 64, at most 2048");
+  const int32_t P = pa::DecodePartitions(max_seq_len, pt);
+  if (static_cast<int64_t>(P) * B * l.num_kv_heads >= (int64_t{1} << 31) - 8)
+    return Fail(PA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = pa::DecodeWorkspaceBytes(B, num_q_heads, l.head_dim, P);
+  if (need && (!workspace || workspace_bytes < need))
+    return Fail(PA_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+  if (need && !Aligned16(workspace)) return Fail(PA_ERR_INVALID, "workspace must be 16-byte aligned");
+  a->out = out;
+  a->q = q;
+  a->k_cache = pool.k_cache;
+  a->v_cache = pool.v_cache;
+  a->block_tables = block_tables;
+  a->seq_lens = seq_lens;
+  a->ws = workspace;
+  a->B = B;
+  a->Hq = num_q_heads;
+  a->Hkv = l.num_kv_heads;
+  a->D = l.head_dim;
+  a->G = G;
+  a->block_size = l.block_size;
+  a->num_blocks = l.num_blocks;
+  a->max_blocks = max_blocks;
+  a->max_seq_len = max_seq_len;
+  a->partition_tokens = pt;
+  a->num_partitions = P;
+  a->scale = scale;
+  a->k_scale = pool.k_scale;
+  a->v_scale = pool.v_scale;
+  a->dtype = l.dtype;
+  *run = true;
+  return PA_OK;
+}
+
+pa_status PreparePrefill(const pa_pool& pool, void* out, const void* q, const int32_t* cu_q_lens,
+                         const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+                         int32_t num_q_heads, int32_t max_q_len, float scale, pa::PrefillArgs* a, bool* run) {
+  *run = false;
+  if (B < 0 || max_blocks < 0 || max_q_len < 0) return Fail(PA_ERR_INVALID, "negative size argument");
+  int32_t G = 0;
+  pa_status s = CheckHeads(&pool, num_q_heads, &G);
+  if (s != PA_OK) return s;
+  const pa_kv_layout& l = pool.layout;
+  if (l.dtype != PA_BF16) return Fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 pools only");
+  if (B == 0 || max_q_len == 0) return PA_OK;
+  if (!out || !q || !cu_q_lens || !block_tables || !seq_lens) return Fail(PA_ERR_INVALID, "null argument");
+  if (!Aligned16(out) || !Aligned16(q)) return Fail(PA_ERR_INVALID, "q and out must be 16-byte aligned");
+  if (pa::PrefillWorkItems(l.num_kv_heads, G, B, max_q_len) >= (int64_t{1} << 31) - 8)
+    return Fail(PA_ERR_UNSUPPORTED, "grid too large");
+  a->out = out;
+  a->q = q;
+  a->k_cache = pool.k_cache;
+  a->v_cache = pool.v_cache;
+  a->cu_q_lens = cu_q_lens;
+  a->block_tables = block_tables;
+  a->seq_lens = seq_lens;
+  a->B = B;
+  a->Hq = num_q_heads;
+  a->Hkv = l.num_kv_heads;
+  a->D = l.head_dim;
+  a->G = G;
+  a->block_size = l.block_size;
+  a->num_blocks = l.num_blocks;
+  a->max_blocks = max_blocks;
+  a->max_q_len = max_q_len;
+  a->scale = scale;
+  *run = true;
+  return PA_OK;
+}
+
+// A mixed step: the scatter of every new row, then decode, then prefill.
+struct StepPlan {
+  WriteCall write{};
+  pa::DecodeArgs dec{};
+  pa::PrefillArgs pre{};
+  bool run_dec = false;
+  bool run_pre = false;
+};
+
+pa_status PrepareStep(const pa_pool& pool, const pa_step_desc& d, StepPlan* plan) {
+  plan->write = WriteCall{d.key, d.value, d.slot_mapping, d.num_new_tokens};
+  pa_status s = CheckWrite(pool, plan->write);
+  if (s != PA_OK) return s;
+  s = PrepareDecode(pool, d.dec_out, d.dec_q, d.dec_block_tables, d.max_blocks, d.dec_seq_lens, d.dec_batch,
+                    d.num_q_heads, d.scale, d.dec_max_seq_len, d.partition_tokens, d.workspace,
+                    d.workspace_bytes, &plan->dec, &plan->run_dec);
+  if (s != PA_OK) return s;
+  return PreparePrefill(pool, d.pre_out, d.pre_q, d.pre_cu_q_lens, d.pre_block_tables, d.max_blocks,
+                        d.pre_seq_lens, d.pre_batch, d.num_q_heads, d.pre_max_q_len, d.scale, &plan->pre,
+                        &plan->run_pre);
+}
+
+pa_status EnqueueStep(const pa_pool& pool, const StepPlan& plan, hipStream_t st) {
+  pa_status s = EnqueueWrite(pool, plan.write, st);
+  if (s != PA_OK) return s;
+  if (plan.run_dec) {
+    s = FromHip(pa::LaunchDecode(plan.dec, st), "decode launch");
+    if (s != PA_OK) return s;
+  }
+  if (plan.run_pre) return FromHip(pa::LaunchPrefill(plan.pre, st), "prefill launch");
   return PA_OK;
 }
 
@@ -199,56 +398,13 @@ pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value, const i
                       int32_t T, void* stream) {
   return Guard([&]() -> pa_status {
     if (!pool) return Fail(PA_ERR_INVALID, "null pool");
-    if (T < 0) return Fail(PA_ERR_INVALID, "T must be >= 0");
-    if (T > 0 && (!key || !value || !slot_mapping)) return Fail(PA_ERR_INVALID, "null argument");
-    if (T > 0 && (!Aligned16(key) || !Aligned16(value)))
-      return Fail(PA_ERR_INVALID, "key and value must be 16-byte aligned");
-    // Copy-on-write copies recorded by earlier appends run first, in order.
-    // Consecutive copies share a launch until one touches a block that an
-    // earlier copy of the launch writes, or writes a block it reads.
-    const pa_kv_layout& l = pool->layout;
-    const int64_t block_bytes =
-        static_cast<int64_t>(l.block_size) * l.num_kv_heads * l.head_dim * ElemBytes(l.dtype);
-    pa::BlockCopyList list{};
-    auto flush = [&]() -> pa_status {
-      const pa_status st = FromHip(pa::LaunchCopyBlocks(pool->k_cache, pool->v_cache, list, block_bytes,
-                                                        static_cast<hipStream_t>(stream)),
-                                   "copy-on-write block copy launch");
-      list.n = 0;
-      return st;
-    };
-    for (const auto& cp : pool->bm.pending_copies()) {
-      bool depends = list.n == pa::kMaxCopiesPerLaunch;
-      for (int32_t i = 0; i < list.n && !depends; ++i)
-        depends = cp.first == list.dst[i] || cp.second == list.dst[i] || cp.second == list.src[i];
-      if (depends) {
-        const pa_status st = flush();
-        if (st != PA_OK) return st;
-      }
-      list.src[list.n] = cp.first;
-      list.dst[list.n] = cp.second;
-      ++list.n;
-    }
-    const pa_status st = flush();
-    if (st != PA_OK) return st;
-    pool->bm.ClearPendingCopies();
-    if (T == 0) return PA_OK;
-    const int64_t row_elems = static_cast<int64_t>(l.num_kv_heads) * l.head_dim;
-    const int64_t num_slots = static_cast<int64_t>(l.num_blocks) * l.block_size;
-    const hipStream_t st_ = static_cast<hipStream_t>(stream);
-    if (l.dtype == PA_FP8_E4M3) {
-      const int64_t chunks = static_cast<int64_t>(T) * (row_elems / 16);
-      if ((chunks + 255) / 256 >= (int64_t{1} << 31)) return Fail(PA_ERR_UNSUPPORTED, "T too large");
-      return FromHip(pa::LaunchWriteKvFp8(key, value, slot_mapping, pool->k_cache, pool->v_cache, T, row_elems,
-                                          num_slots, pool->k_scale, pool->v_scale, st_),
-                     "write_kv launch");
-    }
-    const int64_t row_bytes = row_elems * ElemBytes(l.dtype);
-    const int64_t chunks = static_cast<int64_t>(T) * (row_bytes / 16);
-    if ((chunks + 255) / 256 >= (int64_t{1} << 31)) return Fail(PA_ERR_UNSUPPORTED, "T too large");
-    return FromHip(pa::LaunchWriteKv(key, value, slot_mapping, pool->k_cache, pool->v_cache, T,
-                                     row_bytes, num_slots, st_),
-                   "write_kv launch");
+    const WriteCall w{key, value, slot_mapping, T};
+    pa_status s = CheckWrite(*pool, w);
+    if (s != PA_OK) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    s = FlushCopies(pool, st);
+    if (s != PA_OK) return s;
+    return EnqueueWrite(*pool, w, st);
   });
 }
 
@@ -265,50 +421,11 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
                     size_t workspace_bytes, void* stream) {
   return Guard([&]() -> pa_status {
     if (!pool) return Fail(PA_ERR_INVALID, "null pool");
-    if (B < 0 || max_blocks < 0 || max_seq_len < 0 || partition_tokens < 0)
-      return Fail(PA_ERR_INVALID, "negative size argument");
-    int32_t G = 0;
-    pa_status s = CheckHeads(pool, num_q_heads, &G);
-    if (s != PA_OK) return s;
-    if (B == 0) return PA_OK;
-    if (!out || !q || !block_tables || !seq_lens) return Fail(PA_ERR_INVALID, "null argument");
-    if (!Aligned16(out) || !Aligned16(q)) return Fail(PA_ERR_INVALID, "q and out must be 16-byte aligned");
-    const pa_kv_layout& l = pool->layout;
-    if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * l.block_size)
-      return Fail(PA_ERR_INVALID, "max_seq_len exceeds max_blocks * block_size");
-    const int32_t pt = partition_tokens == 0 ? 512 : partition_tokens;
-    if (pt % 64 || pt > 2048)
-      return Fail(PA_ERR_UNSUPPORTED, "partition_tokens must be a multiple of 64, at most 2048");
-    const int32_t P = pa::DecodePartitions(max_seq_len, pt);
-    if (static_cast<int64_t>(P) * B * l.num_kv_heads >= (int64_t{1} << 31) - 8)
-      return Fail(PA_ERR_UNSUPPORTED, "grid too large");
-    const size_t need = pa::DecodeWorkspaceBytes(B, num_q_heads, l.head_dim, P);
-    if (need && (!workspace || workspace_bytes < need))
-      return Fail(PA_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
-    if (need && !Aligned16(workspace)) return Fail(PA_ERR_INVALID, "workspace must be 16-byte aligned");
     pa::DecodeArgs a{};
-    a.out = out;
-    a.q = q;
-    a.k_cache = pool->k_cache;
-    a.v_cache = pool->v_cache;
-    a.block_tables = block_tables;
-    a.seq_lens = seq_lens;
-    a.ws = workspace;
-    a.B = B;
-    a.Hq = num_q_heads;
-    a.Hkv = l.num_kv_heads;
-    a.D = l.head_dim;
-    a.G = G;
-    a.block_size = l.block_size;
-    a.num_blocks = l.num_blocks;
-    a.max_blocks = max_blocks;
-    a.max_seq_len = max_seq_len;
-    a.partition_tokens = pt;
-    a.num_partitions = P;
-    a.scale = scale;
-    a.k_scale = pool->k_scale;
-    a.v_scale = pool->v_scale;
-    a.dtype = l.dtype;
+    bool run = false;
+    const pa_status s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens, B, num_q_heads, scale,
+                                      max_seq_len, partition_tokens, workspace, workspace_bytes, &a, &run);
+    if (s != PA_OK || !run) return s;
     return FromHip(pa::LaunchDecode(a, static_cast<hipStream_t>(stream)), "decode launch");
   });
 }
@@ -318,38 +435,76 @@ pa_status pa_prefill(pa_pool* pool, void* out, const void* q, const int32_t* cu_
                      int32_t B, int32_t num_q_heads, int32_t max_q_len, float scale, void* stream) {
   return Guard([&]() -> pa_status {
     if (!pool) return Fail(PA_ERR_INVALID, "null pool");
-    if (B < 0 || max_blocks < 0 || max_q_len < 0) return Fail(PA_ERR_INVALID, "negative size argument");
-    int32_t G = 0;
-    pa_status s = CheckHeads(pool, num_q_heads, &G);
-    if (s != PA_OK) return s;
-    const pa_kv_layout& l = pool->layout;
-    if (l.dtype != PA_BF16) return Fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 pools only");
-    if (B == 0 || max_q_len == 0) return PA_OK;
-    if (!out || !q || !cu_q_lens || !block_tables || !seq_lens)
-      return Fail(PA_ERR_INVALID, "null argument");
-    if (!Aligned16(out) || !Aligned16(q)) return Fail(PA_ERR_INVALID, "q and out must be 16-byte aligned");
     pa::PrefillArgs a{};
-    a.out = out;
-    a.q = q;
-    a.k_cache = pool->k_cache;
-    a.v_cache = pool->v_cache;
-    a.cu_q_lens = cu_q_lens;
-    a.block_tables = block_tables;
-    a.seq_lens = seq_lens;
-    a.B = B;
-    a.Hq = num_q_heads;
-    a.Hkv = l.num_kv_heads;
-    a.D = l.head_dim;
-    a.G = G;
-    a.block_size = l.block_size;
-    a.num_blocks = l.num_blocks;
-    a.max_blocks = max_blocks;
-    a.max_q_len = max_q_len;
-    a.scale = scale;
-    hipError_t e = pa::LaunchPrefill(a, static_cast<hipStream_t>(stream));
-    if (e == hipErrorNotSupported) return Fail(PA_ERR_UNSUPPORTED, "prefill shape not supported");
-    return FromHip(e, "prefill launch");
+    bool run = false;
+    const pa_status s = PreparePrefill(*pool, out, q, cu_q_lens, block_tables, max_blocks, seq_lens, B,
+                                       num_q_heads, max_q_len, scale, &a, &run);
+    if (s != PA_OK || !run) return s;
+    return FromHip(pa::LaunchPrefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
   });
+}
+
+pa_status pa_step(pa_pool* pool, const pa_step_desc* desc, void* stream) {
+  return Guard([&]() -> pa_status {
+    if (!pool || !desc) return Fail(PA_ERR_INVALID, "null argument");
+    StepPlan plan;
+    pa_status s = PrepareStep(*pool, *desc, &plan);
+    if (s != PA_OK) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    s = FlushCopies(pool, st);
+    if (s != PA_OK) return s;
+    return EnqueueStep(*pool, plan, st);
+  });
+}
+
+pa_status pa_step_graph_create(pa_pool* pool, const pa_step_desc* desc, pa_step_graph** out) {
+  return Guard([&]() -> pa_status {
+    if (!pool || !desc || !out) return Fail(PA_ERR_INVALID, "null argument");
+    if (!pool->bm.pending_copies().empty())
+      return Fail(PA_ERR_INVALID, "copy-on-write copies are pending: run them first (pa_write_kv with T = 0)");
+    StepPlan plan;
+    pa_status s = PrepareStep(*pool, *desc, &plan);
+    if (s != PA_OK) return s;
+    // Captured on a private stream of default priority, so that no caller
+    // stream (the legacy default stream included) enters capture mode.
+    hipStream_t cap = nullptr;
+    s = FromHip(hipStreamCreateWithFlags(&cap, hipStreamNonBlocking), "capture stream");
+    if (s != PA_OK) return s;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    s = FromHip(hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal), "begin capture");
+    if (s == PA_OK) {
+      const pa_status launched = EnqueueStep(*pool, plan, cap);
+      const pa_status ended = FromHip(hipStreamEndCapture(cap, &graph), "end capture");
+      s = launched != PA_OK ? launched : ended;
+    }
+    if (s == PA_OK) s = FromHip(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "graph instantiate");
+    (void)hipStreamDestroy(cap);
+    if (s != PA_OK) {
+      if (exec) (void)hipGraphExecDestroy(exec);
+      if (graph) (void)hipGraphDestroy(graph);
+      return s;
+    }
+    *out = new pa_step_graph{pool, graph, exec};
+    return PA_OK;
+  });
+}
+
+pa_status pa_step_graph_launch(pa_step_graph* g, void* stream) {
+  return Guard([&]() -> pa_status {
+    if (!g) return Fail(PA_ERR_INVALID, "null graph");
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const pa_status s = FlushCopies(g->pool, st);   // copies vary per step: enqueued outside the graph
+    if (s != PA_OK) return s;
+    return FromHip(hipGraphLaunch(g->exec, st), "graph launch");
+  });
+}
+
+void pa_step_graph_destroy(pa_step_graph* g) {
+  if (!g) return;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
 }
 
 }  // extern "C"

@@ -53,7 +53,8 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32 * kWaves;  // query rows (positions x heads) per workgroup
+constexpr int kRows = kPrefillRows;  // query rows (positions x heads) per workgroup
+static_assert(kRows == 32 * kWaves, "one 32-row MFMA tile per wave");
 constexpr int kKT = 64;             // KV tokens per tile
 constexpr float kLazyMax = 8.f;
 constexpr int kRankedBatch = 256;   // batches up to this size are ordered by cache length
@@ -423,7 +424,7 @@ template <int D, int G>
 hipError_t LaunchTyped(const PrefillArgs& a, hipStream_t stream) {
   constexpr int QP = kRows / G;
   const int n_qtiles = (a.max_q_len + QP - 1) / QP;
-  const int64_t items = static_cast<int64_t>(a.Hkv) * n_qtiles * a.B;
+  const int64_t items = PrefillWorkItems(a.Hkv, a.G, a.B, a.max_q_len);
   if (items == 0) return hipSuccess;
   if (items >= (int64_t{1} << 31) - 8) return hipErrorInvalidValue;
   const int per_xcd = static_cast<int>((items + 7) / 8);

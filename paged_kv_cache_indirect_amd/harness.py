@@ -127,3 +127,134 @@ class GpuCache:
             self.close()
         except Exception:
             pass
+
+
+class MixedRunner:
+    """Mixed decode + chunked-prefill serving steps of a ``make_mixed``
+    workload on one pool, through pa_step (eager) or a captured step graph.
+
+    The pool starts from the workload's initial appends. Every step's device
+    inputs live in fixed buffers allocated once (new K/V rows, slots, both
+    sets of tables and lengths, cu_q_lens, queries, outputs, workspace), so a
+    graph captured on the first step replays later steps after the host
+    refreshes those buffers: append on the host block manager, export tables,
+    one host-to-device copy per buffer.
+    """
+
+    def __init__(self, wl, device="cuda", use_graph: bool = False, partition_tokens: int = 512):
+        from . import StepDesc
+        p = wl.plan
+        self.wl, self.device, self.use_graph = wl, device, use_graph
+        self.Bd, self.Bp, self.chunk = p["Bd"], p["Bp"], p["chunk"]
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        shape = (wl.num_blocks, wl.block_size, wl.Hkv, wl.D)
+        self.k_cache = torch.zeros(shape, dtype=tdt, device=device)
+        self.v_cache = torch.zeros(shape, dtype=tdt, device=device)
+        self.pool = pa_alloc_pool(self.k_cache, self.v_cache, wl.free_order)
+        self.lens = {}
+        for op in wl.ops[:p["n_init"]]:
+            seq, n = op[1], op[2]
+            slots = pa_seq_append(self.pool, seq, n)
+            k, v = wl.kv_rows(seq, 0, n)
+            if n:
+                pa_write_kv(self.pool, to_device(k, wl.dtype, device), to_device(v, wl.dtype, device),
+                            torch.from_numpy(slots).to(device))
+            self.lens[seq] = n
+        self.max_blocks = wl.max_blocks
+        self.max_seq_len = wl.max_seq_len
+        T = self.Bd + self.Bp * self.chunk
+        self.T = T
+        mk = lambda *s, dt=tdt: torch.zeros(s, dtype=dt, device=device)  # noqa: E731
+        self.key, self.value = mk(T, wl.Hkv, wl.D), mk(T, wl.Hkv, wl.D)
+        self.slots = mk(T, dt=torch.int64)
+        self.dec_q, self.dec_out = mk(self.Bd, wl.Hq, wl.D), mk(self.Bd, wl.Hq, wl.D)
+        self.dec_tables = mk(self.Bd, self.max_blocks, dt=torch.int32)
+        self.dec_lens = mk(self.Bd, dt=torch.int32)
+        self.pre_q, self.pre_out = mk(self.Bp * self.chunk, wl.Hq, wl.D), mk(self.Bp * self.chunk, wl.Hq, wl.D)
+        self.pre_tables = mk(self.Bp, self.max_blocks, dt=torch.int32)
+        self.pre_lens = mk(self.Bp, dt=torch.int32)
+        self.cu = torch.from_numpy(np.arange(self.Bp + 1, dtype=np.int32) * self.chunk).to(device)
+        need = pa_decode_workspace_bytes(self.Bd, wl.Hq, wl.D, self.max_seq_len, partition_tokens)
+        self.workspace = mk(max(need, 16), dt=torch.uint8)
+        self.desc = StepDesc(num_q_heads=wl.Hq, scale=wl.scale, max_blocks=self.max_blocks, key=self.key,
+                             value=self.value, slot_mapping=self.slots, dec_out=self.dec_out, dec_q=self.dec_q,
+                             dec_block_tables=self.dec_tables, dec_seq_lens=self.dec_lens,
+                             dec_max_seq_len=self.max_seq_len, partition_tokens=partition_tokens,
+                             workspace=self.workspace, pre_out=self.pre_out, pre_q=self.pre_q,
+                             pre_cu_q_lens=self.cu, pre_block_tables=self.pre_tables, pre_seq_lens=self.pre_lens,
+                             pre_max_q_len=self.chunk)
+        self.graph = None
+        self.host_tables = None
+        self.staged = None
+        torch.cuda.synchronize()
+
+    def stage_inputs(self) -> None:
+        """Generate every step's new K/V rows and queries up front and keep them
+        in HBM, so that prepare() only moves them into the step buffers."""
+        import workloads as W
+        wl, p = self.wl, self.wl.plan
+        lens = dict(self.lens)
+        keys, vals, qds, qps = [], [], [], []
+        for step in range(p["steps"]):
+            ks, vs = [], []
+            for seq in range(self.Bd + self.Bp):
+                n = 1 if seq < self.Bd else self.chunk
+                k, v = wl.kv_rows(seq, lens[seq], n)
+                ks.append(k)
+                vs.append(v)
+                lens[seq] += n
+            keys.append(np.concatenate(ks))
+            vals.append(np.concatenate(vs))
+            qd, qp = W.mixed_step_queries(wl, step)
+            qds.append(qd)
+            qps.append(qp)
+        dev = self.device
+        self.staged = [to_device(np.stack(x), wl.dtype, dev) for x in (keys, vals, qds, qps)]
+        torch.cuda.synchronize()
+
+    def prepare(self, step: int) -> None:
+        """Host side of step ``step``: appends on the block manager and the
+        table export, then the step's inputs into the fixed buffers (device
+        copies from the staged inputs; one upload each for slots, tables,
+        lengths)."""
+        if getattr(self, "staged", None) is None:
+            self.stage_inputs()
+        slots = []
+        order = list(range(self.Bd + self.Bp))
+        for seq in order:
+            n = 1 if seq < self.Bd else self.chunk
+            slots.append(pa_seq_append(self.pool, seq, n))
+            self.lens[seq] += n
+        tables, lens = pa_block_tables(self.pool, order, self.max_blocks)
+        self.host_tables, self.host_lens = tables, lens
+        k, v, qd, qp = (x[step] for x in self.staged)
+        self.key.copy_(k)
+        self.value.copy_(v)
+        self.dec_q.copy_(qd)
+        self.pre_q.copy_(qp)
+        self.slots.copy_(torch.from_numpy(np.concatenate(slots)))
+        self.dec_tables.copy_(torch.from_numpy(tables[:self.Bd]))
+        self.dec_lens.copy_(torch.from_numpy(lens[:self.Bd]))
+        self.pre_tables.copy_(torch.from_numpy(tables[self.Bd:]))
+        self.pre_lens.copy_(torch.from_numpy(lens[self.Bd:]))
+
+    def launch(self, stream=None) -> None:
+        """The device side of a prepared step: pa_step, or the captured graph."""
+        from . import pa_step, pa_step_graph_create, pa_step_graph_launch
+        if not self.use_graph:
+            pa_step(self.pool, self.desc, stream)
+            return
+        if self.graph is None:
+            torch.cuda.synchronize()     # the buffer uploads above ran on torch's stream
+            self.graph = pa_step_graph_create(self.pool, self.desc)
+        pa_step_graph_launch(self.graph, stream)
+
+    def close(self) -> None:
+        from . import pa_step_graph_destroy
+        torch.cuda.synchronize()
+        if self.graph is not None:
+            pa_step_graph_destroy(self.graph)
+            self.graph = None
+        if self.pool:
+            pa_free_pool(self.pool)
+            self.pool = None

@@ -323,3 +323,36 @@ def test_fp8_pool_rules():
     st, bpool = make_pool(16, 16, hkv=2, d=128, dtype=pa.PA_BF16)
     assert pa.lib.pa_pool_set_kv_scales(bpool, 0.5, 0.5) == pa.PA_ERR_UNSUPPORTED
     pa.pa_free_pool(bpool)
+
+
+def test_step_entry_points_validate_before_launch():
+    st, pool = make_pool(64, 16, hkv=2, d=128)
+    assert st == 0
+    dummy = 0x40000
+    d = pa._StepDesc()
+    d.num_q_heads, d.scale, d.max_blocks = 8, 0.1, 16
+    assert pa.lib.pa_step(pool, ctypes.byref(d), None) == pa.PA_OK          # every part empty: no-op
+    d.num_new_tokens = 4                                                       # rows without pointers
+    assert pa.lib.pa_step(pool, ctypes.byref(d), None) == pa.PA_ERR_INVALID
+    d.key = d.value = d.slot_mapping = dummy
+    d.dec_batch, d.dec_out, d.dec_q, d.dec_block_tables, d.dec_seq_lens = 2, dummy, dummy, dummy, dummy
+    d.dec_max_seq_len = 16 * 16 + 1                                          # beyond max_blocks * bs
+    assert pa.lib.pa_step(pool, ctypes.byref(d), None) == pa.PA_ERR_INVALID
+    d.dec_max_seq_len = 256
+    d.pre_batch, d.pre_out, d.pre_q, d.pre_cu_q_lens = 1, dummy, dummy + 2, dummy       # misaligned q
+    d.pre_block_tables, d.pre_seq_lens, d.pre_max_q_len = dummy, dummy, 16
+    assert pa.lib.pa_step(pool, ctypes.byref(d), None) == pa.PA_ERR_INVALID
+    g = ctypes.c_void_p()
+    assert pa.lib.pa_step_graph_create(pool, ctypes.byref(d), ctypes.byref(g)) == pa.PA_ERR_INVALID
+    assert pa.lib.pa_step_graph_launch(None, None) == pa.PA_ERR_INVALID
+    pa.lib.pa_step_graph_destroy(None)
+    # pending copy-on-write copies must be run before a capture
+    pa.pa_seq_append(pool, 0, 5)
+    pa.pa_seq_fork(pool, 0, 1)
+    pa.pa_seq_append(pool, 1, 1)
+    assert pa.pa_pool_stats(pool)["pending_copies"] == 1
+    e = pa._StepDesc()
+    e.num_q_heads, e.scale, e.max_blocks = 8, 0.1, 16
+    assert pa.lib.pa_step_graph_create(pool, ctypes.byref(e), ctypes.byref(g)) == pa.PA_ERR_INVALID
+    assert "pending" in pa.pa_last_error()
+    pa.pa_free_pool(pool)

@@ -38,6 +38,10 @@ a parity case, not a benchmark configuration):
 * ``prefix_cow`` - 32 seqs forked from one 1000-token prefix (1000 = 62·16
                + 8: the last prefix block is half full) plus suffixes
                U[0,300], 32/8, D 128, bf16, bs 16.
+* ``mixed`` - serving steps mixing decode and chunked prefill: 56 decode
+               sequences U[512,4096] plus 8 prefill sequences with cached
+               context U[0,4096] taking 256-token chunks, 8 steps, 32/8, D 128,
+               bf16, bs 16 (seed 1007).
 * ``gqa8b_fp8`` - the ``gqa8b`` shape (seed 1006) with an FP8 (E4M3) cache:
                bf16 rows quantised with per-tensor scales k 0.0137, v 0.0129
                (N(0,1) values up to about 6 map inside ±448).
@@ -51,8 +55,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "Workload", "make_decode", "make_prefix_share", "make_prefill",
-    "CONFIGS", "config", "round_to_bf16_bits", "draw_values",
+    "Workload", "make_decode", "make_prefix_share", "make_prefill", "make_mixed",
+    "CONFIGS", "config", "round_to_bf16_bits", "draw_values", "mixed_step_queries", "ops_through",
 ]
 
 # Tags that separate the independent random streams of one workload.
@@ -115,6 +119,7 @@ class Workload:
     kv_dtype: str = ""             # cache element type: "" = dtype, or "fp8" (E4M3 codes, bf16 rows in)
     k_scale: float = 1.0           # FP8 caches: per-tensor scales (code value * scale)
     v_scale: float = 1.0
+    plan: Optional[dict] = None    # mixed decode + prefill steps (make_mixed)
     _cache: Dict[int, Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict, repr=False)
     _prefix: Optional[Tuple[np.ndarray, np.ndarray]] = field(default=None, repr=False)
 
@@ -296,6 +301,50 @@ def make_prefill(name: str, ctx_lens: Sequence[int], q_lens: Sequence[int], Hq: 
                     q_lens=ql)
 
 
+def make_mixed(name: str, dec_lens: Sequence[int], pre_ctx: Sequence[int], chunk: int, steps: int, Hq: int,
+               Hkv: int, D: int, block_size: int, dtype: str, seed: int, pool_factor: float = 1.1) -> Workload:
+    """Serving steps that mix decode and chunked prefill in one batch.
+
+    Sequences 0..Bd-1 decode: they start with ``dec_lens`` cached tokens and
+    gain one token per step. Sequences Bd..Bd+Bp-1 prefill: they start with
+    ``pre_ctx`` cached tokens and gain a ``chunk``-token chunk per step. Step
+    s appends (decode sequences first, in order, then prefill sequences), then
+    attends: each decode sequence with one query, each chunk with its rows.
+    ``ops`` holds the initial appends followed by every step's appends;
+    ``seq_lens`` are the lengths after the last step. ``plan`` records the
+    split; ``ops_through(s)`` gives the ops that build the cache of step s.
+    """
+    dec = np.asarray(dec_lens, dtype=np.int32)
+    pre = np.asarray(pre_ctx, dtype=np.int32)
+    Bd, Bp = len(dec), len(pre)
+    final = np.concatenate([dec + steps, pre + steps * chunk]).astype(np.int32)
+    need = int(sum(-(-int(L) // block_size) for L in final))
+    nb, perm = _pool(seed, need, pool_factor, None)
+    init = [("append", b, int(L)) for b, L in enumerate(np.concatenate([dec, pre]))]
+    per_step = [("append", b, 1) for b in range(Bd)] + [("append", Bd + i, chunk) for i in range(Bp)]
+    ops = init + per_step * steps
+    plan = {"Bd": Bd, "Bp": Bp, "chunk": chunk, "steps": steps, "n_init": len(init), "n_step": len(per_step)}
+    return Workload(name=name, kind="mixed", B=Bd + Bp, Hq=Hq, Hkv=Hkv, D=D, block_size=block_size,
+                    dtype=dtype, seed=seed, seq_lens=final, num_blocks=nb, free_order=perm, ops=ops,
+                    scale=1.0 / math.sqrt(D), q_lens=np.full(Bp, chunk, dtype=np.int32), plan=plan)
+
+
+def mixed_step_queries(wl: Workload, step: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Queries of mixed step ``step``: decode [Bd, Hq, D] and the chunks' rows
+    [Bp * chunk, Hq, D] (sequence by sequence)."""
+    p = wl.plan
+    rng = _rng(wl.seed, _TAG_STEP, step)
+    qd = draw_values(rng, (p["Bd"], wl.Hq, wl.D), wl.dtype)
+    qp = draw_values(rng, (p["Bp"] * p["chunk"], wl.Hq, wl.D), wl.dtype)
+    return qd, qp
+
+
+def ops_through(wl: Workload, step: int) -> List[tuple]:
+    """The ops of a mixed workload up to and including step ``step``'s appends."""
+    p = wl.plan
+    return wl.ops[:p["n_init"] + (step + 1) * p["n_step"]]
+
+
 def _uniform_ints(seed: int, lo: int, hi: int, n: int) -> np.ndarray:
     """n integers uniform on [lo, hi] inclusive."""
     return _rng(seed, _TAG_LENS, 0).integers(lo, hi + 1, size=n).astype(np.int32)
@@ -322,6 +371,11 @@ def config(name: str) -> Workload:
         return make_decode("gqa8b_fp8", _uniform_ints(s, 512, 4096, 64), Hq=32, Hkv=8, D=128,
                            block_size=16, dtype="bf16", seed=s, kv_dtype="fp8", k_scale=0.0137,
                            v_scale=0.0129)
+    if name == "mixed":
+        s = 1007
+        return make_mixed("mixed", _uniform_ints(s, 512, 4096, 56), _rng(s, _TAG_LENS, 1).integers(
+                          0, 4097, 8).astype(np.int32), 256, 8, Hq=32, Hkv=8, D=128, block_size=16,
+                          dtype="bf16", seed=s)
     if name == "prefix_cow":
         s = 1005
         return make_prefix_share("prefix_cow", 32, 1000, _uniform_ints(s, 0, 300, 32), Hq=32,
