@@ -30,6 +30,9 @@ MFMA peak. ``decode_fp8`` times pa_decode over an FP8 (E4M3) pool of the same
 batch shape (seed 1006), with the bytes it must read (1-byte K/V codes).
 ``mixed_step`` runs serving steps that mix decode and chunked prefill
 (pa_step eager, and the same step captured once as a HIP graph and replayed).
+``prefix_cache`` times token-aware appends with block lookups against blind
+appends and decodes the shared-prompt batch; ``tiered_block_sizes`` decodes
+batches split into per-length-tier pools against one bs-16 pool.
 """
 from __future__ import annotations
 
@@ -303,6 +306,127 @@ def run_mixed(args):
     return res
 
 
+# --------------------------------------------------- prefix cache and tiers
+def run_prefix_cache(args):
+    """Host cost and effect of prefix caching: the 48-request shared-prompt
+    batch appended with token ids (pa_seq_append_tokens: hashing, lookups,
+    shared blocks) versus the same token counts appended blind
+    (pa_seq_append), on two empty pools; then decode over the cached pool."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_indirect_amd import (harness, pa_alloc_pool, pa_free_pool, pa_pool_prefix_stats,
+                                             pa_pool_stats, pa_seq_append, pa_seq_append_tokens)
+
+    wl = W.config("prompt_cache")
+    blind_need = int(sum(-(-int(L) // wl.block_size) for L in wl.seq_lens))   # no sharing at all
+    shape = (blind_need, wl.block_size, wl.Hkv, wl.D)
+    kc = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    res = {"workload": "48 requests sharing a 1000-token prompt plus own tokens U[1,600] (seed 1008), bs 16"}
+    ntok = int(sum(len(op[2]) for op in wl.ops))
+    for mode in ("tokens", "blind"):
+        best = None
+        for _ in range(5):
+            pool = pa_alloc_pool(kc, vc)
+            t0 = time.perf_counter()
+            for op in wl.ops:
+                if mode == "tokens":
+                    pa_seq_append_tokens(pool, op[1], op[2])
+                else:
+                    pa_seq_append(pool, op[1], len(op[2]))
+            dt = time.perf_counter() - t0
+            st = pa_pool_stats(pool)
+            ps = pa_pool_prefix_stats(pool)
+            pa_free_pool(pool)
+            best = dt if best is None else min(best, dt)
+        res[mode] = {"host_ns_per_token": best / ntok * 1e9, "used_blocks": st["used_blocks"],
+                     "shared_blocks": st["shared_blocks"]}
+        if mode == "tokens":
+            res[mode].update({"lookups": ps["lookups"], "hits": ps["hits"], "cached_blocks": ps["cached_blocks"]})
+    del kc, vc
+    torch.cuda.empty_cache()
+    cache = harness.GpuCache(wl, poison=False)
+    ws = cache.workspace_for(512)
+    for _ in range(3):
+        cache.decode(512, ws)
+    n = 20
+    stream = torch.cuda.current_stream()
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        e0[i].record(stream)
+        cache.decode(512, ws)
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)])) * 1e-3
+    nbytes = decode_bytes(wl, wl.seq_lens)
+    cache.close()
+    res["decode"] = {"us_mean": t * 1e6, "logical_gbps": nbytes / t / 1e9,
+                     "unique_kv_bytes": wl.unique_kv_bytes(), "logical_kv_bytes": wl.kv_bytes()}
+    log(f"[bench] prefix cache: {res['tokens']['host_ns_per_token']:.0f} ns/token with lookups, "
+        f"{res['blind']['host_ns_per_token']:.0f} blind; decode {t * 1e6:.1f} us")
+    return res
+
+
+def run_tiered(args):
+    """Block-size tiers by length class: each batch split into per-tier pools
+    (pa_tier_block_size) and decoded with one pa_decode per pool on one
+    stream, against the same batch in one bs-16 pool. Tail waste from the
+    block manager's slot counts."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_indirect_amd import harness, pa_pool_stats, pa_tier_block_size
+
+    out = {}
+    for name in ("gqa8b", "long"):
+        base = W.config(name)
+        groups = {}
+        for L in base.seq_lens.tolist():
+            groups.setdefault(pa_tier_block_size(L), []).append(L)
+        layouts = {"single_bs16": [(16, base.seq_lens.tolist())], "tiered": sorted(groups.items())}
+        res = {}
+        for label, parts in layouts.items():
+            caches = []
+            for i, (bs, lens) in enumerate(parts):
+                wl = W.make_decode(f"{name}_{label}_{bs}", lens, Hq=32, Hkv=8, D=128, block_size=bs, dtype="bf16",
+                                   seed=base.seed + 100 * (i + 1))
+                caches.append((wl, harness.GpuCache(wl, poison=False)))
+            wss = [c.workspace_for(512) for _, c in caches]
+            for _ in range(3):
+                for (_, c), w in zip(caches, wss):
+                    c.decode(512, w)
+            n = 20
+            stream = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                for (_, c), w in zip(caches, wss):
+                    c.decode(512, w)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / n * 1e-3
+            nbytes = sum(decode_bytes(wl, wl.seq_lens) for wl, _ in caches)
+            alloc = sum(pa_pool_stats(c.pool)["allocated_slots"] for _, c in caches)
+            filled = sum(pa_pool_stats(c.pool)["filled_slots"] for _, c in caches)
+            res[label] = {"block_sizes": [bs for bs, _ in parts], "seqs_per_pool": [len(l) for _, l in parts],
+                          "us_per_batch": t * 1e6, "gbps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
+                          "tail_waste_slots": alloc - filled, "tail_waste_frac": (alloc - filled) / alloc}
+            for _, c in caches:
+                c.close()
+            del caches
+            torch.cuda.empty_cache()
+        out[name] = res
+        log(f"[bench] tiers {name}: single {res['single_bs16']['us_per_batch']:.1f} us, "
+            f"tiered {res['tiered']['us_per_batch']:.1f} us")
+    return out
+
+
 # -------------------------------------------------------------------- prefill
 def causal_flops(wl) -> float:
     """4 * D * Hq * sum_b sum_i (ctx_b + i + 1): QK^T and PV over the
@@ -411,6 +535,7 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache decode leg")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-step (eager vs graph) leg")
+    ap.add_argument("--no-extras", action="store_true", help="skip the prefix-cache and block-size-tier legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the decode steps, run one plain 1 GiB device-to-device copy: "
                          "the reference that scales hardware byte counters (FETCH_SIZE, WRITE_SIZE)")
@@ -447,6 +572,8 @@ def main() -> int:
     pre = None if args.no_prefill else run_prefill(args)[1]
     fp8 = None if args.no_fp8 else run_decode_fp8(args)
     mixed = None if args.no_mixed else run_mixed(args)
+    pcache = None if args.no_extras else run_prefix_cache(args)
+    tiers = None if args.no_extras else run_tiered(args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, wl)
 
     line = {
@@ -492,6 +619,8 @@ def main() -> int:
         "prefill": pre,
         "decode_fp8": fp8,
         "mixed_step": mixed,
+        "prefix_cache": pcache,
+        "tiered_block_sizes": tiers,
     }
     print(json.dumps(line), flush=True)
     return 0

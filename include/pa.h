@@ -131,6 +131,44 @@ pa_status pa_seq_append(pa_pool* pool, int64_t seq_id, int32_t n_tokens, int64_t
 pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seq_ids, int32_t n, int32_t n_tokens,
                               int64_t* slots_out);
 
+/* Append n_tokens tokens whose ids are known (token_ids, host, n_tokens
+ * int32), with prefix caching: when several sequences start with the same
+ * prompt, they reuse the same physical blocks ("vLLM 生产级落地深剖",
+ * musen-ai.com, §2; blocks are found by hashing, §5). Every block that
+ * token-aware appends fill completely is registered under a key standing for
+ * the ids of all tokens from position 0 to the block's end (a 64-bit FNV-1a
+ * chain; a match also compares the block's ids and its parent key). When the
+ * append reaches a block boundary, the following full blocks of new tokens
+ * are looked up in order; while found, each is shared (refcount + 1; a
+ * cached block with refcount 0 is taken back off the free list) instead of
+ * allocated, and its tokens get slot -1 in slots_out (host, n_tokens int64):
+ * their K/V is already in the pool, and pa_write_kv skips -1. Lookups stop
+ * at the first miss. A registered block keeps its key after it is freed,
+ * until it is handed out again (then the key is dropped). *n_cached_out
+ * (host) receives the number of -1 slots. Admission is all-or-nothing over
+ * fresh blocks, copy-on-write and cached blocks taken off the free list.
+ * A sequence created or grown by pa_seq_append / pa_seq_append_batch has
+ * token ids the pool does not know: it is never keyed, and this call then
+ * behaves as pa_seq_append. pa_seq_fork copies the keys of the source.
+ * Errors: as pa_seq_append. */
+pa_status pa_seq_append_tokens(pa_pool* pool, int64_t seq_id, const int32_t* token_ids, int32_t n_tokens,
+                               int64_t* slots_out, int32_t* n_cached_out);
+
+/* Prefix-cache counters: blocks holding a registered key (in use or free),
+ * full blocks looked up and found since the pool was created. */
+typedef struct {
+  int32_t cached_blocks;
+  int64_t lookups;
+  int64_t hits;
+} pa_prefix_stats_t;
+pa_status pa_pool_prefix_stats(const pa_pool* pool, pa_prefix_stats_t* out);
+
+/* Block size for a pool of sequences of the given expected length class,
+ * after the tiers of "LLM推理优化：技术原理解析总览" §3.3: 32 below 1024
+ * tokens, 16 from 1024 to below 8192, 8 from 8192 on. A deployment keeps
+ * one pool per tier and routes each sequence to its tier's pool. */
+int32_t pa_tier_block_size(int64_t expected_len);
+
 /* Make dst a new sequence that shares all of src's blocks (prefix sharing:
  * same physical blocks, each block's refcount + 1; "vLLM的'内存分页'到底多神奇",
  * §2 and §3 phase 3), a partly filled last block included. Sharing is

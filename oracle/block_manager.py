@@ -29,6 +29,25 @@ Policy choices the pages leave open (listed in the design doc):
   records a pending copy (shared, fresh); pending copies are kept in order
   until the device performs them, frees included;
 * block ids are int32; tables export padded with -1.
+
+Prefix caching ("vLLM 生产级落地深剖" (musen-ai.com), §2: sequences with the
+same prompt prefix reuse the same physical blocks; §5: blocks are found by
+hashing) — the readings:
+* only appends that carry token ids (``append_tokens``) take part; a
+  sequence whose ids are not all known (created or grown by ``append``) is
+  never keyed, and ``append_tokens`` on it is ``append``;
+* a block that token-aware appends fill completely is registered under the
+  tuple of all token ids from position 0 to its end (this model keys on the
+  ids themselves; the library hashes them), unless that key is already
+  registered;
+* when such an append reaches a block boundary, the following full blocks
+  of new tokens are looked up in order until the first miss; a found block
+  is shared (refcount + 1; taken off the free list, wherever it sits, when
+  its refcount was 0) and its tokens get slot -1; the rest are fresh blocks;
+* physical order within one call: found blocks taken, then the
+  copy-on-write block, then fresh blocks in logical order;
+* a block keeps its key while in use and after it is freed, until it is
+  popped from the free list for new contents.
 """
 from __future__ import annotations
 
@@ -52,6 +71,18 @@ class BlockManagerModel:
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
         self.pending: List[tuple] = []   # copy-on-write block copies (src, dst), in order
+        self.toks: Dict[int, Optional[List[int]]] = {}   # token ids of keyed sequences (None: not keyed)
+        self.cache: Dict[tuple, int] = {}                # prefix ids -> registered block
+        self.block_key: Dict[int, tuple] = {}
+        self.lookups = 0
+        self.hits = 0
+
+    def _pop(self) -> int:
+        blk = self.free.pop()
+        key = self.block_key.pop(blk, None)
+        if key is not None:
+            del self.cache[key]
+        return blk
 
     # ---------------------------------------------------------------- ops
     def append(self, seq: int, n: int):
@@ -68,15 +99,17 @@ class BlockManagerModel:
             return ERR_NO_BLOCKS, []
         table = list(table)
         if cow:
-            old, blk = table[-1], self.free.pop()
+            old, blk = table[-1], self._pop()
             self.ref[blk] += 1
             self.ref[old] -= 1
             table[-1] = blk
             self.pending.append((old, blk))
         for _ in range(tail):
-            blk = self.free.pop()
+            blk = self._pop()
             self.ref[blk] += 1
             table.append(blk)
+        if n > 0 or seq not in self.tables:
+            self.toks[seq] = None
         self.tables[seq] = table
         self.lens[seq] = L + n
         slots = [table[p // bs] * bs + p % bs for p in range(L, L + n)]
@@ -114,6 +147,8 @@ class BlockManagerModel:
             return ERR_INVALID
         self.tables[dst] = list(self.tables[src])
         self.lens[dst] = self.lens[src]
+        t = self.toks.get(src)
+        self.toks[dst] = None if t is None else list(t)
         for blk in self.tables[dst]:
             self.ref[blk] += 1
         return OK
@@ -126,7 +161,89 @@ class BlockManagerModel:
             if self.ref[blk] == 0:
                 self.free.append(blk)
         del self.lens[seq]
+        self.toks.pop(seq, None)
         return OK
+
+    def append_tokens(self, seq: int, ids: Sequence[int]):
+        """Token-aware append with prefix caching. Returns (status, slots,
+        n_cached); slots are -1 for tokens found in cached blocks."""
+        ids = [int(x) for x in ids]
+        n = len(ids)
+        if seq in self.tables and self.toks.get(seq) is None:
+            st, slots = self.append(seq, n)
+            return st, slots, 0
+        bs = self.block_size
+        table = list(self.tables.get(seq, []))
+        L = self.lens.get(seq, 0)
+        have = len(table)
+        r = L % bs
+        fill = min(n, bs - r) if r else 0
+        cow = fill > 0 and self.ref[table[-1]] > 1
+        all_ids = (self.toks.get(seq) or []) + ids
+        tail_key = tuple(all_ids[:(L // bs + 1) * bs]) if r and r + fill == bs else None
+        plan = []              # (key, found block or None) per new full block
+        searching = True
+        pos, lb = fill, have
+        lookups = 0
+        while n - pos >= bs:
+            key = tuple(all_ids[:(lb + 1) * bs])
+            hit = None
+            if searching:
+                lookups += 1
+                hit = self.cache.get(key)
+                if hit is None:
+                    searching = False
+            plan.append((key, hit))
+            pos += bs
+            lb += 1
+        rem = n - pos
+        hits = [h for _, h in plan if h is not None]
+        fresh = len(plan) - len(hits) + (1 if rem > 0 else 0)
+        need = sum(1 for h in hits if self.ref[h] == 0) + cow + fresh
+        if need > len(self.free):
+            return ERR_NO_BLOCKS, [], 0
+        for h in hits:                          # (1) cached blocks taken
+            if self.ref[h] == 0:
+                self.free.remove(h)
+            self.ref[h] += 1
+        if cow:                                 # (2) the copy-on-write block
+            old, blk = table[-1], self._pop()
+            self.ref[blk] += 1
+            self.ref[old] -= 1
+            table[-1] = blk
+            self.pending.append((old, blk))
+        for key, h in plan:                     # (3) fresh blocks in logical order
+            if h is None:
+                h = self._pop()
+                self.ref[h] += 1
+            table.append(h)
+        if rem > 0:
+            blk = self._pop()
+            self.ref[blk] += 1
+            table.append(blk)
+        if tail_key is not None and tail_key not in self.cache:
+            self.cache[tail_key] = table[have - 1]
+            self.block_key[table[have - 1]] = tail_key
+        for i, (key, h) in enumerate(plan):
+            if h is None and key not in self.cache:
+                self.cache[key] = table[have + i]
+                self.block_key[table[have + i]] = key
+        slots = []
+        for p in range(L, L + n):
+            i = p // bs - have
+            if p - L >= fill and 0 <= i < len(plan) and plan[i][1] is not None:
+                slots.append(-1)
+            else:
+                slots.append(table[p // bs] * bs + p % bs)
+        self.tables[seq] = table
+        self.lens[seq] = L + n
+        self.toks[seq] = all_ids
+        self.lookups += lookups
+        self.hits += len(hits)
+        return OK, slots, sum(1 for x in slots if x < 0)
+
+    def prefix_stats(self):
+        return {"cached_blocks": len(self.cache), "lookups": self.lookups, "hits": self.hits}
 
     def block_tables(self, seqs: Iterable[int], max_blocks: int):
         """(status, tables [n][max_blocks] padded -1, lens [n])."""
@@ -172,6 +289,19 @@ class BlockManagerModel:
         assert len(used) + len(self.free) == self.num_blocks, "blocks lost or duplicated"
         for s, t in self.tables.items():
             assert len(t) == -(-self.lens[s] // self.block_size), "table length != ceil(L/bs)"
+        # prefix keys: cache and block_key are inverse maps, and a keyed block
+        # at logical index i of a keyed sequence holds that sequence's ids 0..(i+1)*bs
+        assert {b: k for k, b in self.cache.items()} == self.block_key, "cache / block_key disagree"
+        bs = self.block_size
+        for s, t in self.tables.items():
+            ids = self.toks.get(s)
+            if ids is None:
+                continue
+            assert len(ids) == self.lens[s], "token ids != length"
+            for i, blk in enumerate(t):
+                k = self.block_key.get(blk)
+                if k is not None:
+                    assert k == tuple(ids[:(i + 1) * bs]), "a keyed block's key is not its prefix"
 
 
 def blocks_needed(n_tokens: int, block_size: int) -> int:

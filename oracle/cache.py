@@ -51,6 +51,19 @@ class OracleCache:
                 if only is None or seq in only:
                     k, v = wl.kv_rows(seq, start, n)
                     self._scatter(k, v, np.asarray(slots, dtype=np.int64))
+            elif op[0] == "tokens":
+                seq, ids = op[1], op[2]
+                start = self.bm.lens.get(seq, 0)
+                st, slots, _ = self.bm.append_tokens(seq, ids)
+                if st != 0:
+                    raise RuntimeError(f"oracle block manager refused a token append: status {st}")
+                for src, dst in self.bm.pending:
+                    self.k_cache[dst] = self.k_cache[src]
+                    self.v_cache[dst] = self.v_cache[src]
+                self.bm.pending = []
+                if only is None or seq in only:
+                    k, v = wl.kv_rows(seq, start, len(ids))
+                    self._scatter(k, v, np.asarray(slots, dtype=np.int64))   # -1 slots (cached) skipped
             elif op[0] == "fork":
                 assert self.bm.fork(op[1], op[2]) == 0
             elif op[0] == "free":

@@ -25,7 +25,8 @@ __all__ = [
     "pa_alloc_pool", "pa_free_pool", "pa_seq_append", "pa_seq_append_batch", "pa_seq_fork", "pa_seq_free",
     "pa_block_tables", "pa_pool_stats", "pa_pool_pending_copies", "pa_pool_set_kv_scales", "pa_write_kv",
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error", "StepDesc", "pa_step",
-    "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy",
+    "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy", "pa_seq_append_tokens",
+    "pa_pool_prefix_stats", "pa_tier_block_size",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
@@ -74,6 +75,9 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 _SIGS = {
     "pa_alloc_pool": (_i32, [ctypes.POINTER(_Layout), _vp, _vp, _vp, ctypes.POINTER(_vp)]),
     "pa_free_pool": (None, [_vp]),
+    "pa_seq_append_tokens": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
+    "pa_pool_prefix_stats": (_i32, [_vp, _vp]),
+    "pa_tier_block_size": (_i32, [_i64]),
     "pa_step": (_i32, [_vp, ctypes.POINTER(_StepDesc), _vp]),
     "pa_step_graph_create": (_i32, [_vp, ctypes.POINTER(_StepDesc), ctypes.POINTER(_vp)]),
     "pa_step_graph_launch": (_i32, [_vp, _vp]),
@@ -331,3 +335,30 @@ def pa_step_graph_launch(graph: int, stream=None) -> None:
 
 def pa_step_graph_destroy(graph: int) -> None:
     lib.pa_step_graph_destroy(graph)
+
+
+class _PrefixStats(ctypes.Structure):
+    _fields_ = [("cached_blocks", ctypes.c_int32), ("lookups", ctypes.c_int64), ("hits", ctypes.c_int64)]
+
+
+def pa_seq_append_tokens(pool: int, seq_id: int, token_ids) -> tuple:
+    """Token-aware append with prefix caching. Returns (slots int64 array with
+    -1 where the K/V is already cached, number of cached tokens)."""
+    ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+    n = len(ids)
+    slots = np.empty(max(n, 1), dtype=np.int64)
+    cached = ctypes.c_int32()
+    _check(lib.pa_seq_append_tokens(pool, seq_id, ids.ctypes.data if n else None, n,
+                                    slots.ctypes.data if n else None, ctypes.byref(cached)),
+           "pa_seq_append_tokens")
+    return slots[:n], cached.value
+
+
+def pa_pool_prefix_stats(pool: int) -> dict:
+    st = _PrefixStats()
+    _check(lib.pa_pool_prefix_stats(pool, ctypes.byref(st)), "pa_pool_prefix_stats")
+    return {"cached_blocks": st.cached_blocks, "lookups": st.lookups, "hits": st.hits}
+
+
+def pa_tier_block_size(expected_len: int) -> int:
+    return int(lib.pa_tier_block_size(int(expected_len)))

@@ -84,17 +84,57 @@ class BlockManager {
   const std::vector<std::pair<int32_t, int32_t>>& pending_copies() const { return pending_; }
   void ClearPendingCopies() { pending_.clear(); }
 
+  // Prefix caching: append tokens whose ids are known. A block that a
+  // token-aware append fills completely is registered under a key that
+  // stands for the ids of every token from position 0 to the block's end.
+  // When such an append reaches a block boundary, the following full blocks
+  // of new tokens are looked up in order, and while they are found they are
+  // shared (refcount + 1; a cached block with refcount 0 is taken back off
+  // the free list) instead of allocated; their slots are reported as -1 (the
+  // K/V is already in the pool) and counted in *n_cached. Lookups stop at
+  // the first miss. A registered block keeps its key after it is freed, until
+  // it is handed out again. Physical order of a call: cached blocks taken,
+  // then the copy-on-write block, then fresh blocks in logical order.
+  // A sequence whose tokens did not all arrive through AppendTokens (created
+  // or grown by Append) is not keyed, and AppendTokens on it is Append.
+  Status AppendTokens(int64_t seq, const int32_t* tokens, int32_t n, int64_t* slots_out, int32_t* n_cached,
+                      std::string* err);
+  struct PrefixStats {
+    int32_t cached_blocks = 0;  // blocks holding a registered key (in use or free)
+    int64_t lookups = 0;        // full blocks looked up
+    int64_t hits = 0;           // of which found
+  };
+  PrefixStats prefix_stats() const;
+
  private:
   struct Seq {
     std::vector<int32_t> table;
     int64_t len = 0;
+    bool keyed = false;                // every token arrived through AppendTokens
+    uint64_t key = 0;                  // key of the full blocks so far (kRootKey when none)
+    std::vector<int32_t> tail_tokens;  // ids of the tokens in a partly filled last block
   };
+  struct CacheEntry {
+    int32_t block;
+    uint64_t parent;
+    std::vector<int32_t> tokens;
+  };
+  static constexpr uint64_t kRootKey = 14695981039346656037ull;  // FNV-1a 64-bit offset basis
+  static uint64_t ChainKey(uint64_t parent, const int32_t* ids, int32_t n);
+  // Pops the top of the free list and drops any key the block held.
+  int32_t PopFree();
+  // Takes a given (cached) block off the free list.
+  void TakeFree(int32_t blk);
   int32_t num_blocks_;
   int32_t block_size_;
   std::vector<int32_t> free_;  // stack: back() is the next block handed out
   std::vector<int32_t> ref_;
   std::unordered_map<int64_t, Seq> seqs_;
   std::vector<std::pair<int32_t, int32_t>> pending_;
+  std::unordered_map<uint64_t, CacheEntry> cache_;  // key -> registered block
+  std::vector<uint64_t> block_key_;                 // key a block is registered under
+  std::vector<char> block_keyed_;
+  PrefixStats pstats_;
 };
 
 }  // namespace pa

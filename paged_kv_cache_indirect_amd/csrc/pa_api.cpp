@@ -326,6 +326,32 @@ pa_status pa_seq_append_batch(pa_pool* pool, const int64_t* seq_ids, int32_t n, 
   });
 }
 
+pa_status pa_seq_append_tokens(pa_pool* pool, int64_t seq_id, const int32_t* token_ids, int32_t n_tokens,
+                               int64_t* slots_out, int32_t* n_cached_out) {
+  return Guard([&]() -> pa_status {
+    if (!pool) return Fail(PA_ERR_INVALID, "null pool");
+    std::string err;
+    return FromBm(pool->bm.AppendTokens(seq_id, token_ids, n_tokens, slots_out, n_cached_out, &err), err);
+  });
+}
+
+pa_status pa_pool_prefix_stats(const pa_pool* pool, pa_prefix_stats_t* out) {
+  return Guard([&]() -> pa_status {
+    if (!pool || !out) return Fail(PA_ERR_INVALID, "null argument");
+    const pa::BlockManager::PrefixStats p = pool->bm.prefix_stats();
+    out->cached_blocks = p.cached_blocks;
+    out->lookups = p.lookups;
+    out->hits = p.hits;
+    return PA_OK;
+  });
+}
+
+int32_t pa_tier_block_size(int64_t expected_len) {
+  if (expected_len < 1024) return 32;
+  if (expected_len < 8192) return 16;
+  return 8;
+}
+
 pa_status pa_seq_fork(pa_pool* pool, int64_t src_seq_id, int64_t dst_seq_id) {
   return Guard([&]() -> pa_status {
     if (!pool) return Fail(PA_ERR_INVALID, "null pool");

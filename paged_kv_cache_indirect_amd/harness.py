@@ -13,7 +13,8 @@ import numpy as np
 import torch
 
 from . import (pa_alloc_pool, pa_block_tables, pa_decode, pa_decode_workspace_bytes, pa_free_pool,
-               pa_pool_set_kv_scales, pa_prefill, pa_seq_append, pa_seq_fork, pa_seq_free, pa_write_kv)
+               pa_pool_set_kv_scales, pa_prefill, pa_seq_append, pa_seq_append_tokens, pa_seq_fork, pa_seq_free,
+               pa_write_kv)
 
 # NaN bit patterns used to poison never-written cache slots.
 SENTINEL_BF16 = 0x7FC1
@@ -69,6 +70,15 @@ class GpuCache:
                 self.slots.setdefault(seq, []).append(slots)
                 for a in range(0, n, chunk_tokens):       # bounded host→device staging
                     m = min(chunk_tokens, n - a)
+                    k, v = wl.kv_rows(seq, start + a, m)
+                    self.write(k, v, slots[a:a + m])
+            elif op[0] == "tokens":
+                seq, ids = op[1], op[2]
+                start = self.slots_len(seq)
+                slots, _ = pa_seq_append_tokens(self.pool, seq, ids)
+                self.slots.setdefault(seq, []).append(slots)
+                for a in range(0, len(ids), chunk_tokens):   # -1 slots (cached blocks) are skipped
+                    m = min(chunk_tokens, len(ids) - a)
                     k, v = wl.kv_rows(seq, start + a, m)
                     self.write(k, v, slots[a:a + m])
             elif op[0] == "fork":

@@ -4,7 +4,7 @@
 //
 // Input:  nb bs k order[0..k)   (k = 0: ascending order)
 //         then lines: a <seq> <n> | b <n_tokens> <n> <ids...> | f <src> <dst> | x <seq> |
-//                     t <mb> <n> <ids...> | s
+//                     t <mb> <n> <ids...> | k <seq> <n> <token ids...> | s
 // Output: one line per op.
 #include <cstdio>
 #include <string>
@@ -50,6 +50,21 @@ int main() {
       if (st == 0)
         for (int i = 0; i < n * nt; ++i) std::printf(" %lld", static_cast<long long>(slots[static_cast<size_t>(i)]));
       std::printf("\n");
+    } else if (op[0] == 'k') {
+      long long seq;
+      int n;
+      std::scanf("%lld %d", &seq, &n);
+      std::vector<int32_t> toks(static_cast<size_t>(n) + 1);
+      for (int i = 0; i < n; ++i) std::scanf("%d", &toks[static_cast<size_t>(i)]);
+      std::vector<int64_t> slots(static_cast<size_t>(n) + 1);
+      int32_t cached = 0;
+      int st = bm.AppendTokens(seq, toks.data(), n, slots.data(), &cached, &err);
+      std::printf("%d", st);
+      if (st == 0) {
+        std::printf(" %d", cached);
+        for (int i = 0; i < n; ++i) std::printf(" %lld", static_cast<long long>(slots[static_cast<size_t>(i)]));
+      }
+      std::printf("\n");
     } else if (op[0] == 'f') {
       long long a, b;
       std::scanf("%lld %lld", &a, &b);
@@ -79,6 +94,9 @@ int main() {
       pa::PoolStats s = bm.Stats();
       std::printf("%d %d %d %lld %lld", s.free_blocks, s.used_blocks, s.shared_blocks,
                   static_cast<long long>(s.filled_slots), static_cast<long long>(s.allocated_slots));
+      const pa::BlockManager::PrefixStats ps = bm.prefix_stats();
+      std::printf(" %d %lld %lld", ps.cached_blocks, static_cast<long long>(ps.lookups),
+                  static_cast<long long>(ps.hits));
       for (const auto& c : bm.pending_copies()) std::printf(" %d %d", c.first, c.second);
       std::printf("\n");
     }

@@ -49,11 +49,17 @@ def make_pool(nb, bs, order=None, hkv=2, d=64, dtype=pa.PA_BF16):
 
 
 def random_ops(rng, n_ops, max_seqs=10, max_tokens=80):
+    # shared prompts: token-aware appends often start with one of these
+    templates = [rng.integers(0, 40, 120) for _ in range(3)]
     ops = []
     for _ in range(n_ops):
         r = rng.random()
         s = int(rng.integers(0, max_seqs))
-        if r < 0.4:
+        if r < 0.15:
+            t = templates[int(rng.integers(0, 3))]
+            ids = list(t[:int(rng.integers(0, 121))]) + list(rng.integers(0, 40, int(rng.integers(0, 20))))
+            ops.append(("tokens", s, [int(x) for x in ids]))
+        elif r < 0.4:
             ops.append(("append", s, int(rng.integers(0, max_tokens))))
         elif r < 0.5:
             # a batch of distinct sequences (sometimes a repeated id: rejected)
@@ -81,6 +87,9 @@ def run_model(nb, bs, order, ops):
         elif op[0] == "batch":
             st, slots = m.append_batch(op[2], op[1])
             out.append((st, [x for row in slots for x in row]))
+        elif op[0] == "tokens":
+            st, slots, cached = m.append_tokens(op[1], op[2])
+            out.append((st, list(slots) if st == 0 else [], cached if st == 0 else 0))
         elif op[0] == "fork":
             out.append((m.fork(op[1], op[2]),))
         elif op[0] == "free":
@@ -89,8 +98,11 @@ def run_model(nb, bs, order, ops):
             st, t, l = m.block_tables(op[2], op[1])
             out.append((st, l, t))
         s = m.stats()
+        ps = m.prefix_stats()
         out.append(tuple(s[k] for k in ("free_blocks", "used_blocks", "shared_blocks", "filled_slots",
-                                        "allocated_slots")) + tuple(x for c in m.pending for x in c))
+                                        "allocated_slots")) +
+                   tuple(ps[k] for k in ("cached_blocks", "lookups", "hits")) +
+                   tuple(x for c in m.pending for x in c))
     return out
 
 
@@ -106,6 +118,13 @@ def run_abi(pool, ops):
             slots = np.empty(max(len(ids) * op[1], 1), dtype=np.int64)
             st = pa.lib.pa_seq_append_batch(pool, ids.ctypes.data, len(ids), op[1], slots.ctypes.data)
             out.append((st, slots[:len(ids) * op[1]].tolist() if st == 0 else []))
+        elif op[0] == "tokens":
+            ids = np.array(op[2], dtype=np.int32)
+            slots = np.empty(max(len(ids), 1), dtype=np.int64)
+            cached = ctypes.c_int32()
+            st = pa.lib.pa_seq_append_tokens(pool, op[1], ids.ctypes.data, len(ids), slots.ctypes.data,
+                                             ctypes.byref(cached))
+            out.append((st, slots[:len(ids)].tolist() if st == 0 else [], cached.value if st == 0 else 0))
         elif op[0] == "fork":
             out.append((pa.lib.pa_seq_fork(pool, op[1], op[2]),))
         elif op[0] == "free":
@@ -117,9 +136,11 @@ def run_abi(pool, ops):
             st = pa.lib.pa_block_tables(pool, ids.ctypes.data, len(ids), mb, t.ctypes.data, l.ctypes.data)
             out.append((st, l.tolist(), t[:, :mb].tolist()) if st == 0 else (st, None, None))
         s = pa.pa_pool_stats(pool)
+        ps = pa.pa_pool_prefix_stats(pool)
         out.append(tuple(s[k] for k in ("free_blocks", "used_blocks", "shared_blocks", "filled_slots",
-                                        "allocated_slots")) + tuple(x for c in pa.pa_pool_pending_copies(pool)
-                                                                   for x in c))
+                                        "allocated_slots")) +
+                   tuple(ps[k] for k in ("cached_blocks", "lookups", "hits")) +
+                   tuple(x for c in pa.pa_pool_pending_copies(pool) for x in c))
     return out
 
 
@@ -259,6 +280,8 @@ def _driver_input(nb, bs, order, ops):
             lines.append(f"a {op[1]} {op[2]}")
         elif op[0] == "batch":
             lines.append(f"b {op[1]} {len(op[2])} " + " ".join(map(str, op[2])))
+        elif op[0] == "tokens":
+            lines.append(f"k {op[1]} {len(op[2])} " + " ".join(map(str, op[2])))
         elif op[0] == "fork":
             lines.append(f"f {op[1]} {op[2]}")
         elif op[0] == "free":
@@ -275,6 +298,8 @@ def _model_lines(nb, bs, order, ops):
     for op, r, s in zip(ops, res[0::2], res[1::2]):
         if op[0] in ("append", "batch"):
             lines.append(" ".join([str(r[0])] + [str(x) for x in r[1]]))
+        elif op[0] == "tokens":
+            lines.append(" ".join([str(r[0])] + ([str(r[2])] + [str(x) for x in r[1]] if r[0] == 0 else [])))
         elif op[0] in ("fork", "free"):
             lines.append(str(r[0]))
         else:
@@ -297,11 +322,11 @@ def test_block_manager_under_asan_ubsan(tmp_path):
     assert r.returncode == 0, r.stderr
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
-    for seed in range(4):
+    for seed in range(6):
         rng = np.random.default_rng(200 + seed)
         nb, bs = 40, [8, 16, 32][seed % 3]
         order = rng.permutation(nb).tolist() if seed % 2 else None
-        ops = random_ops(rng, 400)
+        ops = random_ops(rng, 400) if seed < 4 else prefix_ops(rng, 300, bs)
         p = subprocess.run([exe], input=_driver_input(nb, bs, order, ops), capture_output=True, text=True,
                            env=env, timeout=120)
         assert p.returncode == 0, p.stderr[-3000:]
@@ -356,3 +381,60 @@ def test_step_entry_points_validate_before_launch():
     assert pa.lib.pa_step_graph_create(pool, ctypes.byref(e), ctypes.byref(g)) == pa.PA_ERR_INVALID
     assert "pending" in pa.pa_last_error()
     pa.pa_free_pool(pool)
+
+
+def prefix_ops(rng, n_ops, bs):
+    """Token-aware appends of sequences that share prompts, with frees (so
+    cached blocks are found on the free list and evicted by later pops),
+    continuations, forks and a few plain appends."""
+    templates = [rng.integers(0, 30, 6 * bs) for _ in range(4)]
+    ops, live, nxt = [], [], 0
+    for _ in range(n_ops):
+        r = rng.random()
+        if r < 0.45 or not live:
+            t = templates[int(rng.integers(0, 4))]
+            ids = list(t[:int(rng.integers(bs, 6 * bs + 1))]) + list(rng.integers(0, 30, int(rng.integers(0, bs))))
+            ops.append(("tokens", nxt, [int(x) for x in ids]))
+            live.append(nxt)
+            nxt += 1
+        elif r < 0.6:
+            s = live[int(rng.integers(0, len(live)))]
+            ops.append(("tokens", s, [int(x) for x in rng.integers(0, 30, int(rng.integers(0, 2 * bs)))]))
+        elif r < 0.8:
+            s = live.pop(int(rng.integers(0, len(live))))
+            ops.append(("free", s))
+        elif r < 0.9:
+            s = live[int(rng.integers(0, len(live)))]
+            ops.append(("fork", s, nxt))
+            live.append(nxt)
+            nxt += 1
+        else:
+            s = live[int(rng.integers(0, len(live)))]
+            ops.append(("append", s, int(rng.integers(0, bs))))
+    return ops
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefix_cache_streams_match_model(seed):
+    rng = np.random.default_rng(300 + seed)
+    nb, bs = 96, [8, 16, 32][seed % 3]
+    order = rng.permutation(nb) if seed % 2 else None
+    ops = prefix_ops(rng, 400, bs)
+    st, pool = make_pool(nb, bs, order)
+    assert st == 0
+    try:
+        got, want = run_abi(pool, ops), run_model(nb, bs, order, ops)
+        assert got == want
+        cached = sum(r[2] for op, r in zip(ops, want[0::2]) if op[0] == "tokens")
+        assert cached >= 5 * bs, f"stream exercised too few cached tokens ({cached})"
+        print(f"seed {seed} bs {bs}: {cached} cached tokens, {pa.pa_pool_prefix_stats(pool)}")
+    finally:
+        pa.pa_free_pool(pool)
+
+
+def test_tier_block_size_follows_the_page_tiers():
+    """Tiers printed in the inference overview page, §3.3: bs 32 below 1024
+    tokens, 16 from 1024 to below 8192, 8 from 8192 on."""
+    for L, bs in [(0, 32), (1, 32), (1023, 32), (1024, 16), (4096, 16), (8191, 16), (8192, 8), (32768, 8),
+                  (1 << 40, 8)]:
+        assert pa.pa_tier_block_size(L) == bs, L

@@ -73,7 +73,7 @@ def small(lens, Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", seed=5, **kw):
 
 
 # ------------------------------------------------------------------ scatter
-@pytest.mark.parametrize("name", ["tiny", "gqa8b", "prefix", "prefix_cow"])
+@pytest.mark.parametrize("name", ["tiny", "gqa8b", "prefix", "prefix_cow", "prompt_cache"])
 def test_write_kv_bit_exact(name):
     wl = W.config(name)
     gpu, ora = build_both(wl)
@@ -176,6 +176,20 @@ def test_decode_copy_on_write_prefix_full():
     assert st["pending_copies"] == 0
     got = widen_out(gpu.decode(512, gpu.workspace_for(512)), wl.dtype)
     assert_close(got, oracle_out(wl, ora), wl.dtype, "prefix_cow")
+    gpu.close()
+
+
+def test_decode_prompt_cache_full():
+    """48 requests appended with their token ids share a 1000-token prompt
+    found by prefix-cache lookup (no fork): the C++ manager agrees with the
+    model on tables, counters and cache keys; decode matches the oracle."""
+    wl = W.config("prompt_cache")
+    gpu, ora = build_both(wl)
+    from paged_kv_cache_indirect_amd import pa_pool_prefix_stats, pa_pool_stats
+    assert pa_pool_prefix_stats(gpu.pool) == ora.bm.prefix_stats()
+    assert pa_pool_stats(gpu.pool)["shared_blocks"] == 1000 // wl.block_size
+    got = widen_out(gpu.decode(512, gpu.workspace_for(512)), wl.dtype)
+    assert_close(got, oracle_out(wl, ora), wl.dtype, "prompt_cache")
     gpu.close()
 
 

@@ -277,3 +277,76 @@ def test_round_trip_catches_a_dropped_copy(monkeypatch):
     monkeypatch.setattr(BlockManagerModel, "append", forgetful)
     _, bad = _round_trip_mismatches(W.config("prefix_cow"))
     assert bad
+
+
+# ------------------------------------------------------------ prefix caching
+def test_prefix_cache_worked_example():
+    """Hand-derived: 8 blocks of 4 tokens, ascending free order (0 handed out first)."""
+    bm = BlockManagerModel(8, 4)
+    st, s, c = bm.append_tokens(0, [1, 2, 3, 4, 5, 6, 7, 8, 9])     # lookup of the first block misses
+    assert (st, c) == (OK, 0) and bm.tables[0] == [0, 1, 2] and s == list(range(9))
+    st, s, c = bm.append_tokens(1, [1, 2, 3, 4, 5, 6, 7, 8, 10, 11])  # two full blocks found
+    assert c == 8 and bm.tables[1] == [0, 1, 3] and s == [-1] * 8 + [12, 13]
+    st, s, c = bm.append_tokens(2, [1, 2, 3, 4, 9, 9, 9, 9])         # first found, second new
+    assert c == 4 and bm.tables[2] == [0, 4] and s == [-1] * 4 + [16, 17, 18, 19]
+    assert bm.free_seq(0) == OK and bm.free_seq(1) == OK
+    assert bm.free == [7, 6, 5, 2, 1, 3]                              # block 1 free but still keyed
+    st, s, c = bm.append_tokens(3, [1, 2, 3, 4, 5, 6, 7, 8])          # block 1 taken back off the free list
+    assert c == 8 and bm.tables[3] == [0, 1] and bm.free == [7, 6, 5, 2, 3] and bm.ref[1] == 1
+    assert bm.free_seq(2) == OK and bm.free == [7, 6, 5, 2, 3, 4]
+    st, s = bm.append(4, 5)                                          # plain append pops 4: its key is dropped
+    assert bm.tables[4] == [4, 3] and s == [16, 17, 18, 19, 12]
+    assert bm.prefix_stats()["cached_blocks"] == 2
+    st, s, c = bm.append_tokens(5, [1, 2, 3, 4, 9, 9, 9, 9])         # the evicted block misses now
+    assert c == 4 and bm.tables[5] == [0, 2] and s == [-1] * 4 + [8, 9, 10, 11]
+    assert bm.prefix_stats() == {"cached_blocks": 3, "lookups": 9, "hits": 6}
+    st, s, c = bm.append_tokens(6, [1, 2, 3, 4, 5, 6])
+    assert c == 4 and bm.tables[6] == [0, 5] and s == [-1] * 4 + [20, 21]   # positions 4, 5 of block 5
+    st, s, c = bm.append_tokens(6, [7, 8])                           # completes a block equal to block 1:
+    assert c == 0 and s == [22, 23]                                  # positions 6, 7 of block 5
+    assert bm.prefix_stats()["cached_blocks"] == 3                   # the key stays with block 1
+    assert bm.cache[(1, 2, 3, 4, 5, 6, 7, 8)] == 1 and 5 not in bm.block_key
+    bm.check_invariants()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefix_cache_invariants_on_streams(seed):
+    rng = np.random.default_rng(50 + seed)
+    bs = [4, 8, 16, 32][seed]
+    bm = BlockManagerModel(64, bs, rng.permutation(64))
+    tmpl = [list(rng.integers(0, 20, 5 * bs)) for _ in range(3)]
+    live, nxt = [], 0
+    for _ in range(300):
+        r = rng.random()
+        if r < 0.5 or not live:
+            ids = tmpl[int(rng.integers(0, 3))][:int(rng.integers(1, 5 * bs + 1))] + \
+                list(rng.integers(0, 20, int(rng.integers(0, bs))))
+            before = copy.deepcopy((bm.free, bm.ref, bm.tables, bm.lens, bm.cache, bm.block_key))
+            st, slots, c = bm.append_tokens(nxt, ids)
+            if st != OK:
+                assert copy.deepcopy((bm.free, bm.ref, bm.tables, bm.lens, bm.cache, bm.block_key)) == before
+            else:
+                live.append(nxt)
+                assert c == sum(1 for x in slots if x < 0) and c % bs == 0
+            nxt += 1
+        elif r < 0.75:
+            assert bm.free_seq(live.pop(int(rng.integers(0, len(live))))) == OK
+        else:
+            s = live[int(rng.integers(0, len(live)))]
+            bm.append_tokens(s, list(rng.integers(0, 20, int(rng.integers(0, 2 * bs)))))
+        bm.check_invariants()
+    assert bm.prefix_stats()["hits"] > 0
+
+
+def test_cache_round_trip_with_prefix_caching():
+    """48 requests share a 1000-token prompt, each appended with its token ids:
+    the 62 full prompt blocks are found by lookup (refcount 48), and every
+    sequence still reads back exactly its logical rows."""
+    import workloads as W
+    wl = W.config("prompt_cache")
+    c, bad = _round_trip_mismatches(wl)
+    assert bad == []
+    assert c.bm.prefix_stats()["hits"] == (wl.B - 1) * (1000 // 16)
+    shared = {int(b) for b in c.block_tables[0][:62]}
+    assert all(c.bm.ref[b] == wl.B for b in shared)
+    assert all(int(c.block_tables[s][62]) not in shared for s in range(wl.B))

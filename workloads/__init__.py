@@ -42,6 +42,10 @@ a parity case, not a benchmark configuration):
                sequences U[512,4096] plus 8 prefill sequences with cached
                context U[0,4096] taking 256-token chunks, 8 steps, 32/8, D 128,
                bf16, bs 16 (seed 1007).
+* ``prompt_cache`` - 48 requests sharing a 1000-token prompt (62 full
+               blocks + 8 tokens) plus own tokens U[1,600], each appended with
+               its token ids so that prefix caching finds the shared blocks;
+               32/8, D 128, bf16, bs 16 (seed 1008).
 * ``gqa8b_fp8`` - the ``gqa8b`` shape (seed 1006) with an FP8 (E4M3) cache:
                bf16 rows quantised with per-tensor scales k 0.0137, v 0.0129
                (N(0,1) values up to about 6 map inside ±448).
@@ -55,12 +59,12 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "Workload", "make_decode", "make_prefix_share", "make_prefill", "make_mixed",
+    "Workload", "make_decode", "make_prefix_share", "make_prefill", "make_mixed", "make_prompt_cache",
     "CONFIGS", "config", "round_to_bf16_bits", "draw_values", "mixed_step_queries", "ops_through",
 ]
 
 # Tags that separate the independent random streams of one workload.
-_TAG_LENS, _TAG_PERM, _TAG_KV, _TAG_Q, _TAG_PREFIX, _TAG_STEP = 0, 1, 2, 3, 4, 5
+_TAG_LENS, _TAG_PERM, _TAG_KV, _TAG_Q, _TAG_PREFIX, _TAG_STEP, _TAG_TOKENS = 0, 1, 2, 3, 4, 5, 6
 
 
 def _rng(seed: int, tag: int, index: int = 0) -> np.random.Generator:
@@ -94,7 +98,8 @@ class Workload:
     """A seeded synthetic paged-attention workload.
 
     ``ops`` is the block-manager operation stream that builds the cache:
-    ``("append", seq, n)``, ``("fork", src, dst)``, ``("free", seq)``.
+    ``("append", seq, n)``, ``("tokens", seq, ids)`` (a token-aware append of
+    len(ids) tokens), ``("fork", src, dst)``, ``("free", seq)``.
     After every ``append``, the ``n`` new logical rows
     ``kv_rows(seq, start, n)`` (positions start..start+n-1 of ``seq``) are to be
     written into the slots that append returned.
@@ -282,6 +287,30 @@ def make_prefix_share(name: str, B: int, prefix_len: int, suffix_lens: Sequence[
                     partition_tokens=partition_tokens)
 
 
+def make_prompt_cache(name: str, B: int, prompt_len: int, suffix_lens: Sequence[int], Hq: int, Hkv: int,
+                      D: int, block_size: int, dtype: str, seed: int, vocab: int = 32000,
+                      pool_factor: float = 1.1) -> Workload:
+    """B requests that start with the same ``prompt_len``-token prompt, each
+    appended in one token-aware call (op ``("tokens", seq, ids)``) so that the
+    block manager finds the prompt's full blocks by their token ids instead of
+    being told to fork. The K/V rows of prompt positions are the shared
+    prefix rows (equal ids at equal positions give equal K/V)."""
+    suffix_lens = np.asarray(suffix_lens, dtype=np.int32)
+    lens = (suffix_lens + prompt_len).astype(np.int32)
+    rng = _rng(seed, _TAG_TOKENS, 0)
+    prompt = rng.integers(0, vocab, prompt_len).astype(np.int32)
+    ops = []
+    for b in range(B):
+        own = _rng(seed, _TAG_TOKENS, b + 1).integers(0, vocab, int(suffix_lens[b])).astype(np.int32)
+        ops.append(("tokens", b, np.concatenate([prompt, own])))
+    full = prompt_len // block_size
+    need = full + int(sum(-(-int(L) // block_size) - full for L in lens))
+    nb, perm = _pool(seed, need, pool_factor, None)
+    return Workload(name=name, kind="decode", B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=block_size,
+                    dtype=dtype, seed=seed, seq_lens=lens, num_blocks=nb, free_order=perm, ops=ops,
+                    scale=1.0 / math.sqrt(D), prefix_len=prompt_len)
+
+
 def make_prefill(name: str, ctx_lens: Sequence[int], q_lens: Sequence[int], Hq: int, Hkv: int,
                  D: int, block_size: int, dtype: str, seed: int, pool_factor: float = 1.1) -> Workload:
     """Chunked prefill: each sequence has ``ctx`` cached tokens, then a ``q_len`` chunk.
@@ -376,6 +405,10 @@ def config(name: str) -> Workload:
         return make_mixed("mixed", _uniform_ints(s, 512, 4096, 56), _rng(s, _TAG_LENS, 1).integers(
                           0, 4097, 8).astype(np.int32), 256, 8, Hq=32, Hkv=8, D=128, block_size=16,
                           dtype="bf16", seed=s)
+    if name == "prompt_cache":
+        s = 1008
+        return make_prompt_cache("prompt_cache", 48, 1000, _uniform_ints(s, 1, 600, 48), Hq=32, Hkv=8, D=128,
+                                 block_size=16, dtype="bf16", seed=s)
     if name == "prefix_cow":
         s = 1005
         return make_prefix_share("prefix_cow", 32, 1000, _uniform_ints(s, 0, 300, 32), Hq=32,
