@@ -32,9 +32,14 @@
 //    Half the threads stage K, half V. Global loads run two tiles ahead of
 //    the multiply (two register staging sets) and block ids three, so the
 //    latency of a load is covered by two tiles of MFMA work and no load
-//    waits on a table lookup.
-//    Tokens past the causal end of the workgroup are staged as zeros (stale
-//    slots of the last block may hold anything).
+//    waits on a table lookup. A tile's block ids take one table load per
+//    lane; each thread picks its loads' ids with ds_bpermute just before the
+//    per-tile barrier, and a load's address is one 32x32-bit multiply-add.
+//    V rows past the causal end of the workgroup are staged as zeros (stale
+//    slots of the last block may hold anything, and a zero weight does not
+//    cancel a non-finite value); K rows there are left as loaded, since the
+//    causal mask replaces their scores.
+//  * MFMA operands are read from LDS four MFMAs ahead of their use.
 //  * Online softmax in base 2: the tile max is taken on raw scores, the
 //    scale is folded into one FMA ahead of exp2, and the running max is
 //    raised lazily (only when a tile exceeds it by more than 8), so most
@@ -187,17 +192,15 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
 
   const int32_t* trow = tables + static_cast<int64_t>(b) * max_blocks;
   const int64_t slot_stride = static_cast<int64_t>(Hkv) * D;
-  const uint16_t* kbase = kc + static_cast<int64_t>(g) * D;
-  const uint16_t* vbase = vc + static_cast<int64_t>(g) * D;
 
   // ---- staging roles: waves [0, 4) stage K chunks, waves [4, 8) stage V groups.
   // A K stager moves chunks (token, c) with c fastest across lanes (a 256-byte
   // row per 16 lanes). A V stager moves 4-token groups (tg, c) with tg fastest
   // across lanes, so the transposed LDS writes of one instruction spread over
-  // the banks. Both roles issue the same number of table and K/V loads, with
-  // no branch around them (addresses are clamped into the valid range, data
-  // past the causal end is zeroed afterwards): the compiler can then count
-  // loads in flight exactly and wait only for the ones a step needs.
+  // the banks. Both roles issue the same number of K/V loads, with no branch
+  // around them (block ids are clamped into the sequence's valid range): the
+  // compiler can then count loads in flight exactly and wait only for the
+  // ones a step needs.
   const bool k_stager = w < kWaves / 2;  // wave-uniform
   const int st_id = k_stager ? tid : tid - PG::kStageThreads;
   constexpr int kKTokStride = PG::kStageThreads / PG::kChunks;
@@ -214,48 +217,95 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     if (k_stager) return st_id % PG::kChunks;
     return (st_id + (i / GT) * PG::kStageThreads) / kGroupsPerTile;
   };
-  const uint16_t* stage_base = k_stager ? kbase : vbase;
 
   using StageRegs = uint4[PG::kSRegs];  // K: kKLoads chunks; V: 4 tokens per group
-  struct TileIds {
-    int id[PG::kSRegs];
-  };
-  // Block ids for one tile, fetched a tile ahead of its K/V loads.
-  auto fetch_ids = [&](int jt) {
-    TileIds ids;
-    const int t0 = jt * kKT;
+
+  // Per-thread constants of the staging pattern. A 64-token tile starts at a
+  // multiple of 64, so for block sizes up to 64 the block a load falls in
+  // (counted from the tile's first block) and its row inside that block are
+  // the same on every tile; for larger blocks the whole tile sits in one
+  // block at a row offset shared by the workgroup.
+  const bool small_bs = bs <= kKT;
+  const uint32_t blk_bytes = static_cast<uint32_t>(bs * slot_stride * 2);  // < 4 GiB, checked at launch
+  const char* stage_pool = reinterpret_cast<const char*>(k_stager ? kc : vc);
+  int st_bi4[PG::kSRegs];          // 4 x (block of load i within the tile): a ds_bpermute address
+  uint64_t st_off[PG::kSRegs];     // byte offset of load i's row, head and chunk inside its block
 #pragma unroll
-    for (int i = 0; i < PG::kSRegs; ++i) {
-      const int tok = min(t0 + stage_tok(i), kv_end - 1);
-      ids.id[i] = trow[tok >> bs_shift];  // range-checked where it is used
+  for (int i = 0; i < PG::kSRegs; ++i) {
+    const int tk = stage_tok(i);
+    st_bi4[i] = small_bs ? 4 * (tk >> bs_shift) : 0;
+    const int row = small_bs ? (tk & (bs - 1)) : tk;
+    st_off[i] = (static_cast<uint64_t>(row) * slot_stride + static_cast<uint64_t>(g) * D + 8 * stage_chunk(i)) * 2u;
+  }
+
+  // Block ids of one tile, one per lane (lane j: the tile's j-th block,
+  // clamped to the sequence's last block): one table load per lane, issued
+  // two tiles ahead of the K/V loads that use them.
+  auto fetch_ids = [&](int jt) {
+    const int blk0 = (jt * kKT) >> bs_shift;
+    const int last = (kv_end - 1) >> bs_shift;
+    return trow[min(blk0 + lane, last)];  // range-checked in spread_ids
+  };
+  // The block id of each of this thread's loads, taken from the lane that
+  // holds it. Done just before a barrier, whose LDS wait covers the permutes.
+  using LoadIds = int[PG::kSRegs];
+  // (Inline assembly keeps the permutes at this point; it waits for them
+  // itself, since the compiler does not count LDS operations it cannot see.)
+  auto spread_ids = [&](int ids, LoadIds& out) {
+    const int idc = clamp_blk(ids, num_blocks);
+    if constexpr (PG::kSRegs == 4) {
+      asm volatile(
+          "ds_bpermute_b32 %0, %4, %8\n\t"
+          "ds_bpermute_b32 %1, %5, %8\n\t"
+          "ds_bpermute_b32 %2, %6, %8\n\t"
+          "ds_bpermute_b32 %3, %7, %8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+          : "v"(st_bi4[0]), "v"(st_bi4[1]), "v"(st_bi4[2]), "v"(st_bi4[3]), "v"(idc));
+    } else {
+      static_assert(PG::kSRegs == 2, "two or four loads per staging thread");
+      asm volatile(
+          "ds_bpermute_b32 %0, %2, %4\n\t"
+          "ds_bpermute_b32 %1, %3, %4\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(out[0]), "=&v"(out[1])
+          : "v"(st_bi4[0]), "v"(st_bi4[1]), "v"(idc));
     }
-    return ids;
   };
 
-  auto load_tile = [&](int jt, const TileIds& ids, StageRegs& sreg) {
-    const int t0 = jt * kKT;
+  auto load_tile = [&](int jt, const LoadIds& ids, StageRegs& sreg) {
+    const uint64_t row_off =
+        small_bs ? 0 : static_cast<uint64_t>((jt * kKT) & (bs - 1)) * static_cast<uint64_t>(slot_stride) * 2u;
 #pragma unroll
     for (int i = 0; i < PG::kSRegs; ++i) {
-      const int tok = t0 + stage_tok(i);
-      const int tc = min(tok, kv_end - 1);
-      const int64_t slot = (static_cast<int64_t>(clamp_blk(ids.id[i], num_blocks)) << bs_shift) + (tc & (bs - 1));
-      // Rows past the causal end (tok >= kv_end) are zeroed when stored.
-      sreg[i] = *reinterpret_cast<const uint4*>(stage_base + slot * slot_stride + 8 * stage_chunk(i));
+      const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(ids[i])) * static_cast<uint64_t>(blk_bytes) + (st_off[i] + row_off);
+      // Rows past the causal end (a clamped block id: in-bounds, any data)
+      // are zeroed for V when stored and masked out of the scores for K.
+      sreg[i] = *reinterpret_cast<const uint4*>(stage_pool + off);
     }
   };
 
   auto store_tile = [&](int jt, const StageRegs& sreg_in) {
     uint16_t* ks = smem + (jt & 1) * PG::kBufElems;
     uint16_t* vt = ks + PG::kKElems;
-    StageRegs sreg;
-#pragma unroll
-    for (int i = 0; i < PG::kSRegs; ++i)
-      sreg[i] = jt * kKT + stage_tok(i) < kv_end ? sreg_in[i] : make_uint4(0, 0, 0, 0);
     if (k_stager) {
+      // K rows past the causal end need no zeroing: every tile that holds
+      // them takes the causal mask, which replaces their scores.
 #pragma unroll
       for (int i = 0; i < PG::kKLoads; ++i)
-        *reinterpret_cast<uint4*>(ks + stage_tok(i) * PG::kKPitch + 8 * stage_chunk(i)) = sreg[i];
+        *reinterpret_cast<uint4*>(ks + stage_tok(i) * PG::kKPitch + 8 * stage_chunk(i)) = sreg_in[i];
     } else {
+      // V rows past the causal end are zeroed (their weights are 0, but stale
+      // slots may hold non-finite values). Only the last tile has such rows.
+      StageRegs sreg;
+#pragma unroll
+      for (int i = 0; i < PG::kSRegs; ++i) sreg[i] = sreg_in[i];
+      if (jt * kKT + kKT > kv_end) {
+        asm volatile("" ::: "memory");  // keep this a branch, not selects on every tile
+#pragma unroll
+        for (int i = 0; i < PG::kSRegs; ++i)
+          if (jt * kKT + stage_tok(i) >= kv_end) sreg[i] = make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
       for (int gi = 0; gi < PG::kVGroups; ++gi) {
         const int c = stage_chunk(GT * gi);
@@ -305,19 +355,37 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     const uint16_t* ks = smem + buf * PG::kBufElems;
     const uint16_t* vt = ks + PG::kKElems;
 
-    // S^T = K · Q^T, one 32-key accumulator block at a time.
+    // S^T = K · Q^T, one 32-key accumulator block at a time. The K operands
+    // are read from LDS kAhead MFMAs ahead of their use, so each read's
+    // latency is covered by the MFMAs in between.
+    constexpr int kQK = PG::kSBlocks * PG::kKSteps;
+    constexpr int kAhead = 4;
     f32x16v s[PG::kSBlocks];
+    auto k_operand = [&](int idx) {
+      const int tb = idx / PG::kKSteps, st = idx % PG::kKSteps;
+      return __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(ks + k_lane + 32 * tb * PG::kKPitch + 8 * st));
+    };
+    bf16x8v kop[kAhead];
 #pragma unroll
-    for (int tb = 0; tb < PG::kSBlocks; ++tb) {
+    for (int u = 0; u < kAhead; ++u) kop[u] = k_operand(u);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[tb][v] = 0.f;
-      const uint16_t* krow = ks + k_lane + 32 * tb * PG::kKPitch;
-#pragma unroll
-      for (int st = 0; st < PG::kKSteps; ++st) {
-        const bf16x8v a = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(krow + 8 * st));
+    for (int idx = 0; idx < kQK; ++idx) {
+      const int tb = idx / PG::kKSteps, st = idx % PG::kKSteps;
+      const bf16x8v a = kop[idx % kAhead];
+      if (idx + kAhead < kQK) kop[idx % kAhead] = k_operand(idx + kAhead);
+      if (st == 0) {
+        s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], f32x16v{}, 0, 0, 0);
+      } else {
         s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[tb], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int idx = 0; idx < kQK - kAhead; ++idx) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 
     // Causal mask where the tile reaches past min_apos; tile max on raw scores.
     const int t0 = j * kKT;
@@ -364,43 +432,68 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
           p[2 * tb + hs][e] = static_cast<__bf16>(pe);
         }
 
-    // O^T += V^T · P^T.
+    // O^T += V^T · P^T, V operands read kAhead MFMAs ahead.
+    constexpr int kPV = PG::kDBlocks * PG::kPSteps;
+    auto v_operand = [&](int idx) {
+      const int db = idx / PG::kPSteps, k4 = idx % PG::kPSteps;
+      return __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(vt + v_lane + 32 * db * PG::kVPitch + 16 * k4));
+    };
+    bf16x8v vop[kAhead];
 #pragma unroll
-    for (int db = 0; db < PG::kDBlocks; ++db) {
-      const uint16_t* vrow = vt + v_lane + 32 * db * PG::kVPitch;
+    for (int u = 0; u < kAhead; ++u) vop[u] = v_operand(u);
 #pragma unroll
-      for (int ks4 = 0; ks4 < PG::kPSteps; ++ks4) {
-        const bf16x8v a = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(vrow + 16 * ks4));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[ks4], o[db], 0, 0, 0);
-      }
+    for (int idx = 0; idx < kPV; ++idx) {
+      const int db = idx / PG::kPSteps, k4 = idx % PG::kPSteps;
+      const bf16x8v a = vop[idx % kAhead];
+      if (idx + kAhead < kPV) vop[idx % kAhead] = v_operand(idx + kAhead);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[k4], o[db], 0, 0, 0);
     }
-
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int idx = 0; idx < kPV - kAhead; ++idx) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   };
   // Look-ahead loads are issued unconditionally (past the last tile they
   // re-read it, a cache hit) so that the count of loads in flight is the same
   // on every path and each wait covers only the data it needs.
-  auto iteration = [&](int j, StageRegs& in_flight, const StageRegs& arrived, TileIds& ids_next) {
-    const TileIds ids_after = fetch_ids(min(j + 3, n_tiles - 1));
+  auto iteration = [&](int j, StageRegs& in_flight, const StageRegs& arrived, LoadIds& ids_next) {
+    const int ids_after = fetch_ids(min(j + 3, n_tiles - 1));
     load_tile(min(j + 2, n_tiles - 1), ids_next, in_flight);
     compute_tile(j);
-    if (j + 1 < n_tiles) store_tile(j + 1, arrived);
-    ids_next = ids_after;
+    // Unconditional: past the last tile this stores the idle buffer. A
+    // conditional store would leave the register set's loads pending on one
+    // path into the next iteration, and the compiler would then wait for
+    // every load in flight before reusing those registers.
+    store_tile(j + 1, arrived);
+    spread_ids(ids_after, ids_next);
     __syncthreads();
   };
 
   StageRegs sreg_a, sreg_b;
-  TileIds ids_next{};
+  LoadIds ids_next;
   if (n_tiles > 0) {
-    load_tile(0, fetch_ids(0), sreg_a);
+    LoadIds ids0;
+    spread_ids(fetch_ids(0), ids0);
+    load_tile(0, ids0, sreg_a);
     store_tile(0, sreg_a);
-    load_tile(min(1, n_tiles - 1), fetch_ids(min(1, n_tiles - 1)), sreg_a);
-    ids_next = fetch_ids(min(2, n_tiles - 1));
+    spread_ids(fetch_ids(min(1, n_tiles - 1)), ids0);
+    load_tile(min(1, n_tiles - 1), ids0, sreg_a);
+    spread_ids(fetch_ids(min(2, n_tiles - 1)), ids_next);
   }
   __syncthreads();
-  for (int j = 0; j < n_tiles; j += 2) {
+  // Both halves of the pair run unconditionally, so every path into the next
+  // iteration has consumed both register sets (the compiler's wait counting
+  // merges paths and would otherwise wait for all loads in flight); an odd
+  // last tile runs after the loop.
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
     iteration(j, sreg_b, sreg_a, ids_next);
-    if (j + 1 < n_tiles) iteration(j + 1, sreg_a, sreg_b, ids_next);
+    iteration(j + 1, sreg_a, sreg_b, ids_next);
   }
+  if (j < n_tiles) iteration(j, sreg_b, sreg_a, ids_next);
 
   // ---- normalise and store (bf16, round to nearest even)
   const float lt = l + __shfl_xor(l, 32);
@@ -427,6 +520,8 @@ hipError_t LaunchTyped(const PrefillArgs& a, hipStream_t stream) {
   const int64_t items = PrefillWorkItems(a.Hkv, a.G, a.B, a.max_q_len);
   if (items == 0) return hipSuccess;
   if (items >= (int64_t{1} << 31) - 8) return hipErrorInvalidValue;
+  // The kernel forms a block's byte offset in 32 bits.
+  if (static_cast<int64_t>(a.block_size) * a.Hkv * D * 2 >= (int64_t{1} << 32)) return hipErrorInvalidValue;
   const int per_xcd = static_cast<int>((items + 7) / 8);
   const size_t lds = 2 * PGeom<D>::kBufElems * sizeof(uint16_t);
   // More than 64 KiB of dynamic LDS: raise the kernel's limit once.
