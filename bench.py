@@ -11,8 +11,9 @@ One step is one decode step of that batch, through the C ABI:
   2. table export (pa_block_tables) into pinned host memory, then one
      host-to-device copy of (slots, seq_lens, block_tables);
   3. pa_write_kv scatters the step's new K/V rows into the paged pool;
-  4. pa_decode: split-KV paged attention of the step's queries (512-token
-     partitions, merged by log-sum-exp).
+  4. pa_decode: paged attention of the step's queries, in the library's
+     default KV partitions (pa_decode_partition_tokens: here one partition
+     per sequence, so no log-sum-exp pass).
 The step's new K/V rows and queries are generated before timing and are
 resident in HBM. W untimed warm-up steps, then K timed steps between two
 device synchronisations.
@@ -32,7 +33,9 @@ batch shape (seed 1006), with the bytes it must read (1-byte K/V codes).
 (pa_step eager, and the same step captured once as a HIP graph and replayed).
 ``prefix_cache`` times token-aware appends with block lookups against blind
 appends and decodes the shared-prompt batch; ``tiered_block_sizes`` decodes
-batches split into per-length-tier pools against one bs-16 pool.
+batches split into per-length-tier pools against one bs-16 pool;
+``decode_skewed`` decodes a batch of short sequences with one very long one,
+in the library's default partitions and in fixed 512-token ones.
 """
 from __future__ import annotations
 
@@ -101,7 +104,7 @@ def run_decode(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import (harness, pa_block_tables, pa_decode,
+    from paged_kv_cache_indirect_amd import (harness, pa_block_tables, pa_decode, pa_decode_partition_tokens,
                                              pa_decode_workspace_bytes, pa_seq_append_batch,
                                              pa_write_kv)
 
@@ -126,7 +129,8 @@ def run_decode(args):
     # Grid and table width sized once for the longest sequence after S steps.
     max_len = wl.max_seq_len + S
     max_blocks = -(-max_len // bs)
-    pt = args.partition_tokens
+    pt = args.partition_tokens    # 0: the library's choice
+    pt_used = pt or pa_decode_partition_tokens(pool, B, max_len)
     ws_bytes = pa_decode_workspace_bytes(B, Hq, D, max_len, pt)
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
@@ -195,6 +199,7 @@ def run_decode(args):
         "bytes_per_launch": float(np.mean(step_bytes)),
         "kv_bytes_per_step": float(np.mean(step_kv)),
         "achieved_gbps": achieved,
+        "partition_tokens": pt_used,
         "mean_len": float(np.mean([np.mean(lens_per_step[s]) for s in timed])),
         "max_len_bound": max_len,
         "num_blocks": wl.num_blocks,
@@ -216,10 +221,13 @@ def run_decode_fp8(args):
     from paged_kv_cache_indirect_amd import harness
 
     dev = torch.device("cuda:0")
+    from paged_kv_cache_indirect_amd import pa_decode_partition_tokens
+
     wl = W.config("gqa8b_fp8")
     log(f"[bench] building gqa8b_fp8 cache: B={wl.B} nb={wl.num_blocks}")
     cache = harness.GpuCache(wl, device=dev, poison=False)
-    pt = args.fp8_partition_tokens
+    pt = args.partition_tokens    # 0: the library's choice
+    pt_used = pt or pa_decode_partition_tokens(cache.pool, wl.B, wl.max_seq_len)
     ws = cache.workspace_for(pt)
     for _ in range(3):
         cache.decode(pt, ws)
@@ -243,12 +251,47 @@ def run_decode_fp8(args):
         "workload": "8B-shaped GQA decode over an FP8 (OCP E4M3) pool: batch 64, 32 q / 8 kv heads, "
                     "head_dim 128, bf16 q/out, block_size 16, lengths U[512,4096] (seed 1006), "
                     "per-tensor scales k 0.0137 / v 0.0129",
-        "partition_tokens": pt,
+        "partition_tokens": pt_used,
         "us_mean": t * 1e6, "us_median": float(np.median(ms)) * 1e3, "us_min": float(np.min(ms)) * 1e3,
         "tok_per_s": wl.B / t,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "bytes_per_launch": nbytes},
     }
+
+
+def run_decode_skewed(args):
+    """A batch whose one long sequence dominates (63 x 512 tokens + 1 x 32768,
+    8B-shaped heads): the library's default partition against a fixed 512."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_indirect_amd import harness, pa_decode_partition_tokens
+
+    wl = W.make_decode("skewed", [512] * 63 + [32768], Hq=32, Hkv=8, D=128, block_size=16, dtype="bf16", seed=77)
+    cache = harness.GpuCache(wl, poison=False)
+    res = {"workload": "63 x 512-token sequences + 1 x 32768, Hq 32 / Hkv 8, D 128, bf16, bs 16 (seed 77)"}
+    stream = torch.cuda.current_stream()
+    for label, pt in (("default", 0), ("fixed_512", 512)):
+        ws = cache.workspace_for(pt)
+        for _ in range(3):
+            cache.decode(pt, ws)
+        n = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            cache.decode(pt, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / n * 1e-3
+        nbytes = decode_bytes(wl, wl.seq_lens)
+        res[label] = {"partition_tokens": pt or pa_decode_partition_tokens(cache.pool, wl.B, wl.max_seq_len),
+                      "us_mean": t * 1e6, "gbps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+    cache.close()
+    log(f"[bench] skewed batch: default pt {res['default']['partition_tokens']} {res['default']['us_mean']:.1f} us, "
+        f"pt 512 {res['fixed_512']['us_mean']:.1f} us")
+    return res
 
 
 # ----------------------------------------------------------------- mixed step
@@ -317,7 +360,8 @@ def run_prefix_cache(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import (harness, pa_alloc_pool, pa_free_pool, pa_pool_prefix_stats,
+    from paged_kv_cache_indirect_amd import (harness, pa_alloc_pool, pa_decode_partition_tokens, pa_free_pool,
+                                             pa_pool_prefix_stats,
                                              pa_pool_stats, pa_seq_append, pa_seq_append_tokens)
 
     wl = W.config("prompt_cache")
@@ -349,7 +393,8 @@ def run_prefix_cache(args):
     del kc, vc
     torch.cuda.empty_cache()
     cache = harness.GpuCache(wl, poison=False)
-    ppt = 1024   # the shared-prompt batch: 3 partitions of its 1000-1600-token sequences
+    ppt = 0      # the library's choice
+    ppt_used = pa_decode_partition_tokens(cache.pool, wl.B, wl.max_seq_len)
     ws = cache.workspace_for(ppt)
     for _ in range(3):
         cache.decode(ppt, ws)
@@ -366,7 +411,7 @@ def run_prefix_cache(args):
     t = float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)])) * 1e-3
     nbytes = decode_bytes(wl, wl.seq_lens)
     cache.close()
-    res["decode"] = {"partition_tokens": ppt, "us_mean": t * 1e6, "logical_gbps": nbytes / t / 1e9,
+    res["decode"] = {"partition_tokens": ppt_used, "us_mean": t * 1e6, "logical_gbps": nbytes / t / 1e9,
                      "unique_kv_bytes": wl.unique_kv_bytes(), "logical_kv_bytes": wl.kv_bytes()}
     log(f"[bench] prefix cache: {res['tokens']['host_ns_per_token']:.0f} ns/token with lookups, "
         f"{res['blind']['host_ns_per_token']:.0f} blind; decode {t * 1e6:.1f} us")
@@ -398,10 +443,10 @@ def run_tiered(args):
                 wl = W.make_decode(f"{name}_{label}_{bs}", lens, Hq=32, Hkv=8, D=128, block_size=bs, dtype="bf16",
                                    seed=base.seed + 100 * (i + 1))
                 caches.append((wl, harness.GpuCache(wl, poison=False)))
-            wss = [c.workspace_for(512) for _, c in caches]
+            wss = [c.workspace_for(0) for _, c in caches]
             for _ in range(3):
                 for (_, c), w in zip(caches, wss):
-                    c.decode(512, w)
+                    c.decode(0, w)
             n = 20
             stream = torch.cuda.current_stream()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -409,7 +454,7 @@ def run_tiered(args):
             e0.record(stream)
             for _ in range(n):
                 for (_, c), w in zip(caches, wss):
-                    c.decode(512, w)
+                    c.decode(0, w)
             e1.record(stream)
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) / n * 1e-3
@@ -530,9 +575,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition-tokens", type=int, default=512)
-    ap.add_argument("--fp8-partition-tokens", type=int, default=2048,
-                    help="KV partition of the FP8 leg (fewer, longer partitions suit its VALU-bound kernel)")
+    ap.add_argument("--partition-tokens", type=int, default=0,
+                    help="KV partition of the decode legs (0: the library's choice, pa_decode_partition_tokens)")
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -578,6 +622,7 @@ def main() -> int:
     mixed = None if args.no_mixed else run_mixed(args)
     pcache = None if args.no_extras else run_prefix_cache(args)
     tiers = None if args.no_extras else run_tiered(args)
+    skewed = None if args.no_extras else run_decode_skewed(args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, wl)
 
     line = {
@@ -596,9 +641,9 @@ def main() -> int:
         "config": {
             "workload": "8B-shaped GQA paged decode step: batch 64, 32 q / 8 kv heads, head_dim 128, "
                         "bf16, block_size 16, lengths U[512,4096] (seed 1001), shuffled pool of 1.1x need; "
-                        "step = block-manager append + table export/H2D + KV scatter + split-KV decode",
+                        "step = block-manager append + table export/H2D + KV scatter + decode (library's KV partitions)",
             "global_batch": wl.B,
-            "partition_tokens": args.partition_tokens,
+            "partition_tokens": dec["partition_tokens"],
             "mean_seq_len": dec["mean_len"],
         },
         "decode": {
@@ -616,7 +661,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": frac,
             "traffic": measured_traffic("decode"),
-            "kernel": "paged decode (partition + log-sum-exp merge)",
+            "kernel": "paged decode (DecodeKernel; log-sum-exp MergeKernel only for sequences split into partitions)",
             "bytes_per_launch": dec["bytes_per_launch"],
         },
         "cpu_baseline": cpu,
@@ -625,6 +670,7 @@ def main() -> int:
         "mixed_step": mixed,
         "prefix_cache": pcache,
         "tiered_block_sizes": tiers,
+        "decode_skewed": skewed,
     }
     print(json.dumps(line), flush=True)
     return 0

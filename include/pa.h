@@ -241,10 +241,24 @@ pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value,
  * are split into KV partitions of partition_tokens tokens, and when a
  * sequence spans more than one, the workspace holds the fp32 partial state
  * (max, sum, Σ weight·V) of every (sequence, q head, partition). 0 when one
- * partition covers max_seq_len. partition_tokens 0 means the default (512).
- * Returns 0 for invalid arguments. */
+ * partition covers max_seq_len. partition_tokens 0 means the library's
+ * choice (pa_decode_partition_tokens); the size returned for 0 covers it
+ * (that choice is never shorter than 512 tokens unless one partition covers
+ * max_seq_len). Returns 0 for invalid arguments. */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_seq_len, int32_t partition_tokens);
+
+/* The KV partition pa_decode uses for partition_tokens = 0: one partition
+ * per sequence up to 8192 tokens, split further only while the launch has
+ * fewer than 512 (sequence, kv head, partition) work items, never below 512
+ * tokens, rounded up to a multiple of 64. Fewest, longest partitions ran
+ * fastest on MI355X (no log-sum-exp pass when one partition covers every
+ * sequence); the 8192 cap keeps one long sequence in a batch of short ones
+ * from being left to a few workgroups. (The split into partitions merged by
+ * log-sum-exp is this library's; the pages' decode walks a sequence's
+ * blocks in one pass: "vLLM的'内存分页'到底多神奇", xxqk.cn, §3 phase 2.)
+ * Returns 0 for a null pool or negative sizes. */
+int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t B, int32_t max_seq_len);
 
 /* Decode attention: one query token per sequence over its paged cache.
  * out (device): [B, num_q_heads, head_dim], pool dtype (bf16 for an FP8
@@ -263,8 +277,8 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
  * partition_tokens: long contexts are split into KV partitions of this many
  *   tokens, each reduced to (max, sum, Σ weight·V), then merged by
  *   log-sum-exp (a second launch, only when some sequence spans more than
- *   one partition). 0 = 512. Must be a multiple of 64, at most 2048 (else
- *   PA_ERR_UNSUPPORTED).
+ *   one partition). 0 = the library's choice (pa_decode_partition_tokens).
+ *   Must be a multiple of 64, at most 2^24, else PA_ERR_UNSUPPORTED.
  * workspace (device, 16-byte aligned, contents irrelevant) of
  *   workspace_bytes ≥ pa_decode_workspace_bytes(...); may be NULL when that
  *   is 0. Calls that may run concurrently (different streams) need separate

@@ -26,7 +26,7 @@ __all__ = [
     "pa_block_tables", "pa_pool_stats", "pa_pool_pending_copies", "pa_pool_set_kv_scales", "pa_write_kv",
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error", "StepDesc", "pa_step",
     "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy", "pa_seq_append_tokens",
-    "pa_pool_prefix_stats", "pa_tier_block_size",
+    "pa_pool_prefix_stats", "pa_tier_block_size", "pa_decode_partition_tokens",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
@@ -92,6 +92,7 @@ _SIGS = {
     "pa_pool_pending_copies": (_i32, [_vp, _vp, _vp, _i32, _vp]),
     "pa_write_kv": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_partition_tokens": (_i32, [_vp, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
@@ -253,6 +254,11 @@ def pa_write_kv(pool: int, key, value, slot_mapping, stream=None) -> None:
 def pa_decode_workspace_bytes(B: int, num_q_heads: int, head_dim: int, max_seq_len: int,
                               partition_tokens: int = 0) -> int:
     return int(lib.pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_seq_len, partition_tokens))
+
+
+def pa_decode_partition_tokens(pool: int, B: int, max_seq_len: int) -> int:
+    """The KV partition pa_decode uses for partition_tokens=0 on this pool."""
+    return int(lib.pa_decode_partition_tokens(pool, B, max_seq_len))
 
 
 def pa_decode(pool: int, out, q, block_tables, seq_lens, scale: float, max_seq_len: int,

@@ -18,10 +18,11 @@
 //    together in a single pass. Eight lanes cover one D-element row with
 //    16-byte loads (one load instruction fetches 8 whole rows); the loads of
 //    a batch of steps are issued together, then consumed.
-//  * The block ids of the wave's range (at most 64) are loaded once, one per
-//    lane, and broadcast per step with v_readlane (an SGPR), so the table
-//    lookup is off the per-row dependency chain — the extra indirection
-//    paging adds ("LLM推理优化", §2.2) costs one readlane per 8 rows.
+//  * The block ids of the wave's range are loaded 64 at a time, one per
+//    lane (the next 64 while the current ones stream), and broadcast per
+//    step with v_readlane (an SGPR), so the table lookup is off the per-row
+//    dependency chain — the extra indirection paging adds ("LLM推理优化",
+//    §2.2) costs one readlane per 8 rows.
 //  * Each 8-lane row group keeps its own online-softmax state (running max,
 //    sum, Σ w·V for the G heads). q·k: v_dot2_f32_bf16 plus a 3-step DPP sum.
 //    Weights: one exp2 per (token, head) on scores pre-scaled to log2 units;
@@ -39,10 +40,16 @@
 //    kernel through an arrival counter needs an agent-scope release/acquire
 //    per partition — an L2 writeback and invalidate per workgroup on this
 //    chip — which measured far slower than one extra launch.)
-//  * Work items are mapped XCD-major with the kv head outermost: consecutive
-//    hardware workgroup ids go to different XCDs, so each XCD owns a
-//    contiguous range (one kv head when Hkv = 8) and a shared prefix block of
-//    that head is re-read from one XCD's L2.
+//  * Work items are the (kv head, sequence, partition) triples that exist:
+//    each workgroup prefix-sums the sequences' partition counts (batches up
+//    to 1024) and takes its item from that compact list, so partitions past a
+//    sequence's end do not occupy workgroup slots between real ones (the
+//    grid is sized for every sequence at max_seq_len; its surplus comes last
+//    and exits). Measured on MI355X, interleaved empty workgroups slowed a
+//    launch by up to 2.4x. Items are mapped XCD-major with the kv head
+//    outermost: consecutive hardware workgroup ids go to different XCDs, so
+//    each XCD owns a contiguous range (one kv head when Hkv = 8) and a shared
+//    prefix block of that head is re-read from one XCD's L2.
 #include "device_common.h"
 #include "launch.h"
 
@@ -52,6 +59,7 @@ namespace {
 
 constexpr int kWaves = 4;                 // waves per workgroup (one partition)
 constexpr int kThreads = 64 * kWaves;
+constexpr int kCompactBatch = 1024;  // batches up to this size get a compact work list
 constexpr int kLanesPerRow = 8;
 constexpr int kRowsPerStep = 64 / kLanesPerRow;
 constexpr float kLazyMax = 8.f;
@@ -194,12 +202,65 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
 
   // ---- work item (XCD-major; kv head, then sequence, then partition)
   const int wg = blockIdx.x;
-  const int item = (wg & 7) * per_xcd + (wg >> 3);
-  if (item >= Hkv * B * P) return;
-  const int p = item % P;
-  const int bg = item / P;
-  const int b = bg % B;
-  const int g = bg / B;
+  int p, b, g;
+  if (B <= kCompactBatch) {
+    // Compact work list: only the (kv head, sequence, partition) items that
+    // exist, kv head outermost, XCD-major over the real count; the grid's
+    // surplus workgroups (sized for B x P) come last and exit.
+    __shared__ int s_pref[kCompactBatch + 1];
+    __shared__ int s_wsum[kWaves];
+    constexpr int kPer = kCompactBatch / kThreads;  // sequences per thread
+    int cnt[kPer];
+    int tsum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int bb = tid * kPer + i;
+      int Lb = bb < B ? seq_lens[bb] : 0;
+      Lb = min(max(Lb, 0), max_seq_len);
+      cnt[i] = bb < B ? max(1, (Lb + PT - 1) / PT) : 0;
+      tsum += cnt[i];
+    }
+    // inclusive scan of tsum over the workgroup
+    int incl = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_wsum[w] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int ww = 0; ww < w; ++ww) wbase += s_wsum[ww];
+    int run = wbase + incl - tsum;  // exclusive prefix of this thread
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      s_pref[tid * kPer + i] = run;
+      run += cnt[i];
+    }
+    if (tid == kThreads - 1) s_pref[kCompactBatch] = run;
+    __syncthreads();
+    const int S = s_pref[kCompactBatch];  // items per kv head
+    const int per_xcd_real = (Hkv * S + 7) / 8;
+    if ((wg >> 3) >= per_xcd_real) return;
+    const int item = (wg & 7) * per_xcd_real + (wg >> 3);
+    if (item >= Hkv * S) return;
+    g = item / S;
+    const int k = item - g * S;
+    int lo = 0, hi = B - 1;  // largest b with s_pref[b] <= k
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= k) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    p = k - s_pref[b];
+  } else {
+    const int item = (wg & 7) * per_xcd + (wg >> 3);
+    if (item >= Hkv * B * P) return;
+    p = item % P;
+    const int bg = item / P;
+    b = bg % B;
+    g = bg / B;
+  }
   const int Hq = Hkv * G;
 
   int L = seq_lens[b];
@@ -225,15 +286,22 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
           qf[h][i][qq] = *reinterpret_cast<const uint4*>(qb + h * D + (j + kLanesPerRow * i) * EPC + qq * EPQ);
   }
 
-  // Block ids of the wave's range (at most 64): lane x holds logical block lb0 + x.
-  // Steps start on multiples of 8 tokens and block sizes are multiples of 8,
-  // so the 8 rows of one step always sit in one block.
+  // Block ids of the wave's range, 64 at a time (a window): lane x holds
+  // logical block lbw + x of the current window, and the next window's ids
+  // are loaded while this one streams. Steps start on multiples of 8 tokens
+  // and block sizes are multiples of 8, so the 8 rows of one step always sit
+  // in one block; wave ranges start on multiples of 16 tokens, so every
+  // window but the last covers an even number of steps.
+  constexpr int kWinBlocks = 64;
   const int bs = 1 << bs_shift;
   const int32_t* trow = tables + static_cast<int64_t>(b) * max_blocks;
   const int lb0 = w0 >> bs_shift;
-  const int lb_end = (w0 + ntok + bs - 1) >> bs_shift;
+  // A wave with no tokens has no blocks (its start may lie past the table's
+  // last entry when it falls inside a block).
+  const int lb_end = ntok > 0 ? (w0 + ntok + bs - 1) >> bs_shift : lb0;
   int my_blk = 0;
   if (lb0 + lane < lb_end) my_blk = clamp_block(trow[lb0 + lane], num_blocks);
+  int lbw = lb0;  // first block of the current window
 
   const int64_t row_stride = static_cast<int64_t>(Hkv) * D;  // elements between slots
   const KV* kbase = kc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
@@ -253,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
   auto issue = [&](int st, int u) {
     const int tok = w0 + st * kRowsPerStep;
     const int lb = tok >> bs_shift;
-    const int blk = __builtin_amdgcn_readlane(my_blk, lb - lb0);
+    const int blk = __builtin_amdgcn_readlane(my_blk, lb - lbw);
     const int64_t slot0 = (static_cast<int64_t>(blk) << bs_shift) + (tok & (bs - 1));
     const KV* krow = kbase + slot0 * row_stride;
     const KV* vrow = vbase + slot0 * row_stride;
@@ -336,18 +404,25 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
     }
   };
 
-  // Batches of U steps: all U steps' loads are issued (a step past the end
-  // re-reads the last one, a cache hit, so the count of loads in flight is
-  // the same on every path), then consumed in pairs.
-  for (int st0 = 0; st0 < nsteps; st0 += U) {
+  // Per window, batches of U steps: all U steps' loads are issued (a step
+  // past the window's end re-reads its last one, a cache hit, so the count of
+  // loads in flight is the same on every path), then consumed in pairs.
+  for (; lbw < lb_end; lbw += kWinBlocks) {
+    const int st_begin = max(0, (lbw << bs_shift) - w0) / kRowsPerStep;
+    const int st_end = min(nsteps, (((lbw + kWinBlocks) << bs_shift) - w0) / kRowsPerStep);
+    // Next window's ids (clamped index: a valid entry on every lane).
+    const int next_blk = trow[min(lbw + kWinBlocks + lane, lb_end - 1)];
+    for (int st0 = st_begin; st0 < st_end; st0 += U) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) issue(min(st0 + u, nsteps - 1), u);
-    // Keep all U steps' loads ahead of the math (the scheduler would sink
-    // each load next to its first use, exposing memory latency per step).
-    __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < U; ++u) issue(min(st0 + u, st_end - 1), u);
+      // Keep all U steps' loads ahead of the math (the scheduler would sink
+      // each load next to its first use, exposing memory latency per step).
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; u += 2)
-      if (st0 + u < nsteps) consume_pair(st0 + u, u);
+      for (int u = 0; u < U; u += 2)
+        if (st0 + u < st_end) consume_pair(st0 + u, u);
+    }
+    my_blk = clamp_block(next_blk, num_blocks);
   }
 
   // ---- merge the 8 row groups of the wave (lanes that differ in bits 3..5)

@@ -73,6 +73,29 @@ inline int64_t PrefillWorkItems(int32_t Hkv, int32_t G, int32_t B, int32_t max_q
 }
 
 // Grid / workspace geometry shared by the API layer and the launchers.
+//
+// The library's decode partition when the caller passes 0. Measured on
+// MI355X, a decode launch runs fastest with the fewest, longest partitions
+// that still give the GPU enough workgroups (no log-sum-exp pass when one
+// partition covers every sequence), as long as no single sequence is left
+// to a few workgroups: a batch with one very long sequence among short ones
+// needs that sequence split. So: one partition per sequence up to
+// kDecodeDefaultMaxPartition tokens, split further only while the launch has
+// fewer than kDecodeTargetItems (sequence, kv head, partition) items, never
+// below 512 tokens; rounded up to a multiple of 64.
+constexpr int64_t kDecodeTargetItems = 512;
+constexpr int32_t kDecodeDefaultMaxPartition = 8192;
+constexpr int32_t kDecodeMaxPartition = 1 << 24;
+inline int32_t DecodeDefaultPartition(int32_t B, int32_t Hkv, int32_t max_seq_len) {
+  const int64_t len = max_seq_len > 1 ? max_seq_len : 1;
+  const int64_t pairs = static_cast<int64_t>(B > 1 ? B : 1) * (Hkv > 1 ? Hkv : 1);
+  const int64_t parts = (kDecodeTargetItems + pairs - 1) / pairs;
+  int64_t pt = (len + parts - 1) / parts;
+  pt = (pt + 63) / 64 * 64;
+  if (pt > kDecodeDefaultMaxPartition) pt = kDecodeDefaultMaxPartition;
+  if (pt < 512) pt = 512;
+  return static_cast<int32_t>(pt);
+}
 inline int32_t DecodePartitions(int32_t max_seq_len, int32_t partition_tokens) {
   int32_t p = (max_seq_len + partition_tokens - 1) / partition_tokens;
   return p < 1 ? 1 : p;

@@ -180,9 +180,11 @@ pa_status PrepareDecode(const pa_pool& pool, void* out, const void* q, const int
   const pa_kv_layout& l = pool.layout;
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * l.block_size)
     return Fail(PA_ERR_INVALID, "max_seq_len exceeds max_blocks * block_size");
-  const int32_t pt = partition_tokens == 0 ? 512 : partition_tokens;
-  if (pt % 64 || pt > 2048)
-    return Fail(PA_ERR_UNSUPPORTED, "partition_tokens must be a multiple of 64, at most 2048");
+  const int32_t pt =
+      partition_tokens == 0 ? pa::DecodeDefaultPartition(B, l.num_kv_heads, max_seq_len) : partition_tokens;
+  if (pt % 64 || pt > pa::kDecodeMaxPartition)
+    return Fail(PA_ERR_UNSUPPORTED, "partition_tokens must be a multiple of 64, at most " +
+                                        std::to_string(pa::kDecodeMaxPartition));
   const int32_t P = pa::DecodePartitions(max_seq_len, pt);
   if (static_cast<int64_t>(P) * B * l.num_kv_heads >= (int64_t{1} << 31) - 8)
     return Fail(PA_ERR_UNSUPPORTED, "grid too large");
@@ -437,8 +439,16 @@ pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value, const i
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_seq_len, int32_t partition_tokens) {
   if (B < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_tokens < 0) return 0;
+  // 0: the library's choice, which is never shorter than 512 tokens (or it
+  // covers max_seq_len in one partition), so 512 bounds its workspace.
   const int32_t pt = partition_tokens == 0 ? 512 : partition_tokens;
   return pa::DecodeWorkspaceBytes(B, num_q_heads, head_dim, pa::DecodePartitions(max_seq_len, pt));
+}
+
+int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t B, int32_t max_seq_len) {
+  if (!pool || B < 0 || max_seq_len < 0) return 0;
+  const pa_kv_layout& l = pool->layout;
+  return pa::DecodeDefaultPartition(B, l.num_kv_heads, max_seq_len);
 }
 
 pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* block_tables,

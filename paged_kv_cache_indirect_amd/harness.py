@@ -151,7 +151,7 @@ class MixedRunner:
     one host-to-device copy per buffer.
     """
 
-    def __init__(self, wl, device="cuda", use_graph: bool = False, partition_tokens: int = 512):
+    def __init__(self, wl, device="cuda", use_graph: bool = False, partition_tokens: int = 0):
         from . import StepDesc
         p = wl.plan
         self.wl, self.device, self.use_graph = wl, device, use_graph

@@ -232,6 +232,39 @@ def test_alloc_pool_rejects_bad_geometry():
     assert make_pool(4, 16, dtype=7)[0] == pa.PA_ERR_UNSUPPORTED
 
 
+def test_decode_partition_policy():
+    """The library's partition for partition_tokens = 0: one partition per
+    sequence up to 8192 tokens, split further only while the launch has fewer
+    than 512 (sequence, kv head, partition) items, never below 512 tokens,
+    rounded up to a multiple of 64."""
+    pools = {bs: make_pool(64, bs, hkv=8, d=128)[1] for bs in (8, 16, 32)}
+    f = pa.pa_decode_partition_tokens
+    p16 = pools[16]
+    assert f(p16, 64, 4087) == 4096       # 8B-shaped batch: 512 items, one partition per sequence
+    assert f(p16, 64, 4142) == 4160       # ... also past 4096 tokens
+    assert f(p16, 64, 32768) == 8192      # capped: one long sequence is not left to one workgroup per head
+    assert f(p16, 8, 32768) == 4096       # long contexts: 8 partitions -> 512 items
+    assert f(p16, 128, 3068) == 3072
+    assert f(p16, 48, 1591) == 832        # 384 pairs: two partitions
+    assert f(p16, 1, 32768) == 512        # 8 pairs: 64 partitions of 512
+    assert f(p16, 4, 50) == 512 and f(p16, 0, 0) == 512
+    assert f(pools[8], 64, 20000) == 8192 and f(pools[32], 64, 2000) == 2048   # block size plays no part
+    assert f(None, 4, 100) == 0 and f(p16, -1, 100) == 0
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        B = int(rng.integers(0, 300))
+        L = int(rng.integers(0, 70000))
+        pt = f(p16, B, L)
+        assert pt % 64 == 0 and 512 <= pt <= 8192, (B, L, pt)
+        parts = -(-max(L, 1) // pt)
+        # more than one partition only when capped, or when needed for 512 items
+        assert parts == 1 or pt == 8192 or pt == 512 or max(B, 1) * 8 * (parts - 1) < 512, (B, L, pt)
+        # the 512-token workspace bounds the default's
+        assert pa.lib.pa_decode_workspace_bytes(B, 32, 128, L, pt) <= pa.lib.pa_decode_workspace_bytes(B, 32, 128, L, 0)
+    for p in pools.values():
+        pa.pa_free_pool(p)
+
+
 def test_device_entry_points_validate_before_launch():
     st, pool = make_pool(64, 16, hkv=8, d=128)
     assert st == 0
@@ -255,8 +288,10 @@ def test_device_entry_points_validate_before_launch():
     # partition size rules
     assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 32, 0.1, 4096, 100, dummy, 1 << 30, None) \
         == pa.PA_ERR_UNSUPPORTED
-    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 64, 0.1, 4096, 4096, dummy, 1 << 30, None) \
+    big = (1 << 24) + 64   # past the largest partition accepted
+    assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 32, 0.1, 4096, big, dummy, 1 << 30, None) \
         == pa.PA_ERR_UNSUPPORTED
+    assert "at most 16777216" in pa.pa_last_error()
     # misaligned q
     assert pa.lib.pa_decode(pool, dummy, dummy + 2, dummy, 256, dummy, 4, 32, 0.1, 4096, 0, dummy, ws, None) \
         == pa.PA_ERR_INVALID

@@ -135,7 +135,7 @@ def test_decode_gqa8b_full():
     wl = W.config("gqa8b")
     gpu, ora = build_both(wl)
     ref = oracle_out(wl, ora)
-    for pt in (512, 256, 1024, 2048):
+    for pt in (512, 256, 1024, 2048, 4096, 0):   # 0: the library's choice (one 4096-token partition)
         ws = gpu.workspace_for(pt)
         got = widen_out(gpu.decode(pt, ws), wl.dtype)
         assert_close(got, ref, wl.dtype, f"gqa8b pt={pt}")
@@ -146,8 +146,10 @@ def test_decode_long_context_sampled():
     wl = W.config("long")
     sample = [0, 5]
     gpu, ora = build_both(wl, only=sample)
-    got = widen_out(gpu.decode(512, gpu.workspace_for(512)), wl.dtype)[sample]
-    assert_close(got, oracle_out(wl, ora, sample), wl.dtype, "long (sampled seqs 0, 5)")
+    ref = oracle_out(wl, ora, sample)
+    for pt in (512, 4096, 0):   # 0: the library's choice (8 partitions of 4096)
+        got = widen_out(gpu.decode(pt, gpu.workspace_for(pt)), wl.dtype)[sample]
+        assert_close(got, ref, wl.dtype, f"long pt={pt} (sampled seqs 0, 5)")
     gpu.close()
 
 
@@ -234,6 +236,23 @@ def test_write_kv_with_no_rows_runs_pending_copies():
         assert np.array_equal(k[b], k[src]) and np.array_equal(k[c], k[src])
     finally:
         pa.pa_free_pool(pool)
+
+
+@pytest.mark.parametrize("bs,pt", [(8, 2048), (8, 8192), (16, 4096), (16, 16384), (32, 8000), (32, 16000)])
+def test_decode_long_partitions(bs, pt):
+    """Long partitions: each wave streams a quarter of its partition and holds
+    the block ids of its range 64 at a time, so quarters of more than 64
+    blocks take several windows (bs 8 / pt 8192: 4 windows per wave; bs 32 /
+    pt 16000: quarters start mid-block). Lengths around one and two
+    partitions, plus the library's default."""
+    lens = [pt, pt - 1, pt + 1, 2 * pt, 17, 1, 0]
+    wl = small(lens, Hq=8, Hkv=2, D=128, bs=bs, dtype="bf16", seed=21)
+    gpu, ora = build_both(wl)
+    ref = oracle_out(wl, ora)
+    for p in (pt, 0):
+        got = widen_out(gpu.decode(p, gpu.workspace_for(p)), "bf16")
+        assert_close(got, ref, "bf16", f"bs={bs} pt={p} lens={lens}")
+    gpu.close()
 
 
 def test_decode_partition_invariance_and_max_seq_len_slack():
