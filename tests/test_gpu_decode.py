@@ -255,6 +255,23 @@ def test_decode_long_partitions(bs, pt):
     gpu.close()
 
 
+@pytest.mark.parametrize("B,pt", [(300, 64), (300, 0), (1100, 128), (1100, 0)])
+def test_decode_large_batches(B, pt):
+    """Batches past the sizes where the work list is compact (up to 1024
+    sequences) and where one-partition batches are ordered: 300 sequences
+    (compact list, several partitions each at pt 64) and 1100 (the plain
+    (kv head, sequence, partition) mapping). Ragged short lengths, empty ones
+    included."""
+    rng = np.random.default_rng(B + pt)
+    lens = rng.integers(0, 300, B).tolist()
+    lens[0], lens[-1] = 0, 299
+    wl = small(lens, Hq=8, Hkv=2, D=64, bs=16, dtype="bf16", seed=31)
+    gpu, ora = build_both(wl)
+    got = widen_out(gpu.decode(pt, gpu.workspace_for(pt)), "bf16")
+    assert_close(got, oracle_out(wl, ora), "bf16", f"B={B} pt={pt}")
+    gpu.close()
+
+
 def test_decode_partition_invariance_and_max_seq_len_slack():
     from paged_kv_cache_indirect_amd import pa_decode
     wl = small([1, 40, 511, 512, 513, 1500], Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", seed=9)
