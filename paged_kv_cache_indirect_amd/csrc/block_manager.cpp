@@ -4,7 +4,6 @@
 #include <algorithm>
 #include <climits>
 #include <cstddef>
-#include <unordered_set>
 
 namespace pa {
 
@@ -70,9 +69,20 @@ Status BlockManager::Append(int64_t seq, int32_t n, int64_t* slots_out, std::str
   }
   // Everything that can throw happens before the first mutation.
   if (cow) pending_.reserve(pending_.size() + 1);
-  if (it == seqs_.end()) it = seqs_.emplace(seq, Seq{}).first;
+  if (it == seqs_.end()) it = seqs_.try_emplace(seq).first;
   Seq& s = it->second;
   s.table.reserve(static_cast<size_t>(have + tail));
+  Grow(s, n, slots_out);
+  return kOk;
+}
+
+void BlockManager::Grow(Seq& s, int32_t n, int64_t* slots_out) {
+  const int64_t old_len = s.len;
+  const int64_t new_len = old_len + n;
+  const int64_t have = static_cast<int64_t>(s.table.size());
+  const bool cow = n > 0 && have > 0 && old_len % block_size_ != 0 &&
+                   ref_[static_cast<size_t>(s.table.back())] > 1;
+  const int64_t tail = CeilDiv(new_len, block_size_) - have;
   if (n > 0) {  // token ids unknown from here on: no prefix keys for this sequence
     s.keyed = false;
     s.tail_tokens.clear();
@@ -94,7 +104,6 @@ Status BlockManager::Append(int64_t seq, int32_t n, int64_t* slots_out, std::str
   const int64_t bs = block_size_;
   for (int64_t p = old_len; p < new_len; ++p)
     slots_out[p - old_len] = static_cast<int64_t>(s.table[static_cast<size_t>(p / bs)]) * bs + p % bs;
-  return kOk;
 }
 
 Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_tokens,
@@ -109,16 +118,19 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
     return kErrInvalid;
   }
   // Validate the whole batch and count its new blocks before any mutation.
-  std::unordered_set<int64_t> seen;
-  seen.reserve(static_cast<size_t>(n));
+  scratch_ids_.assign(seqs, seqs + n);
+  std::sort(scratch_ids_.begin(), scratch_ids_.end());
+  const auto dup = std::adjacent_find(scratch_ids_.begin(), scratch_ids_.end());
+  if (dup != scratch_ids_.end()) {
+    *err = "sequence " + std::to_string(*dup) + " appears twice in the batch";
+    return kErrInvalid;
+  }
   std::unordered_map<int32_t, int32_t> cow_drops;  // references dropped by copies earlier in the batch
   int64_t need = 0;
+  scratch_grow_.resize(static_cast<size_t>(n));
   for (int32_t i = 0; i < n; ++i) {
-    if (!seen.insert(seqs[i]).second) {
-      *err = "sequence " + std::to_string(seqs[i]) + " appears twice in the batch";
-      return kErrInvalid;
-    }
     auto it = seqs_.find(seqs[i]);
+    scratch_grow_[static_cast<size_t>(i)] = it == seqs_.end() ? nullptr : &it->second;
     const int64_t old_len = it == seqs_.end() ? 0 : it->second.len;
     const int64_t have = it == seqs_.end() ? 0 : static_cast<int64_t>(it->second.table.size());
     if (old_len + n_tokens > static_cast<int64_t>(INT32_MAX)) {
@@ -128,7 +140,8 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
     need += CeilDiv(old_len + n_tokens, block_size_) - have;
     // A copy-on-write of a shared partial last block needs one more block;
     // an earlier copy in the same batch may have left it with one user.
-    if (n_tokens > 0 && have > 0 && old_len % block_size_ != 0) {
+    if (n_tokens > 0 && have > 0 && old_len % block_size_ != 0 &&
+        ref_[static_cast<size_t>(it->second.table.back())] > 1) {
       const int32_t last = it->second.table.back();
       int32_t& dropped = cow_drops[last];
       if (ref_[static_cast<size_t>(last)] - dropped > 1) {
@@ -145,12 +158,19 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
   // New sequences are created before any block moves, so an allocation
   // failure here leaves the pool unchanged apart from empty entries, which
   // are removed again.
+  // (Pointers to map entries stay valid while other entries are inserted.)
   std::vector<int64_t> created;
+  created.reserve(static_cast<size_t>(n));  // so recording a new entry cannot throw
   try {
-    for (int32_t i = 0; i < n; ++i)
-      if (seqs_.emplace(seqs[i], Seq{}).second) created.push_back(seqs[i]);
     for (int32_t i = 0; i < n; ++i) {
-      Seq& s = seqs_.find(seqs[i])->second;
+      Seq*& ps = scratch_grow_[static_cast<size_t>(i)];
+      if (!ps) {
+        ps = &seqs_.try_emplace(seqs[i]).first->second;
+        created.push_back(seqs[i]);
+      }
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      Seq& s = *scratch_grow_[static_cast<size_t>(i)];
       s.table.reserve(static_cast<size_t>(CeilDiv(s.len + n_tokens, block_size_)));
     }
     pending_.reserve(pending_.size() + static_cast<size_t>(n));
@@ -158,11 +178,9 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
     for (int64_t id : created) seqs_.erase(id);
     throw;
   }
-  for (int32_t i = 0; i < n; ++i) {
-    std::string unused;
-    Append(seqs[i], n_tokens, slots_out ? slots_out + static_cast<int64_t>(i) * n_tokens : nullptr,
-           &unused);  // cannot fail: validated and reserved above
-  }
+  for (int32_t i = 0; i < n; ++i)  // cannot fail: validated and reserved above
+    Grow(*scratch_grow_[static_cast<size_t>(i)], n_tokens,
+         slots_out ? slots_out + static_cast<int64_t>(i) * n_tokens : nullptr);
   return kOk;
 }
 
@@ -212,6 +230,7 @@ Status BlockManager::ExportTables(const int64_t* seqs, int32_t n, int32_t max_bl
     *err = "null pointer argument";
     return kErrInvalid;
   }
+  scratch_seqs_.resize(static_cast<size_t>(n));
   for (int32_t i = 0; i < n; ++i) {  // validate all before writing anything
     auto it = seqs_.find(seqs[i]);
     if (it == seqs_.end()) {
@@ -222,12 +241,13 @@ Status BlockManager::ExportTables(const int64_t* seqs, int32_t n, int32_t max_bl
       *err = "sequence " + std::to_string(seqs[i]) + " needs more than max_blocks table entries";
       return kErrInvalid;
     }
+    scratch_seqs_[static_cast<size_t>(i)] = &it->second;
   }
   for (int32_t i = 0; i < n; ++i) {
-    const Seq& s = seqs_.find(seqs[i])->second;
+    const Seq& s = *scratch_seqs_[static_cast<size_t>(i)];
     int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
-    std::fill(row, row + max_blocks, -1);
     std::copy(s.table.begin(), s.table.end(), row);
+    std::fill(row + s.table.size(), row + max_blocks, -1);
     lens[i] = static_cast<int32_t>(s.len);
   }
   return kOk;

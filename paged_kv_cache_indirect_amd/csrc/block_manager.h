@@ -123,6 +123,10 @@ class BlockManager {
   static uint64_t ChainKey(uint64_t parent, const int32_t* ids, int32_t n);
   // Pops the top of the free list and drops any key the block held.
   int32_t PopFree();
+  // Grows s by n tokens (copy-on-write of a shared partly filled last block,
+  // new blocks from the free list) and writes their slots. The caller has
+  // checked that enough blocks are free and reserved s.table and pending_.
+  void Grow(Seq& s, int32_t n, int64_t* slots_out);
   // Takes a given (cached) block off the free list.
   void TakeFree(int32_t blk);
   int32_t num_blocks_;
@@ -134,6 +138,11 @@ class BlockManager {
   std::unordered_map<uint64_t, CacheEntry> cache_;  // key -> registered block
   std::vector<uint64_t> block_key_;                 // key a block is registered under
   std::vector<char> block_keyed_;
+  // Scratch reused by AppendBatch and ExportTables so that a steady serving
+  // loop makes no heap allocation in them.
+  std::vector<int64_t> scratch_ids_;
+  std::vector<Seq*> scratch_grow_;
+  mutable std::vector<const Seq*> scratch_seqs_;
   PrefixStats pstats_;
 };
 
