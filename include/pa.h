@@ -248,16 +248,21 @@ pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value,
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_seq_len, int32_t partition_tokens);
 
-/* The KV partition pa_decode uses for partition_tokens = 0: one partition
- * per sequence up to 8192 tokens, split further only while the launch has
- * fewer than 512 (sequence, kv head, partition) work items, never below 512
- * tokens, rounded up to a multiple of 64. Fewest, longest partitions ran
- * fastest on MI355X (no log-sum-exp pass when one partition covers every
- * sequence); the 8192 cap keeps one long sequence in a batch of short ones
- * from being left to a few workgroups. (The split into partitions merged by
- * log-sum-exp is this library's; the pages' decode walks a sequence's
- * blocks in one pass: "vLLM的'内存分页'到底多神奇", xxqk.cn, §3 phase 2.)
- * Returns 0 for a null pool or negative sizes. */
+/* The KV partition pa_decode uses for partition_tokens = 0, chosen from the
+ * launch shape (the host does not see the lengths). Work items are
+ * (sequence, group of kv heads, partition), with two kv heads per group
+ * when the pool's kv-head count is even. For max_seq_len >= 8192 the
+ * partition is the longest that still gives 256 items at max_seq_len (long
+ * runs per wave stream fastest). Below that, lengths are taken as uniform in
+ * [0, max_seq_len] and the partition is the smallest whose expected item
+ * count is at most 480 (672 for an FP8 pool): shorter partitions even out
+ * the work of sequences of different lengths while every item still finds a
+ * workgroup slot at once on MI355X. It is kept within [640, 8192] tokens
+ * and rounded up to a multiple of 64. A batch that mixes very long and short
+ * sequences runs faster with a caller-chosen partition. (The split into
+ * partitions merged by log-sum-exp is this library's; the pages' decode
+ * walks a sequence's blocks in one pass: "vLLM的'内存分页'到底多神奇",
+ * xxqk.cn, §3 phase 2.) Returns 0 for a null pool or negative sizes. */
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t B, int32_t max_seq_len);
 
 /* Decode attention: one query token per sequence over its paged cache.

@@ -13,11 +13,17 @@
 //    read-only gather of this access pattern reaches ~5.3 TB/s while the math
 //    of a straightforward kernel costs more than the loads: the design is
 //    about VALU instructions per byte as much as about bytes in flight.
-//  * A workgroup of 4 waves owns one KV partition (partition_tokens tokens)
-//    of one (sequence, kv head); each wave streams a quarter of it, K and V
-//    together in a single pass. Eight lanes cover one D-element row with
-//    16-byte loads (one load instruction fetches 8 whole rows); the loads of
-//    a batch of steps are issued together, then consumed.
+//  * A workgroup of 4 waves owns one KV partition of one sequence for a
+//    group of kv heads: two neighbouring heads when Hkv is even (so the
+//    workgroup reads 512 contiguous bytes of every bf16 slot at D = 128, in
+//    lockstep), else one. Each wave streams its head's share of the
+//    partition (a half, or a quarter for one head), K and V together in a
+//    single pass. A sequence's partitions are equal in length (at most
+//    partition_tokens, rounded up to 64 tokens), so no wave of a short
+//    partition idles beside a full one. Eight lanes cover one D-element row
+//    with 16-byte loads (one load instruction fetches 8 whole rows); the
+//    loads of a batch of steps are issued together, and where registers
+//    allow the next batch is issued before the current one is consumed.
 //  * The block ids of the wave's range are loaded 64 at a time, one per
 //    lane (the next 64 while the current ones stream), and broadcast per
 //    step with v_readlane (an SGPR), so the table lookup is off the per-row
@@ -32,24 +38,24 @@
 //    element with v_perm and contracted with v_dot2_f32_bf16 against the two
 //    weights rounded to bf16 (fp32 accumulate) — half the instructions of
 //    unpack + FMA. fp32 caches use plain FMAs.
-//  * At the end the 8 row groups of a wave merge by DPP/shuffles and the 4
-//    waves through LDS, by log-sum-exp. A sequence that fits in one partition
+//  * At the end the 8 row groups of a wave merge by DPP/shuffles and the
+//    waves of one head through LDS, by log-sum-exp. A sequence that fits in one partition
 //    writes its output directly; otherwise every partition writes its partial
 //    state (max, sum, Σ w·V) and a second, small kernel merges them by
 //    log-sum-exp, one wave per (sequence, q head). (Merging inside the first
 //    kernel through an arrival counter needs an agent-scope release/acquire
 //    per partition — an L2 writeback and invalidate per workgroup on this
 //    chip — which measured far slower than one extra launch.)
-//  * Work items are the (kv head, sequence, partition) triples that exist:
+//  * Work items are the (kv-head group, sequence, partition) triples that exist:
 //    each workgroup prefix-sums the sequences' partition counts (batches up
 //    to 1024) and takes its item from that compact list, so partitions past a
 //    sequence's end do not occupy workgroup slots between real ones (the
 //    grid is sized for every sequence at max_seq_len; its surplus comes last
 //    and exits). Measured on MI355X, interleaved empty workgroups slowed a
-//    launch by up to 2.4x. Items are mapped XCD-major with the kv head
+//    launch by up to 2.4x. Items are mapped XCD-major with the head group
 //    outermost: consecutive hardware workgroup ids go to different XCDs, so
-//    each XCD owns a contiguous range (one kv head when Hkv = 8) and a shared
-//    prefix block of that head is re-read from one XCD's L2.
+//    each XCD owns a contiguous range (half a head group when Hkv = 8) and a
+//    shared prefix block of those heads is re-read from few XCDs' L2.
 #include "device_common.h"
 #include "launch.h"
 
@@ -57,7 +63,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;                 // waves per workgroup (one partition)
+constexpr int kWaves = 4;                 // waves per workgroup (one partition of 1, 2 or 4 kv heads)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCompactBatch = 1024;  // batches up to this size get a compact work list
 constexpr int kLanesPerRow = 8;
@@ -83,6 +89,23 @@ struct RowGeom {
   // bytes in flight, so 3 waves per SIMD beat deeper batches at 2 waves.
   static constexpr int kStepsInFlight = kChunksPerLane == 1 ? 4 : 2;
   static_assert(kChunks % kLanesPerRow == 0, "row must split into 8 lanes of 16-byte chunks");
+};
+
+// Whether the main loop double-buffers its loads (batch n + 1 in flight while
+// batch n is consumed). It costs one more batch of registers, so it is used
+// where accumulators, q fragments and two load buffers fit in 192 VGPRs and
+// the kernel still runs 2 waves per SIMD without spilling.
+template <typename T, typename KV, int D, int G>
+struct Pipelined {
+  using RG = RowGeom<KV, D>;
+  static constexpr int kQOut = sizeof(KV) == 1 ? 2 : 1;
+  static constexpr int kAcc = G * RG::kElemPerLane;
+  static constexpr int kQ = G * RG::kChunksPerLane * kQOut * 4;
+  static constexpr int kBuf = RG::kStepsInFlight * RG::kChunksPerLane * 2 * 4;
+  static constexpr bool value = kAcc + kQ + 2 * kBuf <= 192;
+  // Waves per SIMD the register budget is set for: 3 (168 VGPRs) where one
+  // buffer set fits comfortably, else 2 (256 VGPRs).
+  static constexpr int kMinWaves = !value && kAcc + kQ + kBuf <= 128 ? 3 : 2;
 };
 
 template <typename T>
@@ -174,13 +197,13 @@ __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
 // (T itself, or Fp8E4M3 with bf16 T). v_scale multiplies the output (the
 // FP8 value scale; 1 otherwise); the key scale is folded into scale_log2.
 template <typename T, typename KV, int D, int G>
-__global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
+__global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void DecodeKernel(
     T* __restrict__ out, const T* __restrict__ q, const KV* __restrict__ kc,
     const KV* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ seq_lens, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int32_t B, int32_t Hkv,
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
-    int32_t P, int32_t per_xcd, float scale_log2, float v_scale) {
+    int32_t P, int32_t per_xcd, float scale_log2, float v_scale, int32_t hsh) {
   using RG = RowGeom<KV, D>;
   using WD = Widen<KV>;
   constexpr int CPL = RG::kChunksPerLane;
@@ -200,9 +223,10 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
   const int r = lane >> 3;  // row within a step
   const int j = lane & 7;   // lane within the row
 
-  // ---- work item (XCD-major; kv head, then sequence, then partition)
+  // ---- work item (XCD-major; kv-head group, then sequence, then partition)
   const int wg = blockIdx.x;
-  int p, b, g;
+  int p, b, gq;  // gq: group of (1 << hsh) kv heads
+  const int NG = Hkv >> hsh;
   if (B <= kCompactBatch) {
     // Compact work list: only the (kv head, sequence, partition) items that
     // exist, kv head outermost, XCD-major over the real count; the grid's
@@ -240,12 +264,12 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
     if (tid == kThreads - 1) s_pref[kCompactBatch] = run;
     __syncthreads();
     const int S = s_pref[kCompactBatch];  // items per kv head
-    const int per_xcd_real = (Hkv * S + 7) / 8;
+    const int per_xcd_real = (NG * S + 7) / 8;
     if ((wg >> 3) >= per_xcd_real) return;
     const int item = (wg & 7) * per_xcd_real + (wg >> 3);
-    if (item >= Hkv * S) return;
-    g = item / S;
-    const int k = item - g * S;
+    if (item >= NG * S) return;
+    gq = item / S;
+    const int k = item - gq * S;
     int lo = 0, hi = B - 1;  // largest b with s_pref[b] <= k
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -255,12 +279,16 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
     p = k - s_pref[b];
   } else {
     const int item = (wg & 7) * per_xcd + (wg >> 3);
-    if (item >= Hkv * B * P) return;
+    if (item >= NG * B * P) return;
     p = item % P;
     const int bg = item / P;
     b = bg % B;
-    g = bg / B;
+    gq = bg / B;
   }
+  const int WS = 2 - hsh;  // log2(waves per kv head)
+  const int hh = w >> WS;  // kv head within the workgroup
+  const int g = (gq << hsh) + hh;
+  const int wq = w & ((1 << WS) - 1);
   const int Hq = Hkv * G;
 
   int L = seq_lens[b];
@@ -268,8 +296,9 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
   const int Pb = max(1, (L + PT - 1) / PT);  // partitions of this sequence
   if (p >= Pb) return;
 
-  const int TPW = PT / kWaves;               // tokens per wave (a multiple of 16)
-  const int w0 = p * PT + w * TPW;
+  const int PTb = ((L + Pb - 1) / Pb + 63) & ~63;  // equal split, multiple of 64 (<= PT)
+  const int TPW = PTb >> WS;
+  const int w0 = p * PTb + wq * TPW;
   const int ntok = max(0, min(w0 + TPW, L) - w0);
   const int nsteps = (ntok + kRowsPerStep - 1) / kRowsPerStep;
 
@@ -299,8 +328,9 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
   // A wave with no tokens has no blocks (its start may lie past the table's
   // last entry when it falls inside a block).
   const int lb_end = ntok > 0 ? (w0 + ntok + bs - 1) >> bs_shift : lb0;
-  int my_blk = 0;
-  if (lb0 + lane < lb_end) my_blk = clamp_block(trow[lb0 + lane], num_blocks);
+  int cur_blk = 0, nxt_blk = 0;  // ids of the current window and of the next one
+  if (lb0 + lane < lb_end) cur_blk = clamp_block(trow[lb0 + lane], num_blocks);
+  if (lb_end > lb0) nxt_blk = trow[min(lb0 + kWinBlocks + lane, lb_end - 1)];
   int lbw = lb0;  // first block of the current window
 
   const int64_t row_stride = static_cast<int64_t>(Hkv) * D;  // elements between slots
@@ -316,24 +346,30 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  uint4 kb[U][CPL];
-  uint4 vb[U][CPL];
-  auto issue = [&](int st, int u) {
+  // Loads of one step (8 rows) into one buffer slot. Steps are issued in
+  // increasing order, so the window of block ids only ever moves forward, by
+  // at most one window per step.
+  auto issue = [&](int st, uint4 (&kx)[CPL], uint4 (&vx)[CPL]) {
     const int tok = w0 + st * kRowsPerStep;
     const int lb = tok >> bs_shift;
-    const int blk = __builtin_amdgcn_readlane(my_blk, lb - lbw);
+    if (lb - lbw >= kWinBlocks) {
+      lbw += kWinBlocks;
+      cur_blk = clamp_block(nxt_blk, num_blocks);
+      nxt_blk = trow[min(lbw + kWinBlocks + lane, lb_end - 1)];
+    }
+    const int blk = __builtin_amdgcn_readlane(cur_blk, lb - lbw);
     const int64_t slot0 = (static_cast<int64_t>(blk) << bs_shift) + (tok & (bs - 1));
     const KV* krow = kbase + slot0 * row_stride;
     const KV* vrow = vbase + slot0 * row_stride;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      kb[u][i] = *reinterpret_cast<const uint4*>(krow + (j + kLanesPerRow * i) * EPC);
-      vb[u][i] = *reinterpret_cast<const uint4*>(vrow + (j + kLanesPerRow * i) * EPC);
+      kx[i] = *reinterpret_cast<const uint4*>(krow + (j + kLanesPerRow * i) * EPC);
+      vx[i] = *reinterpret_cast<const uint4*>(vrow + (j + kLanesPerRow * i) * EPC);
     }
   };
 
   // Two consecutive steps (rows t and t + 8 for this lane) at a time.
-  auto consume_pair = [&](int st, int u) {
+  auto consume_pair = [&](int st, uint4 (&kb)[U][CPL], uint4 (&vb)[U][CPL], int u) {
     float x0[G], x1[G];  // scores in log2 units
     uint4 k0[CPL][QPC], k1[CPL][QPC];
 #pragma unroll
@@ -404,25 +440,43 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
     }
   };
 
-  // Per window, batches of U steps: all U steps' loads are issued (a step
-  // past the window's end re-reads its last one, a cache hit, so the count of
-  // loads in flight is the same on every path), then consumed in pairs.
-  for (; lbw < lb_end; lbw += kWinBlocks) {
-    const int st_begin = max(0, (lbw << bs_shift) - w0) / kRowsPerStep;
-    const int st_end = min(nsteps, (((lbw + kWinBlocks) << bs_shift) - w0) / kRowsPerStep);
-    // Next window's ids (clamped index: a valid entry on every lane).
-    const int next_blk = trow[min(lbw + kWinBlocks + lane, lb_end - 1)];
-    for (int st0 = st_begin; st0 < st_end; st0 += U) {
+  // Batches of U steps. A step past the wave's end re-reads its last step (a
+  // cache hit), so every path issues the same number of loads and the
+  // compiler's wait counts stay exact. Pipelined: the loads of batch n + 1
+  // are issued before batch n is consumed, so the wave keeps a batch in
+  // flight while it computes; otherwise each batch is loaded, then consumed.
+  if (nsteps > 0) {
+    auto issue_batch = [&](int st0, uint4 (&kx)[U][CPL], uint4 (&vx)[U][CPL]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) issue(min(st0 + u, st_end - 1), u);
-      // Keep all U steps' loads ahead of the math (the scheduler would sink
-      // each load next to its first use, exposing memory latency per step).
-      __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < U; ++u) issue(min(st0 + u, nsteps - 1), kx[u], vx[u]);
+    };
+    auto consume_batch = [&](int st0, uint4 (&kx)[U][CPL], uint4 (&vx)[U][CPL]) {
 #pragma unroll
       for (int u = 0; u < U; u += 2)
-        if (st0 + u < st_end) consume_pair(st0 + u, u);
+        if (st0 + u < nsteps) consume_pair(st0 + u, kx, vx, u);
+    };
+    uint4 kA[U][CPL], vA[U][CPL];
+    if constexpr (Pipelined<T, KV, D, G>::value) {
+      uint4 kB[U][CPL], vB[U][CPL];
+      const int nbat = (nsteps + U - 1) / U;
+      issue_batch(0, kA, vA);
+      for (int n = 0; n < nbat; n += 2) {
+        issue_batch((n + 1) * U, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        consume_batch(n * U, kA, vA);
+        issue_batch((n + 2) * U, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        if (n + 1 < nbat) consume_batch((n + 1) * U, kB, vB);
+      }
+    } else {
+      for (int st0 = 0; st0 < nsteps; st0 += U) {
+        issue_batch(st0, kA, vA);
+        // Keep all U steps' loads ahead of the math (the scheduler would
+        // sink each load next to its first use, exposing memory latency).
+        __builtin_amdgcn_sched_barrier(0);
+        consume_batch(st0, kA, vA);
+      }
     }
-    my_blk = clamp_block(next_blk, num_blocks);
   }
 
   // ---- merge the 8 row groups of the wave (lanes that differ in bits 3..5)
@@ -457,24 +511,25 @@ __global__ __launch_bounds__(kThreads, 3) void DecodeKernel(
   __syncthreads();
 
   // ---- merge the 4 waves; write the output, or this partition's partial state
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int h = idx / D;
-    const int d = idx - h * D;
+  for (int idx = tid; idx < (G * D << hsh); idx += kThreads) {
+    const int hw = idx / (G * D);       // kv head within the workgroup
+    const int h = (idx / D) % G;
+    const int d = idx % D;
+    const int wlo = hw << WS, whi = (hw + 1) << WS;
+    const int qh = ((gq << hsh) + hw) * G + h;  // q head
     float M = kMaxInit;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_ml[ww][h][0]);
+    for (int ww = wlo; ww < whi; ++ww) M = fmaxf(M, s_ml[ww][h][0]);
     float a = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = wlo; ww < whi; ++ww) {
       const float f = fast_exp2(s_ml[ww][h][0] - M);
       a = fmaf(f, s_acc[ww][h][d], a);
       lsum = fmaf(f, s_ml[ww][h][1], lsum);
     }
     a *= v_scale;
     if (Pb == 1) {
-      out[(static_cast<int64_t>(b) * Hq + g * G + h) * D + d] = from_f32<T>(lsum > 0.f ? a / lsum : 0.f);
+      out[(static_cast<int64_t>(b) * Hq + qh) * D + d] = from_f32<T>(lsum > 0.f ? a / lsum : 0.f);
     } else {
-      const int64_t row = (static_cast<int64_t>(b) * Hq + g * G + h) * P + p;  // (b, q head, p)
+      const int64_t row = (static_cast<int64_t>(b) * Hq + qh) * P + p;  // (b, q head, p)
       ws_acc[row * D + d] = a;
       if (d == 0) {
         ws_ml[row * 2 + 0] = M;
@@ -541,7 +596,8 @@ __global__ __launch_bounds__(64) void MergeKernel(T* __restrict__ out, const flo
 template <typename T, typename KV, int D, int G>
 hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   const int P = a.num_partitions;
-  const int64_t items = static_cast<int64_t>(P) * a.B * a.Hkv;
+  const int hsh = DecodeHeadShift(a.Hkv);
+  const int64_t items = static_cast<int64_t>(P) * a.B * (a.Hkv >> hsh);
   const int per_xcd = static_cast<int>((items + 7) / 8);
   const bool fp8 = sizeof(KV) == 1;
   const float scale_log2 = a.scale * (fp8 ? a.k_scale : 1.f) * 1.4426950408889634f;
@@ -552,7 +608,7 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
                      static_cast<const KV*>(a.k_cache), static_cast<const KV*>(a.v_cache),
                      a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
                      __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
-                     P, per_xcd, scale_log2, v_scale);
+                     P, per_xcd, scale_log2, v_scale, hsh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
   hipLaunchKernelGGL((MergeKernel<T, D>), dim3(a.B * a.Hq), dim3(64), 0, stream,

@@ -74,26 +74,53 @@ inline int64_t PrefillWorkItems(int32_t Hkv, int32_t G, int32_t B, int32_t max_q
 
 // Grid / workspace geometry shared by the API layer and the launchers.
 //
-// The library's decode partition when the caller passes 0. Measured on
-// MI355X, a decode launch runs fastest with the fewest, longest partitions
-// that still give the GPU enough workgroups (no log-sum-exp pass when one
-// partition covers every sequence), as long as no single sequence is left
-// to a few workgroups: a batch with one very long sequence among short ones
-// needs that sequence split. So: one partition per sequence up to
-// kDecodeDefaultMaxPartition tokens, split further only while the launch has
-// fewer than kDecodeTargetItems (sequence, kv head, partition) items, never
-// below 512 tokens; rounded up to a multiple of 64.
-constexpr int64_t kDecodeTargetItems = 512;
+// Decode workgroups cover (1 << DecodeHeadShift(Hkv)) kv heads of one
+// partition of one sequence: two neighbouring heads (512 contiguous bytes
+// of every bf16 slot at D = 128) when Hkv is even, measured faster on MI355X
+// than one head (256-byte rows) or four (fewer, longer streams per wave).
+inline int32_t DecodeHeadShift(int32_t Hkv) { return Hkv % 2 == 0 ? 1 : 0; }
+//
+// The library's decode partition when the caller passes 0, from the launch
+// shape alone (the host does not see the lengths). Measured on MI355X:
+//  * Contexts of kDecodeLongContext tokens and more: every wave should
+//    stream a long run of blocks, so the fewest partitions that still give
+//    kDecodeLongItems (sequence, kv-head group, partition) work items,
+//    counted as if every sequence had max_seq_len tokens.
+//  * Shorter contexts: the lengths of a batch differ, and shorter partitions
+//    even out the waves' work, as long as every item still finds a
+//    workgroup slot in the first round (about 512 on 256 CUs; an item left
+//    for a second round costs a whole partition's time). Counting lengths
+//    as uniform in [0, max_seq_len], a sequence has max_seq_len / (2 pt) +
+//    1/2 partitions on average; the partition is the smallest whose
+//    expected item count stays within kDecodeShortItems
+//    (kDecodeShortItemsFp8 for E4M3 pools, whose waves spend more
+//    instructions per byte and gain from more of them).
+// The partition is kept within [kDecodeMinPartition, kDecodeDefaultMaxPartition]
+// and rounded up to a multiple of 64.
+constexpr int32_t kDecodeLongContext = 8192;
+constexpr int64_t kDecodeLongItems = 256;
+constexpr int64_t kDecodeShortItems = 480;
+constexpr int64_t kDecodeShortItemsFp8 = 672;
+constexpr int32_t kDecodeMinPartition = 640;
 constexpr int32_t kDecodeDefaultMaxPartition = 8192;
 constexpr int32_t kDecodeMaxPartition = 1 << 24;
-inline int32_t DecodeDefaultPartition(int32_t B, int32_t Hkv, int32_t max_seq_len) {
+inline int32_t DecodeDefaultPartition(int32_t B, int32_t Hkv, int32_t max_seq_len, bool fp8) {
   const int64_t len = max_seq_len > 1 ? max_seq_len : 1;
-  const int64_t pairs = static_cast<int64_t>(B > 1 ? B : 1) * (Hkv > 1 ? Hkv : 1);
-  const int64_t parts = (kDecodeTargetItems + pairs - 1) / pairs;
-  int64_t pt = (len + parts - 1) / parts;
+  const int64_t groups = Hkv > 1 ? (Hkv >> DecodeHeadShift(Hkv)) : 1;
+  const int64_t pairs = static_cast<int64_t>(B > 1 ? B : 1) * groups;
+  int64_t pt;
+  if (len >= kDecodeLongContext) {
+    const int64_t parts = (kDecodeLongItems + pairs - 1) / pairs;
+    pt = (len + parts - 1) / parts;
+  } else {
+    // smallest pt with pairs * (len / (2 pt) + 1/2) <= target
+    const int64_t target = fp8 ? kDecodeShortItemsFp8 : kDecodeShortItems;
+    const int64_t room = 2 * target - pairs;  // = 2 pairs (target / pairs - 1/2)
+    pt = room > 0 ? (pairs * len + room - 1) / room : len;
+  }
   pt = (pt + 63) / 64 * 64;
   if (pt > kDecodeDefaultMaxPartition) pt = kDecodeDefaultMaxPartition;
-  if (pt < 512) pt = 512;
+  if (pt < kDecodeMinPartition) pt = kDecodeMinPartition;
   return static_cast<int32_t>(pt);
 }
 inline int32_t DecodePartitions(int32_t max_seq_len, int32_t partition_tokens) {

@@ -181,7 +181,8 @@ pa_status PrepareDecode(const pa_pool& pool, void* out, const void* q, const int
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * l.block_size)
     return Fail(PA_ERR_INVALID, "max_seq_len exceeds max_blocks * block_size");
   const int32_t pt =
-      partition_tokens == 0 ? pa::DecodeDefaultPartition(B, l.num_kv_heads, max_seq_len) : partition_tokens;
+      partition_tokens == 0 ? pa::DecodeDefaultPartition(B, l.num_kv_heads, max_seq_len, l.dtype == PA_FP8_E4M3)
+                             : partition_tokens;
   if (pt % 64 || pt > pa::kDecodeMaxPartition)
     return Fail(PA_ERR_UNSUPPORTED, "partition_tokens must be a multiple of 64, at most " +
                                         std::to_string(pa::kDecodeMaxPartition));
@@ -448,7 +449,7 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t B, int32_t max_seq_len) {
   if (!pool || B < 0 || max_seq_len < 0) return 0;
   const pa_kv_layout& l = pool->layout;
-  return pa::DecodeDefaultPartition(B, l.num_kv_heads, max_seq_len);
+  return pa::DecodeDefaultPartition(B, l.num_kv_heads, max_seq_len, l.dtype == PA_FP8_E4M3);
 }
 
 pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* block_tables,

@@ -232,36 +232,52 @@ def test_alloc_pool_rejects_bad_geometry():
     assert make_pool(4, 16, dtype=7)[0] == pa.PA_ERR_UNSUPPORTED
 
 
+def _expected_items(B, L, pt):
+    """Work items the short-context rule expects at partition pt: two kv
+    heads per group (8 kv heads -> 4 groups), lengths uniform in [0, L]."""
+    return max(B, 1) * 4 * (max(L, 1) / (2 * pt) + 0.5)
+
+
 def test_decode_partition_policy():
-    """The library's partition for partition_tokens = 0: one partition per
-    sequence up to 8192 tokens, split further only while the launch has fewer
-    than 512 (sequence, kv head, partition) items, never below 512 tokens,
-    rounded up to a multiple of 64."""
+    """The library's partition for partition_tokens = 0. Work items are
+    (sequence, group of two kv heads, partition). Contexts of 8192 tokens and
+    more: the fewest partitions giving 256 items at max_seq_len. Shorter ones:
+    the smallest partition whose expected item count (lengths uniform in
+    [0, max_seq_len]) is at most 480 (672 for an FP8 pool). Kept within
+    [640, 8192] tokens and rounded up to a multiple of 64."""
     pools = {bs: make_pool(64, bs, hkv=8, d=128)[1] for bs in (8, 16, 32)}
+    fp8_pool = make_pool(64, 16, hkv=8, d=128, dtype=pa.PA_FP8_E4M3)[1]
     f = pa.pa_decode_partition_tokens
     p16 = pools[16]
-    assert f(p16, 64, 4087) == 4096       # 8B-shaped batch: 512 items, one partition per sequence
-    assert f(p16, 64, 4142) == 4160       # ... also past 4096 tokens
-    assert f(p16, 64, 32768) == 8192      # capped: one long sequence is not left to one workgroup per head
-    assert f(p16, 8, 32768) == 4096       # long contexts: 8 partitions -> 512 items
-    assert f(p16, 128, 3068) == 3072
-    assert f(p16, 48, 1591) == 832        # 384 pairs: two partitions
-    assert f(p16, 1, 32768) == 512        # 8 pairs: 64 partitions of 512
-    assert f(p16, 4, 50) == 512 and f(p16, 0, 0) == 512
-    assert f(pools[8], 64, 20000) == 8192 and f(pools[32], 64, 2000) == 2048   # block size plays no part
+    assert f(p16, 64, 4087) == 1536       # 8B-shaped batch: 256 head-group pairs
+    assert f(p16, 64, 4142) == 1536
+    assert f(fp8_pool, 64, 4142) == 1024  # FP8: more items
+    assert f(p16, 56, 4100) == 1280
+    assert f(p16, 64, 32768) == 8192      # long context, capped
+    assert f(p16, 8, 32768) == 4096       # long contexts: 8 partitions -> 256 items
+    assert f(p16, 128, 3068) == 3520      # 512 pairs fill the GPU: one partition
+    assert f(p16, 48, 1591) == 640        # floor
+    assert f(p16, 1, 32768) == 640
+    assert f(p16, 4, 50) == 640 and f(p16, 0, 0) == 640
+    assert f(pools[8], 64, 20000) == 8192 and f(pools[32], 64, 2000) == 768   # block size plays no part
     assert f(None, 4, 100) == 0 and f(p16, -1, 100) == 0
     rng = np.random.default_rng(3)
     for _ in range(300):
         B = int(rng.integers(0, 300))
         L = int(rng.integers(0, 70000))
         pt = f(p16, B, L)
-        assert pt % 64 == 0 and 512 <= pt <= 8192, (B, L, pt)
-        parts = -(-max(L, 1) // pt)
-        # more than one partition only when capped, or when needed for 512 items
-        assert parts == 1 or pt == 8192 or pt == 512 or max(B, 1) * 8 * (parts - 1) < 512, (B, L, pt)
+        assert pt % 64 == 0 and 640 <= pt <= 8192, (B, L, pt)
+        if pt in (640, 8192):
+            continue
+        if L >= 8192:
+            parts = -(-256 // (max(B, 1) * 4))   # partitions for 256 items
+            assert pt == -(-(-(-L // parts)) // 64) * 64, (B, L, pt)
+        elif pt < L:
+            # smallest multiple of 64 within the expected-item target
+            assert _expected_items(B, L, pt) <= 480 + 1e-9 < _expected_items(B, L, pt - 64), (B, L, pt)
         # the 512-token workspace bounds the default's
         assert pa.lib.pa_decode_workspace_bytes(B, 32, 128, L, pt) <= pa.lib.pa_decode_workspace_bytes(B, 32, 128, L, 0)
-    for p in pools.values():
+    for p in list(pools.values()) + [fp8_pool]:
         pa.pa_free_pool(p)
 
 
