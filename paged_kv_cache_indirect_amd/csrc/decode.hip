@@ -226,12 +226,14 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // ---- work item (XCD-major; kv-head group, then sequence, then partition)
   const int wg = blockIdx.x;
   int p, b, gq;  // gq: group of (1 << hsh) kv heads
+  int L;          // the sequence's length, clamped to [0, max_seq_len]
   const int NG = Hkv >> hsh;
   if (B <= kCompactBatch) {
     // Compact work list: only the (kv head, sequence, partition) items that
     // exist, kv head outermost, XCD-major over the real count; the grid's
     // surplus workgroups (sized for B x P) come last and exit.
     __shared__ int s_pref[kCompactBatch + 1];
+    __shared__ int s_len[kCompactBatch];  // clamped lengths
     __shared__ int s_wsum[kWaves];
     constexpr int kPer = kCompactBatch / kThreads;  // sequences per thread
     int cnt[kPer];
@@ -241,6 +243,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       const int bb = tid * kPer + i;
       int Lb = bb < B ? seq_lens[bb] : 0;
       Lb = min(max(Lb, 0), max_seq_len);
+      s_len[bb] = Lb;
       cnt[i] = bb < B ? max(1, (Lb + PT - 1) / PT) : 0;
       tsum += cnt[i];
     }
@@ -277,6 +280,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     }
     b = lo;
     p = k - s_pref[b];
+    L = s_len[b];
   } else {
     const int item = (wg & 7) * per_xcd + (wg >> 3);
     if (item >= NG * B * P) return;
@@ -284,6 +288,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     const int bg = item / P;
     b = bg % B;
     gq = bg / B;
+    L = min(max(seq_lens[b], 0), max_seq_len);
   }
   const int WS = 2 - hsh;  // log2(waves per kv head)
   const int hh = w >> WS;  // kv head within the workgroup
@@ -291,8 +296,6 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   const int wq = w & ((1 << WS) - 1);
   const int Hq = Hkv * G;
 
-  int L = seq_lens[b];
-  L = min(max(L, 0), max_seq_len);
   const int Pb = max(1, (L + PT - 1) / PT);  // partitions of this sequence
   if (p >= Pb) return;
 
@@ -539,50 +542,64 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   }
 }
 
-// Pass 2: log-sum-exp merge of the partitions of each (sequence, q head).
-// One wave; lanes first take the partitions' maxima in parallel, then each
-// lane accumulates D/64 output dims over the partitions with the weights
-// broadcast from the lane that computed them.
+// Pass 2: log-sum-exp merge of the partitions of each (sequence, q head),
+// one wave each, four per workgroup. The partial states are read in chunks
+// of 16 partitions: lane x holds partition x's (max, sum) and every lane
+// its D/64 dims of each partition's Σ w·V, all loaded together once the
+// length is known, so a merge costs two dependent loads. Chunks after the
+// first (more than 16 partitions) rescale the running sums when the maximum
+// grows. Partitions past the sequence's count hold stale data and are
+// excluded by selection (a zero weight would not cancel a NaN).
 template <typename T, int D>
-__global__ __launch_bounds__(64) void MergeKernel(T* __restrict__ out, const float* __restrict__ ws_acc,
-                                                  const float* __restrict__ ws_ml,
-                                                  const int32_t* __restrict__ seq_lens, int32_t Hq,
-                                                  int32_t max_seq_len, int32_t PT, int32_t P) {
+__global__ __launch_bounds__(256) void MergeKernel(T* __restrict__ out, const float* __restrict__ ws_acc,
+                                                   const float* __restrict__ ws_ml,
+                                                   const int32_t* __restrict__ seq_lens, int32_t BH,
+                                                   int32_t Hq, int32_t max_seq_len, int32_t PT, int32_t P) {
   constexpr int EPL = D / 64;
-  const int bh = blockIdx.x;
+  constexpr int kChunk = 16;
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+  if (bh >= BH) return;
   const int b = bh / Hq;
-  const int lane = threadIdx.x;
   int L = seq_lens[b];
   L = min(max(L, 0), max_seq_len);
   const int Pb = (L + PT - 1) / PT;
   if (Pb <= 1) return;  // written by pass 1
   const float* ml = ws_ml + static_cast<int64_t>(bh) * P * 2;
-  const float* acc = ws_acc + static_cast<int64_t>(bh) * P * D;
+  const float* acc = ws_acc + static_cast<int64_t>(bh) * P * D + lane * EPL;
 
-  float M = kMaxInit;
-  for (int x = lane; x < Pb; x += 64) M = fmaxf(M, ml[2 * x]);
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) M = fmaxf(M, __shfl_xor(M, s));
-
+  float M = kMaxInit, lsum = 0.f;
   float a[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) a[e] = 0.f;
-  float lsum = 0.f;
-  for (int x0 = 0; x0 < Pb; x0 += 64) {
-    const int x = x0 + lane;
-    float wgt = 0.f, lx = 0.f;
-    if (x < Pb) {
-      wgt = fast_exp2(ml[2 * x] - M);
-      lx = ml[2 * x + 1];
+  for (int x0 = 0; x0 < Pb; x0 += kChunk) {
+    const int n = min(kChunk, Pb - x0);  // partitions of this chunk
+    float mx = kMaxInit, lx = 0.f;
+    if (lane < n) {
+      mx = ml[2 * (x0 + lane)];
+      lx = ml[2 * (x0 + lane) + 1];
     }
-    lsum += wgt * lx;
-    const int n = min(64, Pb - x0);
-#pragma unroll 8
-    for (int k = 0; k < n; ++k) {
-      const float wk = __shfl(wgt, k);
-      const float* src = acc + static_cast<int64_t>(x0 + k) * D + lane * EPL;
+    float v[kChunk][EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) a[e] = fmaf(wk, src[e], a[e]);
+    for (int k = 0; k < kChunk; ++k)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[k][e] = k < n ? acc[static_cast<int64_t>(x0 + k) * D + e] : 0.f;
+    float Mc = mx;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) Mc = fmaxf(Mc, __shfl_xor(Mc, s));
+    const float Mn = fmaxf(M, Mc);
+    const float f = fast_exp2(M - Mn);
+    lsum *= f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a[e] *= f;
+    M = Mn;
+    const float wgt = lane < n ? fast_exp2(mx - M) : 0.f;
+    lsum = fmaf(wgt, lx, lsum);
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float wk = __shfl(wgt, k);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a[e] = k < n ? fmaf(wk, v[k][e], a[e]) : a[e];
     }
   }
 #pragma unroll
@@ -611,8 +628,9 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
                      P, per_xcd, scale_log2, v_scale, hsh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
-  hipLaunchKernelGGL((MergeKernel<T, D>), dim3(a.B * a.Hq), dim3(64), 0, stream,
-                     static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, a.Hq, a.max_seq_len,
+  const int BH = a.B * a.Hq;
+  hipLaunchKernelGGL((MergeKernel<T, D>), dim3((BH + 3) / 4), dim3(256), 0, stream,
+                     static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, BH, a.Hq, a.max_seq_len,
                      a.partition_tokens, P);
   return hipGetLastError();
 }
