@@ -12,8 +12,8 @@ One step is one decode step of that batch, through the C ABI:
      host-to-device copy of (slots, seq_lens, block_tables);
   3. pa_write_kv scatters the step's new K/V rows into the paged pool;
   4. pa_decode: paged attention of the step's queries, in the library's
-     default KV partitions (pa_decode_partition_tokens: here one partition
-     per sequence, so no log-sum-exp pass).
+     default KV partitions (pa_decode_partition_tokens: here 1536 tokens,
+     1-3 per sequence, merged by log-sum-exp).
 The step's new K/V rows and queries are generated before timing and are
 resident in HBM. W untimed warm-up steps, then K timed steps between two
 device synchronisations.
