@@ -358,8 +358,16 @@ typedef struct {
 } pa_step_desc;
 
 /* Enqueue one mixed step on `stream`: pending copy-on-write copies, the
- * scatter, decode, prefill. Every part is validated before anything is
- * launched. Errors: those of pa_write_kv, pa_decode and pa_prefill. */
+ * scatter, then decode and prefill. When the step has both, the prefill
+ * runs on a stream the pool owns (default priority, made on the first such
+ * call on the device current then), forked from `stream` after the scatter
+ * and joined back before the call's work on `stream` ends, so the
+ * bandwidth-bound decode and the matrix-bound prefill share the GPU; work
+ * enqueued on `stream` afterwards sees both outputs. Steps of one pool
+ * share that stream, so calls for one pool from several host threads must be
+ * serialised, as for every pool call. Every part is validated before
+ * anything is launched. Errors: those of pa_write_kv, pa_decode and
+ * pa_prefill. */
 pa_status pa_step(pa_pool* pool, const pa_step_desc* desc, void* stream);
 
 typedef struct pa_step_graph pa_step_graph; /* opaque, library-owned */
@@ -370,7 +378,9 @@ typedef struct pa_step_graph pa_step_graph; /* opaque, library-owned */
  * caller updates their contents (new rows, slots, tables, lengths, queries,
  * cu_q_lens) between launches. Decode rows with length 0 give zero output and
  * slots of -1 skip their rows, so a frozen batch can carry idle entries.
- * The pool must have no pending copy-on-write copies at capture. The graph
+ * A step with both decode and prefill is captured as two branches joined at
+ * the end, as pa_step runs them. The pool must have no pending copy-on-write
+ * copies at capture. The graph
  * refers to the pool and to the caller's buffers: destroy it before freeing
  * them. Nothing is launched by this call. Errors: those of pa_step;
  * PA_ERR_INVALID when copies are pending; PA_ERR_HIP (capture or
