@@ -295,6 +295,31 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
                     float scale, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* One decode step with the append fused in: the effect of pa_write_kv with
+ * T = B followed by pa_decode, in one launch (plus the log-sum-exp pass).
+ * The pages place a generated token's K/V in its page, then attend over the
+ * sequence's pages ("vLLM的'内存分页'到底多神奇", xxqk.cn, §3 phases 1-2).
+ * For each b with slot_mapping[b] >= 0, row b of key/value ([B, Hkv, D],
+ * the pool dtype, device) is sequence b's newest token: it sits at position
+ * seq_lens[b] - 1, and slot_mapping[b] is its slot (as pa_seq_append_batch
+ * with n_tokens = 1 returns it). The row is written into the pool, and the
+ * block_tables entry of the block that holds it (index (seq_lens[b] - 1) /
+ * block_size of row b) is set to slot_mapping[b] / block_size, so the caller
+ * need not upload tables when a step opens a new block or takes a
+ * copy-on-write block; every other entry must already match the pool's
+ * table (pa_block_tables). slot_mapping[b] < 0: no new token for b (the
+ * decode reads the pool as pa_decode does). Pending copy-on-write copies run
+ * first, as in pa_write_kv. The other arguments and the output are those of
+ * pa_decode. block_tables is read and written on the device; nothing else
+ * is written. bf16 and fp32 pools only. Errors: those of pa_decode;
+ * PA_ERR_INVALID (null or unaligned key/value/slot_mapping with B > 0);
+ * PA_ERR_UNSUPPORTED (FP8 pool). */
+pa_status pa_append_decode(pa_pool* pool, void* out, const void* q, const void* key, const void* value,
+                           const int64_t* slot_mapping, int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t B, int32_t num_q_heads, float scale,
+                           int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Chunked causal prefill (a long prompt processed in chunks: "LLM推理优化：技术
  * 原理解析总览", §2.3; prefill and decode mixed in one step: "vLLM 生产级落地
  * 深剖", musen-ai.com, §2). The chunk's own K/V must already be in the cache

@@ -26,7 +26,7 @@ __all__ = [
     "pa_block_tables", "pa_pool_stats", "pa_pool_pending_copies", "pa_pool_set_kv_scales", "pa_write_kv",
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error", "StepDesc", "pa_step",
     "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy", "pa_seq_append_tokens",
-    "pa_pool_prefix_stats", "pa_tier_block_size", "pa_decode_partition_tokens",
+    "pa_pool_prefix_stats", "pa_tier_block_size", "pa_decode_partition_tokens", "pa_append_decode",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
@@ -95,6 +95,8 @@ _SIGS = {
     "pa_decode_partition_tokens": (_i32, [_vp, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp]),
+    "pa_append_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp,
+                                _sz, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -276,6 +278,25 @@ def pa_decode(pool: int, out, q, block_tables, seq_lens, scale: float, max_seq_l
                          _dptr(seq_lens), B, Hq, float(scale), int(max_seq_len), int(partition_tokens),
                          _dptr(workspace), ws_bytes, _stream(stream)),
            "pa_decode")
+
+
+def pa_append_decode(pool: int, out, q, key, value, slot_mapping, block_tables, seq_lens, scale: float,
+                     max_seq_len: int, partition_tokens: int = 0, workspace=None, stream=None) -> None:
+    """pa_write_kv of one new row per sequence, then pa_decode, in one launch.
+    key/value: device [B, Hkv, D]; slot_mapping: device int64 [B] (slot of
+    sequence b's newest token, or < 0); block_tables: device int32
+    [B, max_blocks], whose entry for each new token's block is filled in."""
+    B, Hq, D = (int(x) for x in q.shape)
+    need = pa_decode_workspace_bytes(B, Hq, D, max_seq_len, partition_tokens)
+    if need and workspace is None:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_append_decode(pool, _dptr(out), _dptr(q), _dptr(key), _dptr(value), _dptr(slot_mapping),
+                                _dptr(block_tables), int(block_tables.shape[1]), _dptr(seq_lens), B, Hq,
+                                float(scale), int(max_seq_len), int(partition_tokens), _dptr(workspace), ws_bytes,
+                                _stream(stream)),
+           "pa_append_decode")
 
 
 def pa_prefill(pool: int, out, q, cu_q_lens, block_tables, seq_lens, scale: float, max_q_len: int,

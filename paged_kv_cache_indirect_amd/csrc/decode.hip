@@ -199,11 +199,13 @@ __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
 template <typename T, typename KV, int D, int G>
 __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void DecodeKernel(
     T* __restrict__ out, const T* __restrict__ q, const KV* __restrict__ kc,
-    const KV* __restrict__ vc, const int32_t* __restrict__ tables,
+    const KV* __restrict__ vc, const int32_t* tables,
     const int32_t* __restrict__ seq_lens, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int32_t B, int32_t Hkv,
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
-    int32_t P, int32_t per_xcd, float scale_log2, float v_scale, int32_t hsh) {
+    int32_t P, int32_t per_xcd, float scale_log2, float v_scale, int32_t hsh,
+    const T* __restrict__ knew, const T* __restrict__ vnew, const int64_t* __restrict__ new_slots,
+    int32_t* tables_out) {
   using RG = RowGeom<KV, D>;
   using WD = Widen<KV>;
   constexpr int CPL = RG::kChunksPerLane;
@@ -299,6 +301,39 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   const int Pb = max(1, (L + PT - 1) / PT);  // partitions of this sequence
   if (p >= Pb) return;
 
+  // Fused append (new_slots given): row b of knew / vnew is sequence b's
+  // newest token, at position L - 1, bound for slot new_slots[b] (< 0, or
+  // outside the pool: no new token). The slot also names the block that
+  // holds it, so that block's table entry is taken from the slot rather than
+  // from the table (a new block, or a copy-on-write block, is not in the
+  // table yet). The workgroup of the last partition writes its kv heads'
+  // part of the row into the pool, and head group 0's also fills in the
+  // table entry for later calls; every wave reads the new token from
+  // knew / vnew, never from the pool.
+  int64_t nslot = -1;
+  if (new_slots != nullptr && L > 0) nslot = new_slots[b];
+  // A slot outside the pool is skipped, as pa_write_kv skips it.
+  const bool has_new = nslot >= 0 && nslot < (static_cast<int64_t>(num_blocks) << bs_shift);  // wave-uniform
+  const int new_tok = has_new ? L - 1 : -1;
+  const int new_lb = has_new ? (L - 1) >> bs_shift : -1;
+  const int new_blk = static_cast<int>(nslot >> bs_shift);
+  const int64_t row_stride = static_cast<int64_t>(Hkv) * D;  // elements between slots
+  if (has_new && p == Pb - 1) {
+    constexpr int kChunkElems = 16 / static_cast<int>(sizeof(KV));
+    constexpr int kHeadChunks = D / kChunkElems;  // 16-byte chunks of one head's row
+    const int heads = 1 << hsh;
+    for (int c = tid; c < 2 * heads * kHeadChunks; c += kThreads) {
+      const int kv = c / (heads * kHeadChunks);
+      const int hc = c - kv * heads * kHeadChunks;
+      const int gh = (gq << hsh) + hc / kHeadChunks;
+      const int e = (hc % kHeadChunks) * kChunkElems;
+      const KV* src = reinterpret_cast<const KV*>(kv ? vnew : knew) + (static_cast<int64_t>(b) * Hkv + gh) * D + e;
+      KV* dst = const_cast<KV*>(kv ? vc : kc) + nslot * row_stride + static_cast<int64_t>(gh) * D + e;
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    }
+    if (gq == 0 && tid == 0) tables_out[static_cast<int64_t>(b) * max_blocks + new_lb] = new_blk;
+  }
+
   const int PTb = ((L + Pb - 1) / Pb + 63) & ~63;  // equal split, multiple of 64 (<= PT)
   const int TPW = PTb >> WS;
   const int w0 = p * PTb + wq * TPW;
@@ -331,12 +366,13 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // A wave with no tokens has no blocks (its start may lie past the table's
   // last entry when it falls inside a block).
   const int lb_end = ntok > 0 ? (w0 + ntok + bs - 1) >> bs_shift : lb0;
+  // Table entry idx, or the fused append's block for the new token's entry.
+  auto table_at = [&](int idx) { return idx == new_lb ? new_blk : trow[idx]; };
   int cur_blk = 0, nxt_blk = 0;  // ids of the current window and of the next one
-  if (lb0 + lane < lb_end) cur_blk = clamp_block(trow[lb0 + lane], num_blocks);
-  if (lb_end > lb0) nxt_blk = trow[min(lb0 + kWinBlocks + lane, lb_end - 1)];
+  if (lb0 + lane < lb_end) cur_blk = clamp_block(table_at(lb0 + lane), num_blocks);
+  if (lb_end > lb0) nxt_blk = table_at(min(lb0 + kWinBlocks + lane, lb_end - 1));
   int lbw = lb0;  // first block of the current window
 
-  const int64_t row_stride = static_cast<int64_t>(Hkv) * D;  // elements between slots
   const KV* kbase = kc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
   const KV* vbase = vc + static_cast<int64_t>(g) * D + static_cast<int64_t>(r) * row_stride;
 
@@ -358,12 +394,18 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     if (lb - lbw >= kWinBlocks) {
       lbw += kWinBlocks;
       cur_blk = clamp_block(nxt_blk, num_blocks);
-      nxt_blk = trow[min(lbw + kWinBlocks + lane, lb_end - 1)];
+      nxt_blk = table_at(min(lbw + kWinBlocks + lane, lb_end - 1));
     }
     const int blk = __builtin_amdgcn_readlane(cur_blk, lb - lbw);
     const int64_t slot0 = (static_cast<int64_t>(blk) << bs_shift) + (tok & (bs - 1));
     const KV* krow = kbase + slot0 * row_stride;
     const KV* vrow = vbase + slot0 * row_stride;
+    if (tok <= new_tok && new_tok < tok + kRowsPerStep) {  // the step holding the fused append's token
+      const int64_t nrow = (static_cast<int64_t>(b) * Hkv + g) * D;
+      const bool mine = tok + r == new_tok;
+      krow = mine ? reinterpret_cast<const KV*>(knew) + nrow : krow;
+      vrow = mine ? reinterpret_cast<const KV*>(vnew) + nrow : vrow;
+    }
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       kx[i] = *reinterpret_cast<const uint4*>(krow + (j + kLanesPerRow * i) * EPC);
@@ -625,7 +667,8 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
                      static_cast<const KV*>(a.k_cache), static_cast<const KV*>(a.v_cache),
                      a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
                      __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
-                     P, per_xcd, scale_log2, v_scale, hsh);
+                     P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),
+                     static_cast<const T*>(a.new_v), a.new_slots, a.tables_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
   const int BH = a.B * a.Hq;

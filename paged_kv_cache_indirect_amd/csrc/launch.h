@@ -46,6 +46,12 @@ struct DecodeArgs {
   float scale;
   float k_scale, v_scale;  // FP8 pools: code value multipliers (1 otherwise)
   int dtype;          // pa_dtype
+  // Fused append (all null for a plain decode): new K/V rows [B, Hkv, D],
+  // their slots [B], and the table buffer that receives their blocks.
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  const int64_t* new_slots = nullptr;
+  int32_t* tables_out = nullptr;
 };
 hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream);
 

@@ -519,6 +519,35 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
   });
 }
 
+pa_status pa_append_decode(pa_pool* pool, void* out, const void* q, const void* key, const void* value,
+                           const int64_t* slot_mapping, int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t B, int32_t num_q_heads, float scale,
+                           int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return Guard([&]() -> pa_status {
+    if (!pool) return Fail(PA_ERR_INVALID, "null pool");
+    if (pool->layout.dtype == PA_FP8_E4M3)
+      return Fail(PA_ERR_UNSUPPORTED, "pa_append_decode needs a bf16 or fp32 pool (use pa_write_kv + pa_decode)");
+    pa::DecodeArgs a{};
+    bool run = false;
+    pa_status s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens, B, num_q_heads, scale,
+                                max_seq_len, partition_tokens, workspace, workspace_bytes, &a, &run);
+    if (s != PA_OK) return s;
+    if (run) {
+      if (!key || !value || !slot_mapping) return Fail(PA_ERR_INVALID, "null argument");
+      if (!Aligned16(key) || !Aligned16(value)) return Fail(PA_ERR_INVALID, "key and value must be 16-byte aligned");
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    s = FlushCopies(pool, st);
+    if (s != PA_OK || !run) return s;
+    a.new_k = key;
+    a.new_v = value;
+    a.new_slots = slot_mapping;
+    a.tables_out = block_tables;
+    return FromHip(pa::LaunchDecode(a, st), "append-decode launch");
+  });
+}
+
 pa_status pa_prefill(pa_pool* pool, void* out, const void* q, const int32_t* cu_q_lens,
                      const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                      int32_t B, int32_t num_q_heads, int32_t max_q_len, float scale, void* stream) {

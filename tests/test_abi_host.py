@@ -316,7 +316,22 @@ def test_device_entry_points_validate_before_launch():
     assert pa.lib.pa_write_kv(pool, None, None, None, 0, None) == pa.PA_OK
     assert pa.lib.pa_write_kv(pool, dummy, dummy, None, 5, None) == pa.PA_ERR_INVALID
     assert pa.lib.pa_write_kv(pool, dummy, dummy, dummy, -1, None) == pa.PA_ERR_INVALID
+    # fused append + decode: pa_decode's checks, then its new rows
+    ad = pa.lib.pa_append_decode
+    assert ad(pool, dummy, dummy, dummy, dummy, dummy, dummy, 256, dummy, 4, 24, 0.1, 4096, 0, dummy, ws, None) \
+        == pa.PA_ERR_UNSUPPORTED                                  # G = 3
+    assert ad(pool, dummy, dummy, None, dummy, dummy, dummy, 256, dummy, 4, 32, 0.1, 4096, 0, dummy, ws, None) \
+        == pa.PA_ERR_INVALID                                      # null key
+    assert ad(pool, dummy, dummy, dummy + 4, dummy, dummy, dummy, 256, dummy, 4, 32, 0.1, 4096, 0, dummy, ws,
+              None) == pa.PA_ERR_INVALID                          # misaligned key
+    assert ad(pool, dummy, dummy, dummy, dummy, None, dummy, 256, dummy, 4, 32, 0.1, 4096, 0, dummy, ws, None) \
+        == pa.PA_ERR_INVALID                                      # null slots
+    assert ad(pool, None, None, None, None, None, None, 0, None, 0, 32, 0.1, 0, 0, None, 0, None) == pa.PA_OK
     pa.pa_free_pool(pool)
+    st, f8 = make_pool(16, 16, hkv=2, d=128, dtype=pa.PA_FP8_E4M3)
+    assert ad(f8, dummy, dummy, dummy, dummy, dummy, dummy, 16, dummy, 2, 8, 0.1, 256, 0, dummy, 1 << 20, None) \
+        == pa.PA_ERR_UNSUPPORTED
+    pa.pa_free_pool(f8)
     st, fpool = make_pool(16, 16, hkv=2, d=64, dtype=pa.PA_F32)
     assert pa.lib.pa_prefill(fpool, dummy, dummy, dummy, dummy, 4, dummy, 2, 4, 16, 0.1, None) \
         == pa.PA_ERR_UNSUPPORTED
