@@ -8,19 +8,22 @@ heads, head_dim 128, bf16, block_size 16, lengths uniform in [512, 4096]
 One step is one decode step of that batch, through the C ABI:
   1. host block manager: every sequence grows by one token
      (pa_seq_append_batch) and gets its slot;
-  2. table export (pa_block_tables) into pinned host memory, then one
-     host-to-device copy of (slots, seq_lens, block_tables);
-  3. pa_write_kv scatters the step's new K/V rows into the paged pool;
-  4. pa_decode: paged attention of the step's queries, in the library's
-     default KV partitions (pa_decode_partition_tokens: here 1536 tokens,
-     1-3 per sequence, merged by log-sum-exp).
+  2. one host-to-device copy of the step's slots and lengths (768 bytes; the
+     block tables were uploaded once before the first step);
+  3. pa_append_decode: the step's new K/V rows are scattered into the paged
+     pool, each new token's block is entered in the device table, and the
+     step's queries attend over their sequences, in the library's default KV
+     partitions (pa_decode_partition_tokens: here 1536 tokens, 1-3 per
+     sequence, merged by log-sum-exp).
+``--unfused-step`` runs the same step as pa_write_kv + pa_decode with the
+whole table exported (pa_block_tables) and uploaded every step.
 The step's new K/V rows and queries are generated before timing and are
 resident in HBM. W untimed warm-up steps, then K timed steps between two
 device synchronisations.
 
 Printed: one JSON line. ``value`` is the whole-step KV throughput (logical
 K+V bytes the decode must read per step, over the step time). ``roofline``
-is the decode op (partition + merge kernels), timed in every timed step with
+is the decode op (pa_append_decode: partition + merge kernels), timed in every timed step with
 a pair of HIP events around ``pa_decode`` on the stream it runs on (the
 only events in the loop: each costs a few microseconds of stream time),
 against 8 TB/s HBM. ``cpu_baseline`` is the CPU oracle
@@ -104,9 +107,9 @@ def run_decode(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import (harness, pa_block_tables, pa_decode, pa_decode_partition_tokens,
-                                             pa_decode_workspace_bytes, pa_seq_append_batch,
-                                             pa_write_kv)
+    from paged_kv_cache_indirect_amd import (harness, pa_append_decode, pa_block_tables, pa_decode,
+                                             pa_decode_partition_tokens, pa_decode_workspace_bytes,
+                                             pa_seq_append_batch, pa_write_kv)
 
     dev = torch.device("cuda:0")
     wl = W.config("gqa8b")
@@ -134,42 +137,78 @@ def run_decode(args):
     ws_bytes = pa_decode_workspace_bytes(B, Hq, D, max_len, pt)
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
-    # Packed per-step metadata: slots int64 [B] | seq_lens int32 [B] | tables int32 [B, max_blocks].
-    off_lens = 8 * B
-    off_tab = off_lens + 4 * B
-    nbytes = off_tab + 4 * B * max_blocks
-    ring = 2
-    pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
-    dmeta = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(ring)]
-    copied = [torch.cuda.Event() for _ in range(ring)]
-    host_views = []
-    for p in pinned:
-        a = p.numpy()
-        host_views.append((a[:off_lens].view(np.int64), a[off_lens:off_tab].view(np.int32),
-                           a[off_tab:].view(np.int32)))
-    dev_views = [(d[:off_lens].view(torch.int64), d[off_lens:off_tab].view(torch.int32),
-                  d[off_tab:].view(torch.int32).view(B, max_blocks)) for d in dmeta]
     seq_ids = np.arange(B, dtype=np.int64)
     stream = torch.cuda.current_stream()
-
     ev_dec0 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
     ev_dec1 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
     lens_per_step = []
+    ring = 2
 
-    def step(s: int) -> None:
-        r = s % ring
-        copied[r].synchronize()                    # pinned[r]'s previous copy has landed
-        slots_h, lens_h, tab_h = host_views[r]
-        pa_seq_append_batch(pool, seq_ids, 1, slots_h)
-        pa_block_tables(pool, seq_ids, max_blocks, tab_h, lens_h)
-        lens_per_step.append(lens_h.copy())
-        dmeta[r].copy_(pinned[r], non_blocking=True)
-        copied[r].record(stream)
-        slots_d, lens_d, tab_d = dev_views[r]
-        pa_write_kv(pool, k_steps[s], v_steps[s], slots_d)
-        ev_dec0[s].record(stream)
-        pa_decode(pool, out, q_steps[s], tab_d, lens_d, wl.scale, max_len, pt, workspace)
-        ev_dec1[s].record(stream)
+    if not args.unfused_step:
+        # Fused step: the device tables are uploaded once; afterwards each
+        # step uploads only its slots and lengths (768 bytes, the runtime's
+        # small-copy path), and pa_append_decode scatters the new rows, fills
+        # in the table entry of each new token's block and decodes.
+        tables0, lens0 = pa_block_tables(pool, seq_ids, max_blocks)
+        tab_d = torch.from_numpy(tables0).to(dev)
+        lens_host = lens0.astype(np.int32)
+        off_lens = 8 * B
+        nbytes = off_lens + 4 * B
+        pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
+        dmeta = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(ring)]
+        copied = [torch.cuda.Event() for _ in range(ring)]
+        host_views = [(p.numpy()[:off_lens].view(np.int64).reshape(B, 1), p.numpy()[off_lens:].view(np.int32))
+                      for p in pinned]
+        dev_views = [(d[:off_lens].view(torch.int64), d[off_lens:].view(torch.int32)) for d in dmeta]
+        torch.cuda.synchronize()
+
+        def step(s: int) -> None:
+            r = s % ring
+            copied[r].synchronize()                    # pinned[r]'s previous copy has landed
+            slots_h, lens_h = host_views[r]
+            pa_seq_append_batch(pool, seq_ids, 1, slots_h)
+            lens_host[:] += 1
+            lens_h[:] = lens_host
+            lens_per_step.append(lens_host.copy())
+            dmeta[r].copy_(pinned[r], non_blocking=True)
+            copied[r].record(stream)
+            slots_d, lens_d = dev_views[r]
+            ev_dec0[s].record(stream)
+            pa_append_decode(pool, out, q_steps[s], k_steps[s], v_steps[s], slots_d, tab_d, lens_d, wl.scale,
+                             max_len, pt, workspace)
+            ev_dec1[s].record(stream)
+    else:
+        # Separate scatter and decode, with the whole table exported and
+        # uploaded every step.
+        # Packed per-step metadata: slots int64 [B] | seq_lens int32 [B] | tables int32 [B, max_blocks].
+        off_lens = 8 * B
+        off_tab = off_lens + 4 * B
+        nbytes = off_tab + 4 * B * max_blocks
+        pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
+        dmeta = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(ring)]
+        copied = [torch.cuda.Event() for _ in range(ring)]
+        host_views = []
+        for p in pinned:
+            a = p.numpy()
+            host_views.append((a[:off_lens].view(np.int64), a[off_lens:off_tab].view(np.int32),
+                               a[off_tab:].view(np.int32)))
+        dev_views = [(d[:off_lens].view(torch.int64), d[off_lens:off_tab].view(torch.int32),
+                      d[off_tab:].view(torch.int32).view(B, max_blocks)) for d in dmeta]
+
+        def step(s: int) -> None:
+            r = s % ring
+            copied[r].synchronize()                    # pinned[r]'s previous copy has landed
+            slots_h, lens_h, tab_h = host_views[r]
+            pa_seq_append_batch(pool, seq_ids, 1, slots_h)
+            pa_block_tables(pool, seq_ids, max_blocks, tab_h, lens_h)
+            lens_per_step.append(lens_h.copy())
+            dmeta[r].copy_(pinned[r], non_blocking=True)
+            copied[r].record(stream)
+            slots_d, lens_d, tab_d = dev_views[r]
+            pa_write_kv(pool, k_steps[s], v_steps[s], slots_d)
+            ev_dec0[s].record(stream)
+            pa_decode(pool, out, q_steps[s], tab_d, lens_d, wl.scale, max_len, pt, workspace)
+            ev_dec1[s].record(stream)
 
     for s in range(args.warmup):
         step(s)
@@ -575,6 +614,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--unfused-step", action="store_true",
+                    help="decode step as pa_write_kv + whole-table upload + pa_decode (default: pa_append_decode)")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="KV partition of the decode legs (0: the library's choice, pa_decode_partition_tokens)")
     ap.add_argument("--prefill-iters", type=int, default=20)
@@ -641,7 +682,10 @@ def main() -> int:
         "config": {
             "workload": "8B-shaped GQA paged decode step: batch 64, 32 q / 8 kv heads, head_dim 128, "
                         "bf16, block_size 16, lengths U[512,4096] (seed 1001), shuffled pool of 1.1x need; "
-                        "step = block-manager append + table export/H2D + KV scatter + decode (library's KV partitions)",
+                        + ("step = block-manager append + table export/H2D + KV scatter + decode"
+                           if args.unfused_step else
+                           "step = block-manager append + slots/lengths H2D + fused KV scatter, table fill-in "
+                           "and decode (pa_append_decode)") + " (library's KV partitions)",
             "global_batch": wl.B,
             "partition_tokens": dec["partition_tokens"],
             "mean_seq_len": dec["mean_len"],
@@ -660,8 +704,11 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": frac,
-            "traffic": measured_traffic("decode"),
-            "kernel": "paged decode (DecodeKernel; log-sum-exp MergeKernel only for sequences split into partitions)",
+            "traffic": None if args.unfused_step else measured_traffic("decode"),
+            "kernel": ("paged decode (DecodeKernel; log-sum-exp MergeKernel only for sequences split into partitions)"
+                       if args.unfused_step else
+                       "fused append + paged decode (DecodeKernel with the step's new rows; log-sum-exp "
+                       "MergeKernel only for sequences split into partitions)"),
             "bytes_per_launch": dec["bytes_per_launch"],
         },
         "cpu_baseline": cpu,

@@ -131,6 +131,17 @@ __device__ __forceinline__ float chunk_dot(const uint4& k, const uint4& q, float
   return acc;
 }
 
+// Element e of a 16-byte chunk as fp32 (8 bf16 or 4 fp32 elements).
+__device__ __forceinline__ float chunk_elem(const uint4& c, int e, uint16_t) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t x = w[e >> 1];
+  return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+}
+__device__ __forceinline__ float chunk_elem(const uint4& c, int e, float) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  return __uint_as_float(w[e]);
+}
+
 __device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) {  // (x.lo, y.lo)
   return __builtin_amdgcn_perm(y, x, 0x05040100u);
 }
@@ -306,38 +317,30 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // outside the pool: no new token). The slot also names the block that
   // holds it, so that block's table entry is taken from the slot rather than
   // from the table (a new block, or a copy-on-write block, is not in the
-  // table yet). The workgroup of the last partition writes its kv heads'
-  // part of the row into the pool, and head group 0's also fills in the
-  // table entry for later calls; every wave reads the new token from
-  // knew / vnew, never from the pool.
+  // table yet). The token is the last of the sequence, so it ends the range
+  // of one wave per kv head: that wave streams the rest of its range as
+  // usual, then takes the token from knew / vnew in one extra step after the
+  // loop and stores its head's part of the row into the pool; head group 0's
+  // workgroup of the last partition fills in the table entry for later calls.
+  constexpr bool kFusable = sizeof(KV) == sizeof(T);  // not for E4M3 pools
   int64_t nslot = -1;
-  if (new_slots != nullptr && L > 0) nslot = new_slots[b];
+  if (kFusable && new_slots != nullptr && L > 0) nslot = new_slots[b];
   // A slot outside the pool is skipped, as pa_write_kv skips it.
   const bool has_new = nslot >= 0 && nslot < (static_cast<int64_t>(num_blocks) << bs_shift);  // wave-uniform
   const int new_tok = has_new ? L - 1 : -1;
   const int new_lb = has_new ? (L - 1) >> bs_shift : -1;
   const int new_blk = static_cast<int>(nslot >> bs_shift);
   const int64_t row_stride = static_cast<int64_t>(Hkv) * D;  // elements between slots
-  if (has_new && p == Pb - 1) {
-    constexpr int kChunkElems = 16 / static_cast<int>(sizeof(KV));
-    constexpr int kHeadChunks = D / kChunkElems;  // 16-byte chunks of one head's row
-    const int heads = 1 << hsh;
-    for (int c = tid; c < 2 * heads * kHeadChunks; c += kThreads) {
-      const int kv = c / (heads * kHeadChunks);
-      const int hc = c - kv * heads * kHeadChunks;
-      const int gh = (gq << hsh) + hc / kHeadChunks;
-      const int e = (hc % kHeadChunks) * kChunkElems;
-      const KV* src = reinterpret_cast<const KV*>(kv ? vnew : knew) + (static_cast<int64_t>(b) * Hkv + gh) * D + e;
-      KV* dst = const_cast<KV*>(kv ? vc : kc) + nslot * row_stride + static_cast<int64_t>(gh) * D + e;
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-    }
-    if (gq == 0 && tid == 0) tables_out[static_cast<int64_t>(b) * max_blocks + new_lb] = new_blk;
-  }
+  if (has_new && p == Pb - 1 && gq == 0 && tid == 0)
+    tables_out[static_cast<int64_t>(b) * max_blocks + new_lb] = new_blk;
 
   const int PTb = ((L + Pb - 1) / Pb + 63) & ~63;  // equal split, multiple of 64 (<= PT)
   const int TPW = PTb >> WS;
   const int w0 = p * PTb + wq * TPW;
-  const int ntok = max(0, min(w0 + TPW, L) - w0);
+  // holds_new: this wave's range ends with the fused append's token, which
+  // the loop leaves for the step after it.
+  const bool holds_new = has_new && w0 <= new_tok && new_tok < w0 + TPW;  // wave-uniform
+  const int ntok = max(0, min(w0 + TPW, L) - w0) - (holds_new ? 1 : 0);
   const int nsteps = (ntok + kRowsPerStep - 1) / kRowsPerStep;
 
   // q fragments: this lane's chunks (j, j + 8, ...) of the G heads.
@@ -400,12 +403,6 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     const int64_t slot0 = (static_cast<int64_t>(blk) << bs_shift) + (tok & (bs - 1));
     const KV* krow = kbase + slot0 * row_stride;
     const KV* vrow = vbase + slot0 * row_stride;
-    if (tok <= new_tok && new_tok < tok + kRowsPerStep) {  // the step holding the fused append's token
-      const int64_t nrow = (static_cast<int64_t>(b) * Hkv + g) * D;
-      const bool mine = tok + r == new_tok;
-      krow = mine ? reinterpret_cast<const KV*>(knew) + nrow : krow;
-      vrow = mine ? reinterpret_cast<const KV*>(vnew) + nrow : vrow;
-    }
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       kx[i] = *reinterpret_cast<const uint4*>(krow + (j + kLanesPerRow * i) * EPC);
@@ -520,6 +517,51 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
         // sink each load next to its first use, exposing memory latency).
         __builtin_amdgcn_sched_barrier(0);
         consume_batch(st0, kA, vA);
+      }
+    }
+  }
+
+  // ---- the fused append's token (the last of the sequence): row group 0
+  // adds it to its state with an exact rescale, and stores the row into the
+  // pool.
+  if constexpr (kFusable) {
+    if (holds_new) {
+      const int64_t nrow = (static_cast<int64_t>(b) * Hkv + g) * D;
+      uint4 kx[CPL], vx[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        kx[i] = *reinterpret_cast<const uint4*>(knew + nrow + (j + kLanesPerRow * i) * EPC);
+        vx[i] = *reinterpret_cast<const uint4*>(vnew + nrow + (j + kLanesPerRow * i) * EPC);
+      }
+      float x[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) a = chunk_dot(kx[i], qf[h][i][0], a, T{});
+        x[h] = sum8(a) * scale_log2;
+      }
+      if (r == 0) {
+        KV* kd = const_cast<KV*>(kc) + nslot * row_stride + static_cast<int64_t>(g) * D;
+        KV* vd = const_cast<KV*>(vc) + nslot * row_stride + static_cast<int64_t>(g) * D;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          *reinterpret_cast<uint4*>(kd + (j + kLanesPerRow * i) * EPC) = kx[i];
+          *reinterpret_cast<uint4*>(vd + (j + kLanesPerRow * i) * EPC) = vx[i];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float mn = fmaxf(m[h], x[h]);
+          const float f = fast_exp2(m[h] - mn);
+          const float wn = fast_exp2(x[h] - mn);
+          l[h] = fmaf(l[h], f, wn);
+#pragma unroll
+          for (int i = 0; i < CPL; ++i)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+              acc[h][i * EPC + e] = fmaf(acc[h][i * EPC + e], f, wn * chunk_elem(vx[i], e, T{}));
+          m[h] = mn;
+        }
       }
     }
   }
