@@ -242,8 +242,8 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   int L;          // the sequence's length, clamped to [0, max_seq_len]
   const int NG = Hkv >> hsh;
   if (B <= kCompactBatch) {
-    // Compact work list: only the (kv head, sequence, partition) items that
-    // exist, kv head outermost, XCD-major over the real count; the grid's
+    // Compact work list: only the (head group, sequence, partition) items
+    // that exist, head group outermost, XCD-major over the real count; the grid's
     // surplus workgroups (sized for B x P) come last and exit.
     __shared__ int s_pref[kCompactBatch + 1];
     __shared__ int s_len[kCompactBatch];  // clamped lengths

@@ -135,7 +135,7 @@ def test_decode_gqa8b_full():
     wl = W.config("gqa8b")
     gpu, ora = build_both(wl)
     ref = oracle_out(wl, ora)
-    for pt in (512, 256, 1024, 2048, 4096, 0):   # 0: the library's choice (one 4096-token partition)
+    for pt in (512, 256, 1024, 2048, 4096, 0):   # 0: the library's choice (1536 tokens here)
         ws = gpu.workspace_for(pt)
         got = widen_out(gpu.decode(pt, ws), wl.dtype)
         assert_close(got, ref, wl.dtype, f"gqa8b pt={pt}")
