@@ -8,12 +8,12 @@ heads, head_dim 128, bf16, block_size 16, lengths uniform in [512, 4096]
 One step is one decode step of that batch, through the C ABI:
   1. host block manager: every sequence grows by one token
      (pa_seq_append_batch) and gets its slot;
-  2. one host-to-device copy of the step's slots and lengths (768 bytes; the
-     block tables were uploaded once before the first step);
-  3. pa_append_decode: the step's new K/V rows are scattered into the paged
-     pool, each new token's block is entered in the device table, and the
-     step's queries attend over their sequences, in the library's default KV
-     partitions (pa_decode_partition_tokens: here 1536 tokens, 1-3 per
+  2. pa_append_decode_args, with the step's slots and lengths passed from
+     host arrays in the launch arguments (the block tables were uploaded once
+     before the first step): the step's new K/V rows are scattered into the
+     paged pool, each new token's block is entered in the device table, and
+     the step's queries attend over their sequences, in the library's default
+     KV partitions (pa_decode_partition_tokens: here 1536 tokens, 1-3 per
      sequence, merged by log-sum-exp).
 ``--unfused-step`` runs the same step as pa_write_kv + pa_decode with the
 whole table exported (pa_block_tables) and uploaded every step.
@@ -23,7 +23,7 @@ device synchronisations.
 
 Printed: one JSON line. ``value`` is the whole-step KV throughput (logical
 K+V bytes the decode must read per step, over the step time). ``roofline``
-is the decode op (pa_append_decode: partition + merge kernels), timed in every fourth timed
+is the decode op (pa_append_decode_args: partition + merge kernels), timed in every fourth timed
 step with a pair of HIP events around the call on the stream it runs on (the
 only events in the loop: a pair costs about 6 us of stream time, so the other
 steps run without),
@@ -64,6 +64,48 @@ KERNEL_SOURCES = {
     "decode": ["decode.hip", "device_common.h", "launch.h"],
     "prefill": ["prefill.hip", "device_common.h", "launch.h"],
 }
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it does not write back and invalidate the caches at system
+    scope, which costs stream time and delays the work after it (about 6 us
+    per event pair around a decode launch with torch's default events). Same
+    use as TimingEvent(): record(stream), then
+    elapsed_time(later_event) in ms once the device is synchronised."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        import torch  # noqa: F401  (its HIP runtime is the one the library uses)
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._ev = ctypes.c_void_p()
+        if TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self._ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream) -> None:
+        if TimingEvent._hip.hipEventRecord(self._ev, stream.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            TimingEvent._hip.hipEventDestroy(self._ev)
+        except Exception:
+            pass
 
 
 def log(msg: str) -> None:
@@ -109,7 +151,7 @@ def run_decode(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import (harness, pa_append_decode, pa_block_tables, pa_decode,
+    from paged_kv_cache_indirect_amd import (harness, pa_append_decode_args, pa_block_tables, pa_decode,
                                              pa_decode_partition_tokens, pa_decode_workspace_bytes,
                                              pa_seq_append_batch, pa_write_kv)
 
@@ -145,44 +187,30 @@ def run_decode(args):
     # a pair costs about 6 us of stream time in the fused step, which the
     # other steps then run without.
     timed_events = {s for s in range(args.warmup, S) if (s - args.warmup) % EVENT_EVERY == 0}
-    ev_dec0 = {s: torch.cuda.Event(enable_timing=True) for s in timed_events}
-    ev_dec1 = {s: torch.cuda.Event(enable_timing=True) for s in timed_events}
+    ev_dec0 = {s: TimingEvent() for s in timed_events}
+    ev_dec1 = {s: TimingEvent() for s in timed_events}
     lens_per_step = []
     ring = 2
 
     if not args.unfused_step:
-        # Fused step: the device tables are uploaded once; afterwards each
-        # step uploads only its slots and lengths (768 bytes, the runtime's
-        # small-copy path), and pa_append_decode scatters the new rows, fills
-        # in the table entry of each new token's block and decodes.
+        # Fused step: the device tables are uploaded once; each step's slots
+        # and lengths travel in the launch arguments of pa_append_decode_args
+        # (no host-to-device copy per step), which scatters the new rows,
+        # enters each new token's block in the device table and decodes.
         tables0, lens0 = pa_block_tables(pool, seq_ids, max_blocks)
         tab_d = torch.from_numpy(tables0).to(dev)
         lens_host = lens0.astype(np.int32)
-        off_lens = 8 * B
-        nbytes = off_lens + 4 * B
-        pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
-        dmeta = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(ring)]
-        copied = [torch.cuda.Event() for _ in range(ring)]
-        host_views = [(p.numpy()[:off_lens].view(np.int64).reshape(B, 1), p.numpy()[off_lens:].view(np.int32))
-                      for p in pinned]
-        dev_views = [(d[:off_lens].view(torch.int64), d[off_lens:].view(torch.int32)) for d in dmeta]
+        slots_h = np.empty((B, 1), dtype=np.int64)
         torch.cuda.synchronize()
 
         def step(s: int) -> None:
-            r = s % ring
-            copied[r].synchronize()                    # pinned[r]'s previous copy has landed
-            slots_h, lens_h = host_views[r]
             pa_seq_append_batch(pool, seq_ids, 1, slots_h)
             lens_host[:] += 1
-            lens_h[:] = lens_host
             lens_per_step.append(lens_host.copy())
-            dmeta[r].copy_(pinned[r], non_blocking=True)
-            copied[r].record(stream)
-            slots_d, lens_d = dev_views[r]
             if s in ev_dec0:
                 ev_dec0[s].record(stream)
-            pa_append_decode(pool, out, q_steps[s], k_steps[s], v_steps[s], slots_d, tab_d, lens_d, wl.scale,
-                             max_len, pt, workspace)
+            pa_append_decode_args(pool, out, q_steps[s], k_steps[s], v_steps[s], slots_h, tab_d, lens_host,
+                                  wl.scale, max_len, pt, workspace)
             if s in ev_dec1:
                 ev_dec1[s].record(stream)
     else:
@@ -227,9 +255,10 @@ def run_decode(args):
     t0 = time.perf_counter()
     for s in range(args.warmup, S):
         step(s)
+    host_s = time.perf_counter() - t0          # host side of the steps (launches are asynchronous)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    log(f"[bench] timed decode steps done: {elapsed * 1e3:.2f} ms")
+    log(f"[bench] timed decode steps done: {elapsed * 1e3:.2f} ms (host {host_s * 1e3:.2f} ms)")
 
     timed = range(args.warmup, S)
     sampled = sorted(timed_events)
@@ -241,6 +270,7 @@ def run_decode(args):
     res = {
         "elapsed_s": elapsed,
         "ms_per_step": elapsed * 1e3 / args.steps,
+        "host_us_per_step": host_s * 1e6 / args.steps,
         "value": sum(step_kv) / elapsed / 1e9,
         "tok_per_s": B * args.steps / elapsed,
         "event_samples": len(dec_ms),
@@ -256,7 +286,7 @@ def run_decode(args):
         "num_blocks": wl.num_blocks,
     }
     cache.close()
-    del cache, k_steps, v_steps, q_steps, workspace, dmeta
+    del cache, k_steps, v_steps, q_steps, workspace
     torch.cuda.empty_cache()
     return wl, res
 
@@ -283,8 +313,8 @@ def run_decode_fp8(args):
     for _ in range(3):
         cache.decode(pt, ws)
     n = args.steps
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    e0 = [TimingEvent() for _ in range(n)]
+    e1 = [TimingEvent() for _ in range(n)]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     for i in range(n):
@@ -328,7 +358,7 @@ def run_decode_skewed(args):
         for _ in range(3):
             cache.decode(pt, ws)
         n = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(n):
@@ -370,7 +400,7 @@ def run_mixed(args):
         for s in range(p["steps"]):
             t0 = time.perf_counter()
             run.prepare(s)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = TimingEvent(), TimingEvent()
             e0.record(stream)
             run.launch()
             e1.record(stream)
@@ -451,8 +481,8 @@ def run_prefix_cache(args):
         cache.decode(ppt, ws)
     n = 20
     stream = torch.cuda.current_stream()
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    e0 = [TimingEvent() for _ in range(n)]
+    e1 = [TimingEvent() for _ in range(n)]
     torch.cuda.synchronize()
     for i in range(n):
         e0[i].record(stream)
@@ -500,7 +530,7 @@ def run_tiered(args):
                     c.decode(0, w)
             n = 20
             stream = torch.cuda.current_stream()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = TimingEvent(), TimingEvent()
             torch.cuda.synchronize()
             e0.record(stream)
             for _ in range(n):
@@ -556,8 +586,8 @@ def run_prefill(args):
     n = args.prefill_iters
     for _ in range(3):
         cache.prefill()
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    e0 = [TimingEvent() for _ in range(n)]
+    e1 = [TimingEvent() for _ in range(n)]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     for i in range(n):
@@ -627,7 +657,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--unfused-step", action="store_true",
-                    help="decode step as pa_write_kv + whole-table upload + pa_decode (default: pa_append_decode)")
+                    help="decode step as pa_write_kv + whole-table upload + pa_decode (default: pa_append_decode_args)")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="KV partition of the decode legs (0: the library's choice, pa_decode_partition_tokens)")
     ap.add_argument("--prefill-iters", type=int, default=20)
@@ -696,8 +726,8 @@ def main() -> int:
                         "bf16, block_size 16, lengths U[512,4096] (seed 1001), shuffled pool of 1.1x need; "
                         + ("step = block-manager append + table export/H2D + KV scatter + decode"
                            if args.unfused_step else
-                           "step = block-manager append + slots/lengths H2D + fused KV scatter, table fill-in "
-                           "and decode (pa_append_decode)") + " (library's KV partitions)",
+                           "step = block-manager append + fused KV scatter, table fill-in and decode with "
+                           "slots/lengths in the launch arguments (pa_append_decode_args)") + " (library's KV partitions)",
             "global_batch": wl.B,
             "partition_tokens": dec["partition_tokens"],
             "mean_seq_len": dec["mean_len"],
@@ -710,6 +740,7 @@ def main() -> int:
             "kernel_us_min": dec["decode_us_min"],
             "kv_gbps_kernel": dec["kv_bytes_per_step"] / (dec["decode_us_mean"] * 1e-6) / 1e9,
             "event_timed_launches": dec["event_samples"],
+            "host_us_per_step": dec["host_us_per_step"],
         },
         "roofline": {
             "bound": "hbm",

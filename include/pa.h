@@ -320,6 +320,21 @@ pa_status pa_append_decode(pa_pool* pool, void* out, const void* q, const void* 
                            int32_t max_seq_len, int32_t partition_tokens, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* pa_append_decode for a batch of at most 128 sequences whose slots and
+ * lengths are on the host: slot_mapping_host [B] and seq_lens_host [B] are
+ * read during the call and travel in the kernels' launch arguments, so a
+ * decode step needs no host-to-device copy at all (a copy costs a few
+ * microseconds to a few tens of them per step on MI355X, against a decode of
+ * about a hundred). Same meaning, output and table update as
+ * pa_append_decode; key, value, q, out, block_tables and workspace are
+ * device pointers. Errors: those of pa_append_decode; PA_ERR_UNSUPPORTED
+ * when B > 128. */
+pa_status pa_append_decode_args(pa_pool* pool, void* out, const void* q, const void* key, const void* value,
+                                const int64_t* slot_mapping_host, int32_t* block_tables, int32_t max_blocks,
+                                const int32_t* seq_lens_host, int32_t B, int32_t num_q_heads, float scale,
+                                int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Chunked causal prefill (a long prompt processed in chunks: "LLM推理优化：技术
  * 原理解析总览", §2.3; prefill and decode mixed in one step: "vLLM 生产级落地
  * 深剖", musen-ai.com, §2). The chunk's own K/V must already be in the cache

@@ -27,6 +27,7 @@ __all__ = [
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error", "StepDesc", "pa_step",
     "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy", "pa_seq_append_tokens",
     "pa_pool_prefix_stats", "pa_tier_block_size", "pa_decode_partition_tokens", "pa_append_decode",
+    "pa_append_decode_args",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
@@ -97,6 +98,8 @@ _SIGS = {
     "pa_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp]),
     "pa_append_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp,
                                 _sz, _vp]),
+    "pa_append_decode_args": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32,
+                                     _vp, _sz, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -297,6 +300,28 @@ def pa_append_decode(pool: int, out, q, key, value, slot_mapping, block_tables, 
                                 float(scale), int(max_seq_len), int(partition_tokens), _dptr(workspace), ws_bytes,
                                 _stream(stream)),
            "pa_append_decode")
+
+
+def pa_append_decode_args(pool: int, out, q, key, value, slots: np.ndarray, block_tables, seq_lens: np.ndarray,
+                          scale: float, max_seq_len: int, partition_tokens: int = 0, workspace=None,
+                          stream=None) -> None:
+    """pa_append_decode with the slots (int64 [B]) and lengths (int32 [B])
+    given as host arrays, passed in the launch arguments (B <= 128)."""
+    B, Hq, D = (int(x) for x in q.shape)
+    sl = np.ascontiguousarray(slots, dtype=np.int64).reshape(-1)
+    ln = np.ascontiguousarray(seq_lens, dtype=np.int32).reshape(-1)
+    if sl.size < B or ln.size < B:
+        raise ValueError("slots and seq_lens need B entries")
+    need = pa_decode_workspace_bytes(B, Hq, D, max_seq_len, partition_tokens)
+    if need and workspace is None:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_append_decode_args(pool, _dptr(out), _dptr(q), _dptr(key), _dptr(value), sl.ctypes.data,
+                                     _dptr(block_tables), int(block_tables.shape[1]), ln.ctypes.data, B, Hq,
+                                     float(scale), int(max_seq_len), int(partition_tokens), _dptr(workspace),
+                                     ws_bytes, _stream(stream)),
+           "pa_append_decode_args")
 
 
 def pa_prefill(pool: int, out, q, cu_q_lens, block_tables, seq_lens, scale: float, max_q_len: int,

@@ -211,12 +211,12 @@ template <typename T, typename KV, int D, int G>
 __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void DecodeKernel(
     T* __restrict__ out, const T* __restrict__ q, const KV* __restrict__ kc,
     const KV* __restrict__ vc, const int32_t* tables,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ ws_acc,
+    const int32_t* seq_lens_in, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int32_t B, int32_t Hkv,
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
     int32_t P, int32_t per_xcd, float scale_log2, float v_scale, int32_t hsh,
-    const T* __restrict__ knew, const T* __restrict__ vnew, const int64_t* __restrict__ new_slots,
-    int32_t* tables_out) {
+    const T* __restrict__ knew, const T* __restrict__ vnew, const int64_t* new_slots_in,
+    int32_t* tables_out, const StepArgs meta) {
   using RG = RowGeom<KV, D>;
   using WD = Widen<KV>;
   constexpr int CPL = RG::kChunksPerLane;
@@ -230,6 +230,10 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_ml[kWaves][G][2];
 
+  // Lengths (and the fused append's slots) come from device memory, or from
+  // the launch arguments when seq_lens_in is null. (The arguments are read in
+  // place: no pointer into them is formed, which would make the compiler
+  // copy them to private memory.)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int bb = tid * kPer + i;
-      int Lb = bb < B ? seq_lens[bb] : 0;
+      int Lb = bb < B ? (seq_lens_in != nullptr ? seq_lens_in[bb] : meta.lens[bb]) : 0;
       Lb = min(max(Lb, 0), max_seq_len);
       s_len[bb] = Lb;
       cnt[i] = bb < B ? max(1, (Lb + PT - 1) / PT) : 0;
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     const int bg = item / P;
     b = bg % B;
     gq = bg / B;
-    L = min(max(seq_lens[b], 0), max_seq_len);
+    L = min(max(seq_lens_in != nullptr ? seq_lens_in[b] : meta.lens[b], 0), max_seq_len);
   }
   const int WS = 2 - hsh;  // log2(waves per kv head)
   const int hh = w >> WS;  // kv head within the workgroup
@@ -324,7 +328,8 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // workgroup of the last partition fills in the table entry for later calls.
   constexpr bool kFusable = sizeof(KV) == sizeof(T);  // not for E4M3 pools
   int64_t nslot = -1;
-  if (kFusable && new_slots != nullptr && L > 0) nslot = new_slots[b];
+  if (kFusable && knew != nullptr && L > 0)
+    nslot = seq_lens_in != nullptr ? (new_slots_in != nullptr ? new_slots_in[b] : -1) : meta.slots[b];
   // A slot outside the pool is skipped, as pa_write_kv skips it.
   const bool has_new = nslot >= 0 && nslot < (static_cast<int64_t>(num_blocks) << bs_shift);  // wave-uniform
   const int new_tok = has_new ? L - 1 : -1;
@@ -637,15 +642,16 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
 template <typename T, int D>
 __global__ __launch_bounds__(256) void MergeKernel(T* __restrict__ out, const float* __restrict__ ws_acc,
                                                    const float* __restrict__ ws_ml,
-                                                   const int32_t* __restrict__ seq_lens, int32_t BH,
-                                                   int32_t Hq, int32_t max_seq_len, int32_t PT, int32_t P) {
+                                                   const int32_t* seq_lens_in, int32_t BH,
+                                                   int32_t Hq, int32_t max_seq_len, int32_t PT, int32_t P,
+                                                   const StepArgs meta) {
   constexpr int EPL = D / 64;
   constexpr int kChunk = 16;
   const int lane = threadIdx.x & 63;
   const int bh = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
   if (bh >= BH) return;
   const int b = bh / Hq;
-  int L = seq_lens[b];
+  int L = seq_lens_in != nullptr ? seq_lens_in[b] : meta.lens[b];
   L = min(max(L, 0), max_seq_len);
   const int Pb = (L + PT - 1) / PT;
   if (Pb <= 1) return;  // written by pass 1
@@ -704,19 +710,21 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   const float scale_log2 = a.scale * (fp8 ? a.k_scale : 1.f) * 1.4426950408889634f;
   const float v_scale = fp8 ? a.v_scale : 1.f;
   DecodeWorkspace ws = DecodeWorkspaceLayout(a.ws, a.B, a.Hq, a.D, P);
+  static const StepArgs kNoStepArgs{};
+  const StepArgs& meta = a.step_args != nullptr ? *a.step_args : kNoStepArgs;
   hipLaunchKernelGGL((DecodeKernel<T, KV, D, G>), dim3(per_xcd * 8), dim3(kThreads), 0, stream,
                      static_cast<T*>(a.out), static_cast<const T*>(a.q),
                      static_cast<const KV*>(a.k_cache), static_cast<const KV*>(a.v_cache),
                      a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
                      __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
                      P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),
-                     static_cast<const T*>(a.new_v), a.new_slots, a.tables_out);
+                     static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, meta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
   const int BH = a.B * a.Hq;
   hipLaunchKernelGGL((MergeKernel<T, D>), dim3((BH + 3) / 4), dim3(256), 0, stream,
                      static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, BH, a.Hq, a.max_seq_len,
-                     a.partition_tokens, P);
+                     a.partition_tokens, P, meta);
   return hipGetLastError();
 }
 

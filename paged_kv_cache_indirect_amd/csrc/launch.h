@@ -32,6 +32,14 @@ struct BlockCopyList {
 hipError_t LaunchCopyBlocks(void* k_cache, void* v_cache, const BlockCopyList& list, int64_t block_bytes,
                             hipStream_t stream);
 
+// A decode step's per-sequence slots and lengths passed by value in the
+// launch (pa_append_decode_args), for batches up to kStepArgBatch.
+constexpr int kStepArgBatch = 128;
+struct StepArgs {
+  int64_t slots[kStepArgBatch];
+  int32_t lens[kStepArgBatch];
+};
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -52,6 +60,8 @@ struct DecodeArgs {
   const void* new_v = nullptr;
   const int64_t* new_slots = nullptr;
   int32_t* tables_out = nullptr;
+  // Slots and lengths in the launch arguments (seq_lens and new_slots null).
+  const StepArgs* step_args = nullptr;
 };
 hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream);
 

@@ -548,6 +548,45 @@ pa_status pa_append_decode(pa_pool* pool, void* out, const void* q, const void* 
   });
 }
 
+pa_status pa_append_decode_args(pa_pool* pool, void* out, const void* q, const void* key, const void* value,
+                                const int64_t* slot_mapping_host, int32_t* block_tables, int32_t max_blocks,
+                                const int32_t* seq_lens_host, int32_t B, int32_t num_q_heads, float scale,
+                                int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return Guard([&]() -> pa_status {
+    if (!pool) return Fail(PA_ERR_INVALID, "null pool");
+    if (pool->layout.dtype == PA_FP8_E4M3)
+      return Fail(PA_ERR_UNSUPPORTED, "pa_append_decode_args needs a bf16 or fp32 pool");
+    if (B > pa::kStepArgBatch)
+      return Fail(PA_ERR_UNSUPPORTED, "pa_append_decode_args takes at most " + std::to_string(pa::kStepArgBatch) +
+                                          " sequences (use pa_append_decode)");
+    pa::DecodeArgs a{};
+    bool run = false;
+    pa_status s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens_host, B, num_q_heads, scale,
+                                max_seq_len, partition_tokens, workspace, workspace_bytes, &a, &run);
+    if (s != PA_OK) return s;
+    if (run) {
+      if (!key || !value || !slot_mapping_host) return Fail(PA_ERR_INVALID, "null argument");
+      if (!Aligned16(key) || !Aligned16(value)) return Fail(PA_ERR_INVALID, "key and value must be 16-byte aligned");
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    s = FlushCopies(pool, st);
+    if (s != PA_OK || !run) return s;
+    pa::StepArgs args{};
+    for (int32_t b = 0; b < B; ++b) {
+      args.slots[b] = slot_mapping_host[b];
+      args.lens[b] = seq_lens_host[b];
+    }
+    a.seq_lens = nullptr;
+    a.new_k = key;
+    a.new_v = value;
+    a.new_slots = nullptr;
+    a.tables_out = block_tables;
+    a.step_args = &args;
+    return FromHip(pa::LaunchDecode(a, st), "append-decode launch");
+  });
+}
+
 pa_status pa_prefill(pa_pool* pool, void* out, const void* q, const int32_t* cu_q_lens,
                      const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                      int32_t B, int32_t num_q_heads, int32_t max_q_len, float scale, void* stream) {

@@ -331,7 +331,23 @@ def test_device_entry_points_validate_before_launch():
     st, f8 = make_pool(16, 16, hkv=2, d=128, dtype=pa.PA_FP8_E4M3)
     assert ad(f8, dummy, dummy, dummy, dummy, dummy, dummy, 16, dummy, 2, 8, 0.1, 256, 0, dummy, 1 << 20, None) \
         == pa.PA_ERR_UNSUPPORTED
+    aa = pa.lib.pa_append_decode_args
+    slots_h = np.zeros(200, dtype=np.int64)
+    lens_h = np.ones(200, dtype=np.int32)
+    assert aa(f8, dummy, dummy, dummy, dummy, slots_h.ctypes.data, dummy, 16, lens_h.ctypes.data, 2, 8, 0.1, 256, 0,
+              dummy, 1 << 20, None) == pa.PA_ERR_UNSUPPORTED
     pa.pa_free_pool(f8)
+    st, pool = make_pool(64, 16, hkv=8, d=128)
+    # launch-argument variant: at most 128 sequences; the host arrays are required
+    assert aa(pool, dummy, dummy, dummy, dummy, slots_h.ctypes.data, dummy, 256, lens_h.ctypes.data, 129, 32, 0.1,
+              4096, 0, dummy, 1 << 30, None) == pa.PA_ERR_UNSUPPORTED
+    assert "at most 128" in pa.pa_last_error()
+    assert aa(pool, dummy, dummy, dummy, dummy, None, dummy, 256, lens_h.ctypes.data, 4, 32, 0.1, 4096, 0, dummy,
+              1 << 30, None) == pa.PA_ERR_INVALID
+    assert aa(pool, dummy, dummy, dummy, dummy, slots_h.ctypes.data, dummy, 256, None, 4, 32, 0.1, 4096, 0, dummy,
+              1 << 30, None) == pa.PA_ERR_INVALID
+    assert aa(pool, None, None, None, None, None, None, 0, None, 0, 32, 0.1, 0, 0, None, 0, None) == pa.PA_OK
+    pa.pa_free_pool(pool)
     st, fpool = make_pool(16, 16, hkv=2, d=64, dtype=pa.PA_F32)
     assert pa.lib.pa_prefill(fpool, dummy, dummy, dummy, dummy, 4, dummy, 2, 4, 16, 0.1, None) \
         == pa.PA_ERR_UNSUPPORTED

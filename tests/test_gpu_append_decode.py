@@ -16,7 +16,9 @@ block-manager model + scatter oracle). Then every step:
 After the last step the fused pool equals the unfused pool and the oracle's
 pool bit for bit (never-written slots poisoned with NaN on all sides), and the
 fused path's device table equals the exported tables.
-Cases cover steps that open new blocks (block sizes 8, 16, 32), copy-on-write
+Both entry points are covered: slots and lengths in device memory
+(pa_append_decode) and from host arrays in the launch arguments
+(pa_append_decode_args). Cases cover steps that open new blocks (block sizes 8, 16, 32), copy-on-write
 of a shared partly filled block (the new token's block is a fresh copy), rows
 with slot -1 (no new token), several partitions per sequence, G in {1, 4, 8},
 D in {64, 128}, and the 8B-shaped batch at full size.
@@ -39,11 +41,11 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-def run_case(wl, steps, pt, skip=()):
-    from paged_kv_cache_indirect_amd import (harness, pa_append_decode, pa_block_tables, pa_decode,
-                                             pa_seq_append_batch, pa_write_kv)
+def run_case(wl, steps, pt, skip=(), host_args=False):
+    from paged_kv_cache_indirect_amd import (harness, pa_append_decode, pa_append_decode_args, pa_block_tables,
+                                             pa_decode, pa_seq_append_batch, pa_write_kv)
     print(f"[case] {wl.name} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} bs={wl.block_size} {wl.dtype} "
-          f"steps={steps} pt={pt} skip={list(skip)}", flush=True)
+          f"steps={steps} pt={pt} skip={list(skip)} host_args={host_args}", flush=True)
     dev = "cuda"
     fused = harness.GpuCache(wl, device=dev)
     plain = harness.GpuCache(wl, device=dev)
@@ -91,8 +93,11 @@ def run_case(wl, steps, pt, skip=()):
         pa_decode(plain.pool, out_plain, qd, torch.from_numpy(tp).to(dev), lens_d, wl.scale, msl, pt, ws_plain)
         # fused
         out_fused = torch.empty_like(qd)
-        pa_append_decode(fused.pool, out_fused, qd, kd, vd, torch.from_numpy(sf).to(dev), tab_fused, lens_d,
-                         wl.scale, msl, pt, ws)
+        if host_args:     # slots and lengths from host arrays, in the launch arguments
+            pa_append_decode_args(fused.pool, out_fused, qd, kd, vd, sf, tab_fused, lens, wl.scale, msl, pt, ws)
+        else:
+            pa_append_decode(fused.pool, out_fused, qd, kd, vd, torch.from_numpy(sf).to(dev), tab_fused, lens_d,
+                             wl.scale, msl, pt, ws)
         torch.cuda.synchronize()
         got = OA.widen(harness.to_host(out_fused, wl.dtype), wl.dtype).astype(np.float64)
         unf = OA.widen(harness.to_host(out_plain, wl.dtype), wl.dtype).astype(np.float64)
@@ -128,12 +133,13 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("host_args", [False, True])
 @pytest.mark.parametrize("lens,Hq,Hkv,D,bs,dtype,pt,steps,skip", SMALL)
-def test_append_decode_small(lens, Hq, Hkv, D, bs, dtype, pt, steps, skip):
+def test_append_decode_small(lens, Hq, Hkv, D, bs, dtype, pt, steps, skip, host_args):
     need = sum(-(-(L + steps) // bs) for L in lens)
     wl = W.make_decode("append_small", lens, Hq=Hq, Hkv=Hkv, D=D, block_size=bs, dtype=dtype, seed=11,
                        num_blocks=need + 8)
-    run_case(wl, steps, pt, skip)
+    run_case(wl, steps, pt, skip, host_args)
 
 
 def test_append_decode_copy_on_write():
@@ -144,11 +150,12 @@ def test_append_decode_copy_on_write():
     wl = W.make_prefix_share("cow_step", 6, 1000, [0, 0, 0, 5, 0, 17], Hq=8, Hkv=2, D=128, block_size=16,
                              dtype="bf16", seed=21)
     run_case(wl, 2, 0)
-    run_case(wl, 2, 256)
+    run_case(wl, 2, 256, host_args=True)
 
 
-def test_append_decode_gqa8b_full():
-    run_case(W.config("gqa8b"), 2, 0)
+@pytest.mark.parametrize("host_args", [False, True])
+def test_append_decode_gqa8b_full(host_args):
+    run_case(W.config("gqa8b"), 2, 0, host_args=host_args)
 
 
 def test_append_decode_rejects_fp8_pool():
