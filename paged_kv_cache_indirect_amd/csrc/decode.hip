@@ -39,10 +39,11 @@
 //    weights rounded to bf16 (fp32 accumulate) — half the instructions of
 //    unpack + FMA. fp32 caches use plain FMAs.
 //  * At the end the 8 row groups of a wave merge by DPP/shuffles and the
-//    waves of one head through LDS, by log-sum-exp. A sequence that fits in one partition
-//    writes its output directly; otherwise every partition writes its partial
-//    state (max, sum, Σ w·V) and a second, small kernel merges them by
-//    log-sum-exp, one wave per (sequence, q head). (Merging inside the first
+//    waves of one head through LDS, by log-sum-exp. A sequence that fits in
+//    one partition writes its output directly; otherwise every partition
+//    writes its partial state (max, sum, Σ w·V) and a second, small kernel
+//    merges them by log-sum-exp, one wave per (sequence, q head), four per
+//    workgroup. (Merging inside the first
 //    kernel through an arrival counter needs an agent-scope release/acquire
 //    per partition — an L2 writeback and invalidate per workgroup on this
 //    chip — which measured far slower than one extra launch.)
@@ -56,6 +57,14 @@
 //    outermost: consecutive hardware workgroup ids go to different XCDs, so
 //    each XCD owns a contiguous range (half a head group when Hkv = 8) and a
 //    shared prefix block of those heads is re-read from few XCDs' L2.
+//  * Fused append (a decode step in one call): each sequence's new token is
+//    the last of its sequence, so it ends the range of exactly one wave per
+//    kv head. That wave streams the rest of its range as usual, then adds
+//    the token from the step's input row in one extra step and stores the
+//    row into the pool; its block's table entry is taken from the token's
+//    slot and written back for later calls. The step's lengths and slots
+//    come from device memory or, for batches up to 128, from the launch
+//    arguments (no host-to-device copy per step).
 #include "device_common.h"
 #include "launch.h"
 
