@@ -152,8 +152,8 @@ def run_decode(args):
 
     import workloads as W
     from paged_kv_cache_indirect_amd import (harness, pa_append_decode_args, pa_block_tables, pa_decode,
-                                             pa_decode_partition_tokens, pa_decode_workspace_bytes,
-                                             pa_seq_append_batch, pa_write_kv)
+                                             pa_decode_partition_tokens, pa_decode_partition_tokens_for_lengths,
+                                             pa_decode_workspace_bytes, pa_seq_append_batch, pa_write_kv)
 
     dev = torch.device("cuda:0")
     wl = W.config("gqa8b")
@@ -280,7 +280,8 @@ def run_decode(args):
         "bytes_per_launch": float(np.mean(step_bytes)),
         "kv_bytes_per_step": float(np.mean(step_kv)),
         "achieved_gbps": achieved,
-        "partition_tokens": pt_used,
+        "partition_tokens": pt_used if (pt or args.unfused_step) else
+        sorted({pa_decode_partition_tokens_for_lengths(pool, lens_per_step[s], max_len) for s in timed}),
         "mean_len": float(np.mean([np.mean(lens_per_step[s]) for s in timed])),
         "max_len_bound": max_len,
         "num_blocks": wl.num_blocks,
@@ -342,12 +343,15 @@ def run_decode_fp8(args):
 
 def run_decode_skewed(args):
     """A batch whose one long sequence dominates (63 x 512 tokens + 1 x 32768,
-    8B-shaped heads): the library's default partition against a fixed 512."""
+    8B-shaped heads): pa_decode in the library's shape-based default partition
+    and in a fixed 512, and pa_append_decode_args (lengths on the host, no new
+    tokens) in its length-based default."""
     import numpy as np
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import harness, pa_decode_partition_tokens
+    from paged_kv_cache_indirect_amd import (harness, pa_append_decode_args, pa_decode_partition_tokens,
+                                             pa_decode_partition_tokens_for_lengths)
 
     wl = W.make_decode("skewed", [512] * 63 + [32768], Hq=32, Hkv=8, D=128, block_size=16, dtype="bf16", seed=77)
     cache = harness.GpuCache(wl, poison=False)
@@ -369,9 +373,33 @@ def run_decode_skewed(args):
         nbytes = decode_bytes(wl, wl.seq_lens)
         res[label] = {"partition_tokens": pt or pa_decode_partition_tokens(cache.pool, wl.B, wl.max_seq_len),
                       "us_mean": t * 1e6, "gbps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+    # Lengths on the host: the partition comes from the lengths themselves.
+    lens = np.asarray(wl.seq_lens, dtype=np.int32)
+    no_slots = np.full(wl.B, -1, dtype=np.int64)
+    rows = torch.zeros((wl.B, wl.Hkv, wl.D), dtype=torch.bfloat16, device="cuda")
+    ws = cache.workspace_for(0)
+
+    def host_call():
+        pa_append_decode_args(cache.pool, cache.out, cache.q, rows, rows, no_slots, cache.block_tables, lens,
+                              wl.scale, wl.max_seq_len, 0, ws)
+    for _ in range(3):
+        host_call()
+    n = 20
+    e0, e1 = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        host_call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / n * 1e-3
+    nbytes = decode_bytes(wl, wl.seq_lens)
+    res["host_lengths"] = {"partition_tokens": pa_decode_partition_tokens_for_lengths(cache.pool, lens, wl.max_seq_len),
+                           "us_mean": t * 1e6, "gbps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
     cache.close()
     log(f"[bench] skewed batch: default pt {res['default']['partition_tokens']} {res['default']['us_mean']:.1f} us, "
-        f"pt 512 {res['fixed_512']['us_mean']:.1f} us")
+        f"pt 512 {res['fixed_512']['us_mean']:.1f} us, host lengths pt {res['host_lengths']['partition_tokens']} "
+        f"{res['host_lengths']['us_mean']:.1f} us")
     return res
 
 

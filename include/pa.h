@@ -265,6 +265,18 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
  * xxqk.cn, §3 phase 2.) Returns 0 for a null pool or negative sizes. */
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t B, int32_t max_seq_len);
 
+/* The KV partition pa_append_decode_args uses for partition_tokens = 0, from
+ * the lengths themselves (seq_lens_host [B], host): when every sequence has
+ * at least 8192 tokens, the shape rule of pa_decode_partition_tokens;
+ * otherwise the smallest multiple of 64 tokens, at least 512, for which the
+ * launch has at most 480 (sequence, kv-head group, partition) items, so that
+ * every item starts at once on MI355X and a long sequence among short ones
+ * is split finely (one partition per sequence when no partition gets that
+ * low). Returns 0 for a null pool, negative sizes or null lengths with
+ * B > 0. */
+int32_t pa_decode_partition_tokens_for_lengths(const pa_pool* pool, const int32_t* seq_lens_host, int32_t B,
+                                               int32_t max_seq_len);
+
 /* Decode attention: one query token per sequence over its paged cache.
  * out (device): [B, num_q_heads, head_dim], pool dtype (bf16 for an FP8
  *   pool), written.
@@ -327,8 +339,9 @@ pa_status pa_append_decode(pa_pool* pool, void* out, const void* q, const void* 
  * microseconds to a few tens of them per step on MI355X, against a decode of
  * about a hundred). Same meaning, output and table update as
  * pa_append_decode; key, value, q, out, block_tables and workspace are
- * device pointers. Errors: those of pa_append_decode; PA_ERR_UNSUPPORTED
- * when B > 128. */
+ * device pointers. partition_tokens = 0 takes the partition from the
+ * actual lengths (pa_decode_partition_tokens_for_lengths). Errors: those of
+ * pa_append_decode; PA_ERR_UNSUPPORTED when B > 128. */
 pa_status pa_append_decode_args(pa_pool* pool, void* out, const void* q, const void* key, const void* value,
                                 const int64_t* slot_mapping_host, int32_t* block_tables, int32_t max_blocks,
                                 const int32_t* seq_lens_host, int32_t B, int32_t num_q_heads, float scale,

@@ -27,7 +27,7 @@ __all__ = [
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error", "StepDesc", "pa_step",
     "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy", "pa_seq_append_tokens",
     "pa_pool_prefix_stats", "pa_tier_block_size", "pa_decode_partition_tokens", "pa_append_decode",
-    "pa_append_decode_args",
+    "pa_append_decode_args", "pa_decode_partition_tokens_for_lengths",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
@@ -94,6 +94,7 @@ _SIGS = {
     "pa_write_kv": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_partition_tokens": (_i32, [_vp, _i32, _i32]),
+    "pa_decode_partition_tokens_for_lengths": (_i32, [_vp, _vp, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp]),
     "pa_append_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp,
@@ -264,6 +265,14 @@ def pa_decode_workspace_bytes(B: int, num_q_heads: int, head_dim: int, max_seq_l
 def pa_decode_partition_tokens(pool: int, B: int, max_seq_len: int) -> int:
     """The KV partition pa_decode uses for partition_tokens=0 on this pool."""
     return int(lib.pa_decode_partition_tokens(pool, B, max_seq_len))
+
+
+def pa_decode_partition_tokens_for_lengths(pool: int, seq_lens, max_seq_len: int) -> int:
+    """The partition pa_append_decode_args picks for partition_tokens = 0
+    from the host lengths ``seq_lens`` (int32 [B])."""
+    ln = np.ascontiguousarray(seq_lens, dtype=np.int32).reshape(-1)
+    return int(lib.pa_decode_partition_tokens_for_lengths(pool, ln.ctypes.data if ln.size else None, int(ln.size),
+                                                          int(max_seq_len)))
 
 
 def pa_decode(pool: int, out, q, block_tables, seq_lens, scale: float, max_seq_len: int,

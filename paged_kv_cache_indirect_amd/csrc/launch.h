@@ -1,6 +1,7 @@
 // Kernel launchers called by the C-ABI layer (pa_api.cpp). Arguments are
 // validated by the caller; these only enqueue work on `stream`.
 #pragma once
+#include <climits>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -138,6 +139,41 @@ inline int32_t DecodeDefaultPartition(int32_t B, int32_t Hkv, int32_t max_seq_le
   if (pt > kDecodeDefaultMaxPartition) pt = kDecodeDefaultMaxPartition;
   if (pt < kDecodeMinPartition) pt = kDecodeMinPartition;
   return static_cast<int32_t>(pt);
+}
+// The default partition when the caller's lengths are on the host
+// (pa_append_decode_args): batches whose every sequence is a long context
+// keep the shape rule above; otherwise the smallest partition (a multiple of
+// 64, at least 512 tokens) whose actual item count, head groups x
+// sum_b max(1, ceil(L_b / pt)), is at most kDecodeShortItems, so that every
+// item starts in the first round while long sequences in a batch of short
+// ones are split finely. One partition per sequence when even that exceeds
+// the count.
+inline int32_t DecodePartitionForLengths(const int32_t* lens, int32_t B, int32_t Hkv, int32_t max_seq_len) {
+  int64_t lo = INT64_MAX, hi = 1;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t L = lens[b] < 0 ? 0 : (lens[b] > max_seq_len ? max_seq_len : lens[b]);
+    lo = L < lo ? L : lo;
+    hi = L > hi ? L : hi;
+  }
+  if (B > 0 && lo >= kDecodeLongContext) return DecodeDefaultPartition(B, Hkv, max_seq_len, false);
+  const int64_t groups = Hkv > 1 ? (Hkv >> DecodeHeadShift(Hkv)) : 1;
+  const int64_t top = (hi + 63) / 64 * 64;
+  auto items = [&](int64_t pt) {
+    int64_t n = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      const int64_t L = lens[b] < 0 ? 0 : (lens[b] > max_seq_len ? max_seq_len : lens[b]);
+      n += L > pt ? (L + pt - 1) / pt : 1;
+    }
+    return n * groups;
+  };
+  int64_t a = 512, z = top < 512 ? 512 : top;  // smallest pt in [a, z] with items(pt) <= target
+  if (items(z) > kDecodeShortItems) return static_cast<int32_t>(z);
+  while (a < z) {
+    const int64_t mid = (a + z) / 2 / 64 * 64;
+    if (mid < a) break;
+    if (items(mid) <= kDecodeShortItems) z = mid; else a = mid + 64;
+  }
+  return static_cast<int32_t>(z);
 }
 inline int32_t DecodePartitions(int32_t max_seq_len, int32_t partition_tokens) {
   int32_t p = (max_seq_len + partition_tokens - 1) / partition_tokens;

@@ -498,6 +498,13 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
   return pa::DecodeWorkspaceBytes(B, num_q_heads, head_dim, pa::DecodePartitions(max_seq_len, pt));
 }
 
+int32_t pa_decode_partition_tokens_for_lengths(const pa_pool* pool, const int32_t* seq_lens_host, int32_t B,
+                                               int32_t max_seq_len) {
+  if (!pool || B < 0 || max_seq_len < 0 || (B > 0 && !seq_lens_host)) return 0;
+  if (B == 0) return pa::DecodeDefaultPartition(0, pool->layout.num_kv_heads, max_seq_len, false);
+  return pa::DecodePartitionForLengths(seq_lens_host, B, pool->layout.num_kv_heads, max_seq_len);
+}
+
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t B, int32_t max_seq_len) {
   if (!pool || B < 0 || max_seq_len < 0) return 0;
   const pa_kv_layout& l = pool->layout;
@@ -562,8 +569,11 @@ pa_status pa_append_decode_args(pa_pool* pool, void* out, const void* q, const v
                                           " sequences (use pa_append_decode)");
     pa::DecodeArgs a{};
     bool run = false;
+    const int32_t pt = partition_tokens == 0 && B > 0 && seq_lens_host && max_seq_len >= 0
+                           ? pa::DecodePartitionForLengths(seq_lens_host, B, pool->layout.num_kv_heads, max_seq_len)
+                           : partition_tokens;
     pa_status s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens_host, B, num_q_heads, scale,
-                                max_seq_len, partition_tokens, workspace, workspace_bytes, &a, &run);
+                                max_seq_len, pt, workspace, workspace_bytes, &a, &run);
     if (s != PA_OK) return s;
     if (run) {
       if (!key || !value || !slot_mapping_host) return Fail(PA_ERR_INVALID, "null argument");

@@ -281,6 +281,42 @@ def test_decode_partition_policy():
         pa.pa_free_pool(p)
 
 
+def test_decode_partition_for_host_lengths():
+    """pa_append_decode_args's partition for partition_tokens = 0, from the
+    lengths: all sequences >= 8192 tokens -> the shape rule; otherwise the
+    smallest multiple of 64 (>= 512) with at most 480 items (4 head groups
+    of two kv heads x sum_b max(1, ceil(L_b / pt))), else one partition per
+    sequence."""
+    st, p16 = make_pool(64, 16, hkv=8, d=128)
+    f = pa.pa_decode_partition_tokens_for_lengths
+    import workloads as W
+    assert f(p16, W.config("gqa8b").seq_lens, 4142) == 1536
+    assert f(p16, [512] * 63 + [32768], 32768) == 576            # the long one split finely
+    assert f(p16, [32768] * 8, 32768) == pa.pa_decode_partition_tokens(p16, 8, 32768) == 4096
+    assert f(p16, [3000] * 128, 3072) == 3008                      # 512 items at least: one partition each
+    assert f(None, [1, 2], 10) == 0 and f(p16, [1, 2], -1) == 0
+
+    def items(L, pt):
+        return 4 * sum(max(1, -(-x // pt)) for x in L)
+
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        B = int(rng.integers(1, 130))
+        hi = int(rng.integers(1, 9000))
+        L = rng.integers(0, hi + 1, B).tolist()
+        msl = max(L) + int(rng.integers(0, 50))
+        pt = f(p16, L, msl)
+        top = max(512, -(-max(max(L), 1) // 64) * 64)
+        if min(L) >= 8192:
+            continue
+        assert pt % 64 == 0 and 512 <= pt <= top, (L, pt)
+        if items(L, top) > 480:
+            assert pt == top
+        else:
+            assert items(L, pt) <= 480 and (pt == 512 or items(L, pt - 64) > 480), (pt, items(L, pt))
+    pa.pa_free_pool(p16)
+
+
 def test_device_entry_points_validate_before_launch():
     st, pool = make_pool(64, 16, hkv=8, d=128)
     assert st == 0
