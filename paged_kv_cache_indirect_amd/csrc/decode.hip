@@ -68,6 +68,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace pa {
 
 namespace {
@@ -216,7 +218,17 @@ __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
 // T: q / out / arithmetic type (float or bf16 bits); KV: cache element type
 // (T itself, or Fp8E4M3 with bf16 T). v_scale multiplies the output (the
 // FP8 value scale; 1 otherwise); the key scale is folded into scale_log2.
-template <typename T, typename KV, int D, int G>
+// Launch-argument block of the fused variants; the plain decode takes an
+// empty one (a 1.5 KB argument block and the reads of it cost the plain
+// kernel about 13 VGPRs and 2-3% of its time).
+struct NoStepArgs {};
+template <bool kFused>
+using StepArgsOf = typename std::conditional<kFused, StepArgs, NoStepArgs>::type;
+
+// kFused: the fused-append variant (pa_append_decode*); the plain decode is
+// compiled without that code. kArgs (with kFused): lengths and slots come
+// from the launch arguments (pa_append_decode_args), not device memory.
+template <typename T, typename KV, int D, int G, bool kFused, bool kArgs>
 __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void DecodeKernel(
     T* __restrict__ out, const T* __restrict__ q, const KV* __restrict__ kc,
     const KV* __restrict__ vc, const int32_t* tables,
@@ -225,7 +237,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
     int32_t P, int32_t per_xcd, float scale_log2, float v_scale, int32_t hsh,
     const T* __restrict__ knew, const T* __restrict__ vnew, const int64_t* new_slots_in,
-    int32_t* tables_out, const StepArgs meta) {
+    int32_t* tables_out, const StepArgsOf<kArgs> meta) {
   using RG = RowGeom<KV, D>;
   using WD = Widen<KV>;
   constexpr int CPL = RG::kChunksPerLane;
@@ -240,7 +252,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   __shared__ float s_ml[kWaves][G][2];
 
   // Lengths (and the fused append's slots) come from device memory, or from
-  // the launch arguments when seq_lens_in is null. (The arguments are read in
+  // the launch arguments in the kArgs variant. (The arguments are read in
   // place: no pointer into them is formed, which would make the compiler
   // copy them to private memory.)
   const int tid = threadIdx.x;
@@ -267,7 +279,11 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int bb = tid * kPer + i;
-      int Lb = bb < B ? (seq_lens_in != nullptr ? seq_lens_in[bb] : meta.lens[bb]) : 0;
+      int Lb = 0;
+      if (bb < B) {
+        if constexpr (kArgs) Lb = meta.lens[bb];
+        else Lb = seq_lens_in[bb];
+      }
       Lb = min(max(Lb, 0), max_seq_len);
       s_len[bb] = Lb;
       cnt[i] = bb < B ? max(1, (Lb + PT - 1) / PT) : 0;
@@ -314,7 +330,10 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     const int bg = item / P;
     b = bg % B;
     gq = bg / B;
-    L = min(max(seq_lens_in != nullptr ? seq_lens_in[b] : meta.lens[b], 0), max_seq_len);
+    int Lr;
+    if constexpr (kArgs) Lr = meta.lens[b];
+    else Lr = seq_lens_in[b];
+    L = min(max(Lr, 0), max_seq_len);
   }
   const int WS = 2 - hsh;  // log2(waves per kv head)
   const int hh = w >> WS;  // kv head within the workgroup
@@ -335,10 +354,14 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // usual, then takes the token from knew / vnew in one extra step after the
   // loop and stores its head's part of the row into the pool; head group 0's
   // workgroup of the last partition fills in the table entry for later calls.
-  constexpr bool kFusable = sizeof(KV) == sizeof(T);  // not for E4M3 pools
+  constexpr bool kFusable = kFused && sizeof(KV) == sizeof(T);  // not for E4M3 pools
   int64_t nslot = -1;
-  if (kFusable && knew != nullptr && L > 0)
-    nslot = seq_lens_in != nullptr ? (new_slots_in != nullptr ? new_slots_in[b] : -1) : meta.slots[b];
+  if constexpr (kFusable) {
+    if (knew != nullptr && L > 0) {
+      if constexpr (kArgs) nslot = meta.slots[b];
+      else nslot = new_slots_in != nullptr ? new_slots_in[b] : -1;
+    }
+  }
   // A slot outside the pool is skipped, as pa_write_kv skips it.
   const bool has_new = nslot >= 0 && nslot < (static_cast<int64_t>(num_blocks) << bs_shift);  // wave-uniform
   const int new_tok = has_new ? L - 1 : -1;
@@ -384,7 +407,10 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // last entry when it falls inside a block).
   const int lb_end = ntok > 0 ? (w0 + ntok + bs - 1) >> bs_shift : lb0;
   // Table entry idx, or the fused append's block for the new token's entry.
-  auto table_at = [&](int idx) { return idx == new_lb ? new_blk : trow[idx]; };
+  auto table_at = [&](int idx) {
+    if constexpr (kFusable) return idx == new_lb ? new_blk : trow[idx];
+    else return trow[idx];
+  };
   int cur_blk = 0, nxt_blk = 0;  // ids of the current window and of the next one
   if (lb0 + lane < lb_end) cur_blk = clamp_block(table_at(lb0 + lane), num_blocks);
   if (lb_end > lb0) nxt_blk = table_at(min(lb0 + kWinBlocks + lane, lb_end - 1));
@@ -648,19 +674,21 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
 // first (more than 16 partitions) rescale the running sums when the maximum
 // grows. Partitions past the sequence's count hold stale data and are
 // excluded by selection (a zero weight would not cancel a NaN).
-template <typename T, int D>
+template <typename T, int D, bool kArgs>
 __global__ __launch_bounds__(256) void MergeKernel(T* __restrict__ out, const float* __restrict__ ws_acc,
                                                    const float* __restrict__ ws_ml,
                                                    const int32_t* seq_lens_in, int32_t BH,
                                                    int32_t Hq, int32_t max_seq_len, int32_t PT, int32_t P,
-                                                   const StepArgs meta) {
+                                                   const StepArgsOf<kArgs> meta) {
   constexpr int EPL = D / 64;
   constexpr int kChunk = 16;
   const int lane = threadIdx.x & 63;
   const int bh = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
   if (bh >= BH) return;
   const int b = bh / Hq;
-  int L = seq_lens_in != nullptr ? seq_lens_in[b] : meta.lens[b];
+  int L;
+  if constexpr (kArgs) L = meta.lens[b];
+  else L = seq_lens_in[b];
   L = min(max(L, 0), max_seq_len);
   const int Pb = (L + PT - 1) / PT;
   if (Pb <= 1) return;  // written by pass 1
@@ -721,19 +749,34 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   DecodeWorkspace ws = DecodeWorkspaceLayout(a.ws, a.B, a.Hq, a.D, P);
   static const StepArgs kNoStepArgs{};
   const StepArgs& meta = a.step_args != nullptr ? *a.step_args : kNoStepArgs;
-  hipLaunchKernelGGL((DecodeKernel<T, KV, D, G>), dim3(per_xcd * 8), dim3(kThreads), 0, stream,
-                     static_cast<T*>(a.out), static_cast<const T*>(a.q),
-                     static_cast<const KV*>(a.k_cache), static_cast<const KV*>(a.v_cache),
-                     a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
-                     __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
-                     P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),
-                     static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, meta);
+  auto launch = [&](auto kernel, const auto& meta) {
+    hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(kThreads), 0, stream,
+                       static_cast<T*>(a.out), static_cast<const T*>(a.q),
+                       static_cast<const KV*>(a.k_cache), static_cast<const KV*>(a.v_cache),
+                       a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
+                       __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
+                       P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),
+                       static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, meta);
+  };
+  if constexpr (sizeof(KV) == sizeof(T)) {
+    if (a.new_k != nullptr && a.step_args != nullptr) launch(DecodeKernel<T, KV, D, G, true, true>, meta);
+    else if (a.new_k != nullptr) launch(DecodeKernel<T, KV, D, G, true, false>, NoStepArgs{});
+    else launch(DecodeKernel<T, KV, D, G, false, false>, NoStepArgs{});
+  } else {
+    launch(DecodeKernel<T, KV, D, G, false, false>, NoStepArgs{});
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
   const int BH = a.B * a.Hq;
-  hipLaunchKernelGGL((MergeKernel<T, D>), dim3((BH + 3) / 4), dim3(256), 0, stream,
-                     static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, BH, a.Hq, a.max_seq_len,
-                     a.partition_tokens, P, meta);
+  if (a.seq_lens == nullptr) {  // lengths in the launch arguments
+    hipLaunchKernelGGL((MergeKernel<T, D, true>), dim3((BH + 3) / 4), dim3(256), 0, stream,
+                       static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, BH, a.Hq, a.max_seq_len,
+                       a.partition_tokens, P, meta);
+  } else {
+    hipLaunchKernelGGL((MergeKernel<T, D, false>), dim3((BH + 3) / 4), dim3(256), 0, stream,
+                       static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, BH, a.Hq, a.max_seq_len,
+                       a.partition_tokens, P, NoStepArgs{});
+  }
   return hipGetLastError();
 }
 
