@@ -40,6 +40,8 @@
 //    cancel a non-finite value); K rows there are left as loaded, since the
 //    causal mask replaces their scores.
 //  * MFMA operands are read from LDS four MFMAs ahead of their use.
+//  * Wave priority: 0 during the softmax of a tile, 1 otherwise, so that of
+//    the two waves sharing a SIMD the one with MFMAs to issue goes first.
 //  * Online softmax in base 2: the tile max is taken on raw scores, the
 //    scale is folded into one FMA ahead of exp2, and the running max is
 //    raised lazily (only when a tile exceeds it by more than 8), so most
@@ -350,7 +352,14 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
   // ago) and tile j + 2's loads are in flight into the other register set;
   // block ids run one tile further ahead. The loop is unrolled by two so the
   // two register sets keep fixed registers.
+  // Wave priorities: the two waves of a SIMD share its issue slots, and
+  // after each tile's barrier they tend to reach the same phase together.
+  // A wave in its softmax (VALU) phase drops to priority 0, so the SIMD's
+  // other wave issues its MFMAs first and the matrix pipe stays fed while
+  // the VALU work fills the gaps (measured about 2% faster on the 16 x 512
+  // chunk workload with the GPU warmed up, identical results).
   auto compute_tile = [&](int j) {
+    __builtin_amdgcn_s_setprio(1);
     const int buf = j & 1;
     const uint16_t* ks = smem + buf * PG::kBufElems;
     const uint16_t* vt = ks + PG::kKElems;
@@ -387,6 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 
+    __builtin_amdgcn_s_setprio(0);
     // Causal mask where the tile reaches past min_apos; tile max on raw scores.
     const int t0 = j * kKT;
     if (t0 + kKT - 1 > min_apos) {
@@ -432,6 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
           p[2 * tb + hs][e] = static_cast<__bf16>(pe);
         }
 
+    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T · P^T, V operands read kAhead MFMAs ahead.
     constexpr int kPV = PG::kDBlocks * PG::kPSteps;
     auto v_operand = [&](int idx) {
