@@ -183,9 +183,6 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     if (row_valid) v = *reinterpret_cast<const uint4*>(q + row_off + (D / 2) * h2 + 8 * s);
     qf[s] = __builtin_bit_cast(bf16x8v, v);
   }
-  // Let the q loads land now, before any K/V load is in flight: the loop's
-  // wait counting then never has to treat them as pending.
-  __builtin_amdgcn_s_waitcnt(0);
 
   // Keys the workgroup needs: 0 .. kv_end-1 (the last valid row's position).
   const int kv_end = max(0, ctx + min(q0 + QP, nq));
@@ -485,14 +482,25 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
 
   StageRegs sreg_a, sreg_b;
   LoadIds ids_next;
+  // Start-up: the block ids of the first three tiles load together with q,
+  // and one wait covers them all, before any K/V load is in flight (the
+  // loop's wait counting then never has to treat them as pending). Tiles 0
+  // and 1 then load back to back, tile 0 through the register set that the
+  // first iteration refills.
   if (n_tiles > 0) {
-    LoadIds ids0;
-    spread_ids(fetch_ids(0), ids0);
-    load_tile(0, ids0, sreg_a);
-    store_tile(0, sreg_a);
-    spread_ids(fetch_ids(min(1, n_tiles - 1)), ids0);
-    load_tile(min(1, n_tiles - 1), ids0, sreg_a);
-    spread_ids(fetch_ids(min(2, n_tiles - 1)), ids_next);
+    const int raw0 = fetch_ids(0);
+    const int raw1 = fetch_ids(min(1, n_tiles - 1));
+    const int raw2 = fetch_ids(min(2, n_tiles - 1));
+    __builtin_amdgcn_s_waitcnt(0);
+    LoadIds ids0, ids1;
+    spread_ids(raw0, ids0);
+    spread_ids(raw1, ids1);
+    spread_ids(raw2, ids_next);
+    load_tile(0, ids0, sreg_b);
+    load_tile(min(1, n_tiles - 1), ids1, sreg_a);
+    store_tile(0, sreg_b);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
   // Both halves of the pair run unconditionally, so every path into the next
