@@ -31,8 +31,8 @@ import numpy as np
 from .fp8 import decode_e4m3
 
 __all__ = [
-    "widen", "widen_kv", "gather_sequence", "attend", "paged_decode", "paged_decode_one",
-    "paged_prefill", "partial_state", "merge_partials",
+    "widen", "widen_kv", "gather_sequence", "attend", "paged_decode", "paged_prefill",
+    "paged_prefill_masked", "partial_state", "merge_partials",
 ]
 
 
@@ -89,15 +89,6 @@ def _gqa_group(Hq: int, Hkv: int) -> int:
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     return Hq // Hkv
-
-
-def paged_decode_one(q_bh: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
-                     table_row: np.ndarray, L: int, kv_head: int, block_size: int,
-                     scale: float, dtype: str):
-    """One (sequence, q head) decode output: (out [D] fp64, lse)."""
-    K = widen(gather_sequence(k_cache, table_row, L, block_size)[:, kv_head, :], dtype)
-    V = widen(gather_sequence(v_cache, table_row, L, block_size)[:, kv_head, :], dtype)
-    return attend(widen(q_bh, dtype), K, V, scale)
 
 
 def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
@@ -163,6 +154,50 @@ def paged_prefill(q: np.ndarray, cu_q_lens: np.ndarray, k_cache: np.ndarray, v_c
                 g = h // G
                 kv = max(pos + 1, 0)   # a row before the cache start sees no keys
                 out[r0 + i, h], lse[r0 + i, h] = attend(qi[h], K[:kv, g, :], V[:kv, g, :], scale)
+    return out, lse
+
+
+def paged_prefill_masked(q: np.ndarray, cu_q_lens: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                         block_tables: np.ndarray, seq_lens: np.ndarray, scale: float, dtype: str):
+    """The same causal chunked prefill as ``paged_prefill``, one matrix per
+    (sequence, q head) instead of one vector per row, so that a whole
+    512-row chunk over thousands of cached tokens is checked in seconds.
+
+    For sequence b with n rows over L cached tokens: gather K_b, V_b through
+    the table (as in decode), S = scale · Q_bh K_gᵀ ([n, L]), set S[i, t] to
+    -inf where t > L - n + i (the causal mask over absolute positions), take
+    the exact two-pass softmax of each row (row max, then exp and sum), and
+    return weights · V_g. A row whose position is negative has every key
+    masked: zero output, lse -inf. Returns (out [T, Hq, D], lse [T, Hq]).
+    """
+    T, Hq, D = q.shape
+    block_size, Hkv = k_cache.shape[1], k_cache.shape[2]
+    G = _gqa_group(Hq, Hkv)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    lse = np.full((T, Hq), -np.inf, dtype=np.float64)
+    for b in range(len(seq_lens)):
+        L = int(seq_lens[b])
+        r0, r1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+        n = r1 - r0
+        if n == 0:
+            continue
+        K = widen(gather_sequence(k_cache, block_tables[b], L, block_size), dtype)
+        V = widen(gather_sequence(v_cache, block_tables[b], L, block_size), dtype)
+        Q = widen(q[r0:r1], dtype)                                   # [n, Hq, D]
+        pos = (L - n) + np.arange(n)                                 # absolute position of each row
+        allowed = np.arange(L)[None, :] <= pos[:, None]              # [n, L]
+        seen = allowed.any(axis=1)                                   # rows with at least one key
+        for h in range(Hq):
+            g = h // G
+            S = scale * (Q[:, h, :] @ K[:, g, :].T)                  # [n, L]
+            S = np.where(allowed, S, -np.inf)
+            m = np.where(seen, S.max(axis=1, initial=-np.inf), 0.0)
+            W = np.exp(S - m[:, None])                               # masked entries give 0
+            den = W.sum(axis=1)
+            num = W @ V[:, g, :]
+            ok = seen & (den > 0)
+            out[r0:r1, h] = np.where(ok[:, None], num / np.where(ok, den, 1.0)[:, None], 0.0)
+            lse[r0:r1, h] = np.where(ok, m + np.log(np.where(ok, den, 1.0)), -np.inf)
     return out, lse
 
 

@@ -66,7 +66,8 @@ def quantize_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
     The quotient is taken in fp32 (NumPy's fp32 division is IEEE
     round-to-nearest-even), clamped to ±448, then rounded to the nearest
     finite E4M3 value; a tie goes to the code with an even mantissa. The sign
-    is kept separately, so -0.0 and tiny negatives give code 0x80.
+    is kept separately, so -0.0 and tiny negatives give code 0x80. A NaN
+    quotient gives the NaN code 0x7F with the input's sign bit.
     """
     x = np.asarray(x, dtype=np.float32)
     q = (x / np.float32(scale)).astype(np.float32)
@@ -80,5 +81,6 @@ def quantize_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
     d_hi = _POS_VALS[hi] - mag
     take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi != lo) & ((_POS_CODES[hi] & 1) == 0))
     code = np.where(take_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
+    code = np.where(np.isnan(q), np.uint8(NAN_CODE), code).astype(np.uint8)
     neg = np.signbit(q)
     return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)

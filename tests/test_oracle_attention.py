@@ -315,6 +315,85 @@ def test_prefill_matches_masked_sdpa(ctx, qlens, Hq, Hkv, D, bs):
             np.testing.assert_allclose(out[cu[b]:cu[b + 1]], ref2, rtol=0, atol=TOL)
 
 
+@pytest.mark.parametrize("ctx,qlens,Hq,Hkv,D,bs", [
+    ([0, 0, 0], [5, 16, 33], 4, 2, 16, 16),
+    ([0, 3, 40, 17], [7, 1, 20, 32], 4, 1, 16, 8),
+    ([64, 0, 9], [12, 40, 0], 6, 3, 8, 32),       # an empty chunk
+])
+def test_prefill_masked_matches_masked_sdpa(ctx, qlens, Hq, Hkv, D, bs):
+    """The matrix form of the causal prefill against the library's masked
+    attention (fp64 SDPA with an explicit boolean mask)."""
+    rng = np.random.default_rng(18)
+    Ks, Vs, q, kp, vp, tables, lens, cu = prefill_case(rng, ctx, qlens, Hq, Hkv, D, bs)
+    out, lse = OA.paged_prefill_masked(q, cu, kp, vp, tables, lens, 0.25, "f32")
+    for b, (c, n) in enumerate(zip(ctx, qlens)):
+        if n == 0:
+            continue
+        L = c + n
+        mask = np.arange(L)[None, :] <= (c + np.arange(n))[:, None]
+        ref = sdpa_masked(q[cu[b]:cu[b + 1]].astype(np.float64), Ks[b].astype(np.float64),
+                          Vs[b].astype(np.float64), 0.25, mask)
+        np.testing.assert_allclose(out[cu[b]:cu[b + 1]], ref, rtol=0, atol=TOL)
+    assert np.all(np.isfinite(lse))
+
+
+def test_prefill_masked_rows_before_cache_start():
+    """A 6-row chunk over a 4-token cache: rows at negative positions see no
+    keys (zero output, lse -inf), the row at position 0 returns V[0], the last
+    row attends to every token (library SDPA, no mask)."""
+    rng = np.random.default_rng(11)
+    Ks, Vs, q, kp, vp, tables, lens, cu = prefill_case(rng, [0], [4], 2, 1, 8, 8)   # L = 4
+    q6 = rng.standard_normal((6, 2, 8)).astype(np.float32)
+    out, lse = OA.paged_prefill_masked(q6, np.array([0, 6]), kp, vp, tables, lens, 0.5, "f32")
+    assert np.array_equal(out[:2], np.zeros((2, 2, 8))) and np.all(lse[:2] == -np.inf)
+    np.testing.assert_array_equal(out[2, :, :], np.repeat(Vs[0][0:1, 0, :].astype(np.float64), 2, 0))
+    ref = sdpa_masked(q6[5:6].astype(np.float64), Ks[0].astype(np.float64), Vs[0].astype(np.float64),
+                      0.5, np.ones((1, 4), bool))
+    np.testing.assert_allclose(out[5], ref[0], rtol=0, atol=TOL)
+
+
+def test_prefill_masked_brute_force():
+    """Pure-Python loops with math.exp over a paged bf16 cache (tables walked
+    by hand, one score at a time) against the matrix form."""
+    rng = np.random.default_rng(19)
+    ctx, qlens, Hq, Hkv, D, bs = [3, 0], [4, 5], 4, 2, 8, 4
+    lens = [c + n for c, n in zip(ctx, qlens)]
+    nb = sum(-(-L // bs) for L in lens) + 2
+    kp = W.draw_values(rng, (nb, bs, Hkv, D), "bf16")
+    vp = W.draw_values(rng, (nb, bs, Hkv, D), "bf16")
+    q = W.draw_values(rng, (sum(qlens), Hq, D), "bf16")
+    perm = rng.permutation(nb)
+    tables = np.full((2, 3), -1, dtype=np.int32)
+    k = 0
+    for b, L in enumerate(lens):
+        for i in range(-(-L // bs)):
+            tables[b, i] = perm[k]
+            k += 1
+    cu = np.concatenate([[0], np.cumsum(qlens)])
+    out, _ = OA.paged_prefill_masked(q, cu, kp, vp, tables, np.array(lens), 0.3, "bf16")
+
+    def val(bits):
+        return float(np.array([int(bits) << 16], dtype=np.uint32).view(np.float32)[0])
+
+    for b, (c, n) in enumerate(zip(ctx, qlens)):
+        L = c + n
+        for i in range(n):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                scores = []
+                for t in range(L - n + i + 1):
+                    blk, off = int(tables[b, t // bs]), t % bs
+                    scores.append(0.3 * sum(val(q[cu[b] + i, h, d]) * val(kp[blk, off, g, d]) for d in range(D)))
+                m = max(scores)
+                w = [math.exp(x - m) for x in scores]
+                for d in range(D):
+                    acc = 0.0
+                    for t, wt in enumerate(w):
+                        blk, off = int(tables[b, t // bs]), t % bs
+                        acc += wt * val(vp[blk, off, g, d])
+                    assert abs(acc / sum(w) - out[cu[b] + i, h, d]) < 1e-12
+
+
 def test_prefill_last_row_equals_decode():
     rng = np.random.default_rng(9)
     Ks, Vs, q, kp, vp, tables, lens, cu = prefill_case(rng, [10, 0, 33], [6, 9, 16], 4, 2, 16, 16)
@@ -371,6 +450,9 @@ def _pins_pass(mod):
         test_decode_matches_unpaged_sdpa(*CASES[1])
         test_paged_decode_api_matches_sdpa_on_f32_data(*CASES[3])
         test_prefill_matches_masked_sdpa([0, 3, 40, 17], [7, 1, 20, 32], 4, 1, 16, 8)
+        test_prefill_masked_matches_masked_sdpa([0, 3, 40, 17], [7, 1, 20, 32], 4, 1, 16, 8)
+        test_prefill_masked_matches_masked_sdpa([64, 0, 9], [12, 40, 0], 6, 3, 8, 32)
+        test_prefill_masked_rows_before_cache_start()
         for s in range(3):
             test_lse_merge_equals_unsplit(s)
         test_decode_brute_force_tiny_workload()
@@ -447,6 +529,45 @@ def _m5(monkeypatch):
                                                           K[:pos, h // G], V[:pos, h // G], scale)
         return out, lse
     monkeypatch.setattr(OA, "paged_prefill", paged_prefill)
+
+
+def _masked_mutant(monkeypatch, allowed_fn, kv_head_fn):
+    """A matrix-form prefill with one planted change: the key mask or the
+    kv head a q head reads."""
+    def paged_prefill_masked(q, cu, kc, vc, bt, sl, scale, dtype):
+        T, Hq, D = q.shape
+        bs, Hkv = kc.shape[1], kc.shape[2]
+        out = np.zeros((T, Hq, D)); lse = np.full((T, Hq), -np.inf)
+        for b in range(len(sl)):
+            L = int(sl[b]); r0, r1 = int(cu[b]), int(cu[b + 1]); n = r1 - r0
+            if n == 0:
+                continue
+            K = OA.widen(OA.gather_sequence(kc, bt[b], L, bs), dtype)
+            V = OA.widen(OA.gather_sequence(vc, bt[b], L, bs), dtype)
+            Q = OA.widen(q[r0:r1], dtype)
+            pos = (L - n) + np.arange(n)
+            allowed = allowed_fn(np.arange(L)[None, :], pos[:, None])
+            for h in range(Hq):
+                g = kv_head_fn(h, Hq, Hkv)
+                S = np.where(allowed, scale * (Q[:, h] @ K[:, g].T), -np.inf)
+                m = S.max(axis=1, initial=-np.inf)
+                m = np.where(np.isfinite(m), m, 0.0)
+                Wt = np.exp(S - m[:, None])
+                den = Wt.sum(axis=1)
+                out[r0:r1, h] = np.where(den[:, None] > 0, (Wt @ V[:, g]) / np.where(den > 0, den, 1)[:, None], 0)
+                lse[r0:r1, h] = np.where(den > 0, m + np.log(np.where(den > 0, den, 1)), -np.inf)
+        return out, lse
+    monkeypatch.setattr(OA, "paged_prefill_masked", paged_prefill_masked)
+
+
+@_mut("matrix-form prefill: causal mask t < pos")
+def _m8(monkeypatch):
+    _masked_mutant(monkeypatch, lambda t, p: t < p, lambda h, Hq, Hkv: h // (Hq // Hkv))
+
+
+@_mut("matrix-form prefill: kv head h % Hkv")
+def _m9(monkeypatch):
+    _masked_mutant(monkeypatch, lambda t, p: t <= p, lambda h, Hq, Hkv: h % Hkv)
 
 
 @_mut("merge without rescaling by exp(m_p - M)")

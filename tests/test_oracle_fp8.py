@@ -68,6 +68,21 @@ def test_quantize_every_bf16_matches_torch():
     assert np.array_equal(F8.quantize_e4m3(x, 1.0), _torch_codes(x))
 
 
+def test_quantize_nan_keeps_nan_and_sign():
+    """Every bf16 NaN pattern (both signs, any payload) gives the NaN code
+    with its sign, as torch's float8_e4m3fn conversion does; clamping must
+    not turn a NaN into ±448."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    x = (bits << np.uint32(16)).view(np.float32)
+    nan = x[np.isnan(x)]
+    assert len(nan) == 2 * 127
+    codes = F8.quantize_e4m3(nan, 1.0)
+    assert np.array_equal(codes, _torch_codes(nan))
+    assert set(codes.tolist()) == {0x7F, 0xFF}
+    assert np.array_equal(codes == 0xFF, np.signbit(nan))
+    assert np.array_equal(F8.quantize_e4m3(nan, 0.0137), codes)
+
+
 @pytest.mark.parametrize("scale", [0.0137, 0.0129, 3.0, 2.0 ** -7])
 def test_quantize_scaled_matches_torch(scale):
     rng = np.random.default_rng(7)
