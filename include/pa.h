@@ -92,7 +92,12 @@ typedef struct {
 /* Pool and host block manager                                               */
 /* ------------------------------------------------------------------------ */
 
-/* Create a pool over caller-owned device buffers k_cache and v_cache, each
+/* Create a pool over caller-owned device buffers k_cache and v_cache: the
+ * fixed-size physical pages and the free-page list the scheduler hands them
+ * out from ("vLLM的'内存分页'到底多神奇", xxqk.cn, §2), each buffer laid out
+ * [num_blocks, block_size, num_kv_heads, head_dim] ("LLM推理优化：技术原理解析
+ * 总览", §3.3), sized by the caller to its memory budget (the budget setting
+ * of the same xxqk.cn page, §4). Each buffer holds
  * layout->num_blocks × block_size × num_kv_heads × head_dim elements of
  * layout->dtype, row-major in that order. free_order (host, may be NULL) is a
  * permutation of [0, num_blocks) giving the order in which free blocks are
@@ -105,7 +110,8 @@ pa_status pa_alloc_pool(const pa_kv_layout* layout, void* k_cache, void* v_cache
                         const int32_t* free_order, pa_pool** out);
 
 /* Destroy a pool handle (host bookkeeping only; device buffers stay the
- * caller's). NULL is ignored. */
+ * caller's). NULL is ignored. Library addition (no passage): the handle's
+ * lifetime. */
 void pa_free_pool(pa_pool* pool);
 
 /* Grow sequence seq_id by n_tokens (creating it if unknown), taking new blocks
@@ -155,7 +161,10 @@ pa_status pa_seq_append_tokens(pa_pool* pool, int64_t seq_id, const int32_t* tok
                                int64_t* slots_out, int32_t* n_cached_out);
 
 /* Prefix-cache counters: blocks holding a registered key (in use or free),
- * full blocks looked up and found since the pool was created. */
+ * full blocks looked up and found since the pool was created (the cache hit
+ * rate the prefix caching of "vLLM 生产级落地深剖", §2, is judged by; the
+ * counters themselves are a library addition). Errors: PA_ERR_INVALID (null
+ * pointers). */
 typedef struct {
   int32_t cached_blocks;
   int64_t lookups;
@@ -191,8 +200,12 @@ pa_status pa_seq_fork(pa_pool* pool, int64_t src_seq_id, int64_t dst_seq_id);
  * PA_ERR_UNKNOWN_SEQ. */
 pa_status pa_seq_free(pa_pool* pool, int64_t seq_id);
 
-/* Export block tables and lengths for n sequences, in the order given by
- * seq_ids (host, n). tables_out (host, n × max_blocks int32, row-major) gets
+/* Export block tables and lengths for n sequences: each sequence's page table
+ * mapping logical page i to its physical page ("vLLM的'内存分页'到底多神奇",
+ * §2), one row per sequence, as the device calls read them. max_blocks, the
+ * row width, bounds the pages one sequence may hold, as the page's
+ * longest-sequence setting does (same page, §3 phase 3). Rows follow the
+ * order given by seq_ids (host, n). tables_out (host, n × max_blocks int32, row-major) gets
  * each sequence's physical block ids, padded with -1; seq_lens_out (host, n
  * int32) gets each length. Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID (a
  * sequence needs more than max_blocks entries, a length above INT32_MAX, or
@@ -200,10 +213,19 @@ pa_status pa_seq_free(pa_pool* pool, int64_t seq_id);
 pa_status pa_block_tables(const pa_pool* pool, const int64_t* seq_ids, int32_t n,
                           int32_t max_blocks, int32_t* tables_out, int32_t* seq_lens_out);
 
-/* Current block accounting into *out (host). */
+/* The geometry the pool was created with (host *out): a binding checks the
+ * shapes and element types of device buffers against it before a call, since
+ * the kernels size every access from it. Library addition (no passage).
+ * Errors: PA_ERR_INVALID (null pointers). */
+pa_status pa_pool_layout(const pa_pool* pool, pa_kv_layout* out);
+
+/* Current block accounting into *out (host): the cache-usage figures the
+ * monitoring of "vLLM的'内存分页'到底多神奇", §5, watches (see
+ * pa_pool_stats_t). Errors: PA_ERR_INVALID (null pointers). */
 pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
 
-/* The pending copy-on-write block copies, in the order they will run:
+/* The pending copy-on-write block copies (the copy a write into a shared page
+ * needs first: "vLLM的'内存分页'到底多神奇", §3 phase 3), in the order they will run:
  * src_out[i] -> dst_out[i] (host, capacity entries each); *n_out receives the
  * count. Errors: PA_ERR_INVALID (null pointers, capacity below the count). */
 pa_status pa_pool_pending_copies(const pa_pool* pool, int32_t* src_out, int32_t* dst_out, int32_t capacity,
@@ -237,7 +259,9 @@ pa_status pa_pool_set_kv_scales(pa_pool* pool, float k_scale, float v_scale);
 pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value,
                       const int64_t* slot_mapping, int32_t T, void* stream);
 
-/* Bytes of device workspace pa_decode needs for this shape: long contexts
+/* Bytes of device workspace pa_decode needs for this shape. Library addition:
+ * the pages' decode walks a sequence's pages in one pass
+ * ("vLLM的'内存分页'到底多神奇", §3 phase 2); here long contexts
  * are split into KV partitions of partition_tokens tokens, and when a
  * sequence spans more than one, the workspace holds the fp32 partial state
  * (max, sum, Σ weight·V) of every (sequence, q head, partition). 0 when one
@@ -277,7 +301,10 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t B, int32_t max_s
 int32_t pa_decode_partition_tokens_for_lengths(const pa_pool* pool, const int32_t* seq_lens_host, int32_t B,
                                                int32_t max_seq_len);
 
-/* Decode attention: one query token per sequence over its paged cache.
+/* Decode attention: one query token per sequence over its paged cache
+ * ("vLLM的'内存分页'到底多神奇", xxqk.cn, §3 phase 2: walk the sequence's page
+ * table, read its pages in logical order, attend; GQA head mapping and the
+ * scale are this library's readings, see the file header).
  * out (device): [B, num_q_heads, head_dim], pool dtype (bf16 for an FP8
  *   pool), written.
  * q (device): [B, num_q_heads, head_dim], pool dtype (bf16 for an FP8 pool).
@@ -410,7 +437,7 @@ typedef struct {
   int32_t pre_max_q_len;
 } pa_step_desc;
 
-/* Enqueue one mixed step on `stream`: pending copy-on-write copies, the
+/* Enqueue one mixed step ("vLLM 生产级落地深剖", §2) on `stream`: pending copy-on-write copies, the
  * scatter, then decode and prefill. When the step has both, the prefill
  * runs on a stream the pool owns (default priority, made on the first such
  * call on the device current then), forked from `stream` after the scatter
@@ -425,7 +452,8 @@ pa_status pa_step(pa_pool* pool, const pa_step_desc* desc, void* stream);
 
 typedef struct pa_step_graph pa_step_graph; /* opaque, library-owned */
 
-/* Capture the launches of one mixed step (pa_step without copies) into an
+/* Capture the launches of one mixed step ("vLLM 生产级落地深剖", §2; the capture
+ * itself is a library addition) (pa_step without copies) into an
  * instantiated HIP graph. Sizes, grid shapes and every pointer in `desc` are
  * frozen; the device buffers they name are read when the graph runs, so the
  * caller updates their contents (new rows, slots, tables, lengths, queries,
@@ -440,17 +468,37 @@ typedef struct pa_step_graph pa_step_graph; /* opaque, library-owned */
  * instantiation failed). */
 pa_status pa_step_graph_create(pa_pool* pool, const pa_step_desc* desc, pa_step_graph** out);
 
-/* Launch the captured step on `stream`, after enqueueing the pool's pending
+/* Launch the captured step ("vLLM 生产级落地深剖", §2: one engine step mixing
+ * prefill and decode) on `stream`, after enqueueing the pool's pending
  * copy-on-write copies (they change from step to step, so they stay outside
  * the graph). Errors: PA_ERR_INVALID (null graph), PA_ERR_HIP. */
 pa_status pa_step_graph_launch(pa_step_graph* graph, void* stream);
 
 /* Release the graph (NULL is ignored). Call it once the graph's launches
- * have completed (synchronise their stream first). */
+ * have completed (synchronise their stream first). Library addition (no
+ * passage): the graph's lifetime. */
 void pa_step_graph_destroy(pa_step_graph* graph);
 
+/* Debug checks of the device calls' integer inputs. Two rows of one scatter
+ * with the same slot race, and a block id outside the pool is undefined (the
+ * pages leave both open: a slot names one place in one page, "vLLM的'内存分页'
+ * 到底多神奇", §3 phase 1; a table maps each logical page to a physical one,
+ * §2). With the checks on, pa_write_kv, pa_decode, pa_append_decode,
+ * pa_append_decode_args, pa_prefill, pa_step and pa_step_graph_create first
+ * copy the slots, block tables and lengths they are given to the host (on
+ * their stream, waiting for the copy: slow, for debugging), and return
+ * PA_ERR_INVALID, launching nothing, when a slot in the pool appears twice
+ * in one call or when a table entry the call reads (logical blocks 0 ..
+ * ceil(L / block_size) - 1 of each row, L clamped as the kernels clamp it;
+ * for a fused append, not the entry the call fills in itself) is not in
+ * [0, num_blocks). enable != 0 turns them on, 0 off, for the whole process;
+ * returns the previous setting. The initial setting is on when the
+ * environment variable PA_DEBUG_CHECKS is set to a value other than "0". */
+int32_t pa_set_debug_checks(int32_t enable);
+
 /* Thread-local text describing the last non-OK status returned on this
- * thread ("" if none). Valid until the next call on this thread. */
+ * thread ("" if none). Valid until the next call on this thread. Library
+ * addition (no passage): error reporting. */
 const char* pa_last_error(void);
 
 #ifdef __cplusplus

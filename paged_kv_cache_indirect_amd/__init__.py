@@ -27,7 +27,7 @@ __all__ = [
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_last_error", "StepDesc", "pa_step",
     "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy", "pa_seq_append_tokens",
     "pa_pool_prefix_stats", "pa_tier_block_size", "pa_decode_partition_tokens", "pa_append_decode",
-    "pa_append_decode_args", "pa_decode_partition_tokens_for_lengths",
+    "pa_append_decode_args", "pa_decode_partition_tokens_for_lengths", "pa_pool_layout", "pa_set_debug_checks",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
@@ -90,6 +90,7 @@ _SIGS = {
     "pa_seq_free": (_i32, [_vp, _i64]),
     "pa_block_tables": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "pa_pool_stats": (_i32, [_vp, ctypes.POINTER(_Stats)]),
+    "pa_pool_layout": (_i32, [_vp, ctypes.POINTER(_Layout)]),
     "pa_pool_pending_copies": (_i32, [_vp, _vp, _vp, _i32, _vp]),
     "pa_write_kv": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -102,6 +103,7 @@ _SIGS = {
     "pa_append_decode_args": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32,
                                      _vp, _sz, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
+    "pa_set_debug_checks": (_i32, [_i32]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -148,12 +150,89 @@ def _dtype_code(t) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+# ------------------------------------------------------- argument checks
+# The library sizes every device access from the pool's layout, so a tensor
+# whose shape or element type disagrees with it would be read or written out
+# of bounds on the device. Each device call checks its tensors here first
+# (shape and dtype, then that they live on a GPU) and raises ValueError.
+
+def pa_pool_layout(pool: int) -> dict:
+    """The pool's geometry: num_blocks, block_size, num_kv_heads, head_dim, dtype."""
+    lay = _Layout()
+    _check(lib.pa_pool_layout(pool, ctypes.byref(lay)), "pa_pool_layout")
+    return {"num_blocks": lay.num_blocks, "block_size": lay.block_size, "num_kv_heads": lay.num_kv_heads,
+            "head_dim": lay.head_dim, "dtype": lay.dtype}
+
+
+def _compute_dtype(layout: dict):
+    """Element type of q, out and K/V rows for a pool: the pool's own, bf16
+    for an FP8 pool."""
+    import torch
+    return {PA_F32: torch.float32, PA_BF16: torch.bfloat16, PA_FP8_E4M3: torch.bfloat16}[layout["dtype"]]
+
+
+def _want(t, name: str, shape, dtype) -> None:
+    """``t`` must be a contiguous tensor of ``dtype`` on a GPU whose shape is
+    ``shape`` (entries None are free)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != len(shape) or any(w is not None and int(g) != w for g, w in zip(t.shape, shape)):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple('*' if w is None else w for w in shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _want_gpu(**named) -> None:
+    """Every given tensor (None skipped) lives on a GPU. Called after the
+    shape and dtype checks of a call."""
+    for name, t in named.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _want_rows(layout: dict, name: str, t, rows=None) -> None:
+    """q / out ([rows, Hq, D]) against the pool: head_dim, element type and
+    a q-head count that is a multiple of the kv heads."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    _want(t, name, (rows, None, layout["head_dim"]), _compute_dtype(layout))
+    if int(t.shape[1]) % layout["num_kv_heads"]:
+        raise ValueError(f"{name}: {int(t.shape[1])} q heads is not a multiple of {layout['num_kv_heads']} kv heads")
+
+
+def _want_kv_rows(layout: dict, name: str, t, rows=None) -> None:
+    """New K/V rows [rows, Hkv, D] for a scatter into the pool."""
+    _want(t, name, (rows, layout["num_kv_heads"], layout["head_dim"]), _compute_dtype(layout))
+
+
+def _want_workspace(t, name: str = "workspace") -> None:
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _want_host(a, name: str, n: int, dtype) -> np.ndarray:
+    """A host array of at least n entries, converted to ``dtype``."""
+    import torch
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError(f"{name} must be a host array")
+        a = a.numpy()
+    arr = np.ascontiguousarray(a, dtype=dtype).reshape(-1)
+    if arr.size < n:
+        raise ValueError(f"{name} needs {n} entries, got {arr.size}")
+    return arr
+
+
 # ------------------------------------------------------------------- pools
 def pa_alloc_pool(k_cache, v_cache, free_order: Optional[Sequence[int]] = None) -> int:
     """Create a pool over k_cache/v_cache (torch device tensors [nb, bs, Hkv, D]).
     Returns the opaque handle (an int)."""
     if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.dim() != 4 or k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache must be matching [num_blocks, block_size, Hkv, D] tensors")
+    if not (k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("k_cache and v_cache must be contiguous GPU tensors")
     nb, bs, hkv, d = (int(x) for x in k_cache.shape)
     layout = _Layout(nb, bs, hkv, d, _dtype_code(k_cache))
     order = None
@@ -244,6 +323,12 @@ def pa_last_error() -> str:
     return lib.pa_last_error().decode(errors="replace")
 
 
+def pa_set_debug_checks(enable: bool) -> bool:
+    """Turn the library's host-side checks of slots and block tables on or
+    off (process-wide); returns the previous setting."""
+    return bool(lib.pa_set_debug_checks(1 if enable else 0))
+
+
 # ------------------------------------------------------------ device ops
 def pa_pool_set_kv_scales(pool: int, k_scale: float, v_scale: float) -> None:
     """Per-tensor scales of an FP8 pool (a code c stands for value(c) * scale)."""
@@ -252,7 +337,13 @@ def pa_pool_set_kv_scales(pool: int, k_scale: float, v_scale: float) -> None:
 
 def pa_write_kv(pool: int, key, value, slot_mapping, stream=None) -> None:
     """key/value: device [T, Hkv, D]; slot_mapping: device int64 [T]."""
+    import torch
+    lay = pa_pool_layout(pool)
+    _want(slot_mapping, "slot_mapping", (None,), torch.int64)
     T = int(slot_mapping.shape[0])
+    _want_kv_rows(lay, "key", key, T)
+    _want_kv_rows(lay, "value", value, T)
+    _want_gpu(key=key, value=value, slot_mapping=slot_mapping)
     _check(lib.pa_write_kv(pool, _dptr(key), _dptr(value), _dptr(slot_mapping), T, _stream(stream)),
            "pa_write_kv")
 
@@ -275,11 +366,28 @@ def pa_decode_partition_tokens_for_lengths(pool: int, seq_lens, max_seq_len: int
                                                           int(max_seq_len)))
 
 
+def _check_decode_args(pool, out, q, block_tables, seq_lens=None, workspace=None) -> dict:
+    """q/out [B, Hq, D] of the pool's compute type, block_tables int32
+    [B, max_blocks], seq_lens int32 [B] (None: lengths on the host)."""
+    import torch
+    lay = pa_pool_layout(pool)
+    _want_rows(lay, "q", q)
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    _want(out, "out", (B, Hq, lay["head_dim"]), q.dtype)
+    _want(block_tables, "block_tables", (B, None), torch.int32)
+    if seq_lens is not None:
+        _want(seq_lens, "seq_lens", (B,), torch.int32)
+    _want_workspace(workspace)
+    _want_gpu(out=out, q=q, block_tables=block_tables, seq_lens=seq_lens, workspace=workspace)
+    return lay
+
+
 def pa_decode(pool: int, out, q, block_tables, seq_lens, scale: float, max_seq_len: int,
               partition_tokens: int = 0, workspace=None, stream=None) -> None:
     """out/q: device [B, Hq, D]; block_tables: device int32 [B, max_blocks];
     seq_lens: device int32 [B]. ``workspace`` (device uint8 tensor) is
     allocated here with torch when not given and needed."""
+    _check_decode_args(pool, out, q, block_tables, seq_lens, workspace)
     B, Hq, D = (int(x) for x in q.shape)
     need = pa_decode_workspace_bytes(B, Hq, D, max_seq_len, partition_tokens)
     if need and workspace is None:
@@ -298,7 +406,13 @@ def pa_append_decode(pool: int, out, q, key, value, slot_mapping, block_tables, 
     key/value: device [B, Hkv, D]; slot_mapping: device int64 [B] (slot of
     sequence b's newest token, or < 0); block_tables: device int32
     [B, max_blocks], whose entry for each new token's block is filled in."""
+    import torch
+    lay = _check_decode_args(pool, out, q, block_tables, seq_lens, workspace)
     B, Hq, D = (int(x) for x in q.shape)
+    _want_kv_rows(lay, "key", key, B)
+    _want_kv_rows(lay, "value", value, B)
+    _want(slot_mapping, "slot_mapping", (B,), torch.int64)
+    _want_gpu(key=key, value=value, slot_mapping=slot_mapping)
     need = pa_decode_workspace_bytes(B, Hq, D, max_seq_len, partition_tokens)
     if need and workspace is None:
         import torch
@@ -316,11 +430,13 @@ def pa_append_decode_args(pool: int, out, q, key, value, slots: np.ndarray, bloc
                           stream=None) -> None:
     """pa_append_decode with the slots (int64 [B]) and lengths (int32 [B])
     given as host arrays, passed in the launch arguments (B <= 128)."""
+    lay = _check_decode_args(pool, out, q, block_tables, None, workspace)
     B, Hq, D = (int(x) for x in q.shape)
-    sl = np.ascontiguousarray(slots, dtype=np.int64).reshape(-1)
-    ln = np.ascontiguousarray(seq_lens, dtype=np.int32).reshape(-1)
-    if sl.size < B or ln.size < B:
-        raise ValueError("slots and seq_lens need B entries")
+    _want_kv_rows(lay, "key", key, B)
+    _want_kv_rows(lay, "value", value, B)
+    sl = _want_host(slots, "slots", B, np.int64)
+    ln = _want_host(seq_lens, "seq_lens", B, np.int32)
+    _want_gpu(key=key, value=value)
     need = pa_decode_workspace_bytes(B, Hq, D, max_seq_len, partition_tokens)
     if need and workspace is None:
         import torch
@@ -336,9 +452,19 @@ def pa_append_decode_args(pool: int, out, q, key, value, slots: np.ndarray, bloc
 def pa_prefill(pool: int, out, q, cu_q_lens, block_tables, seq_lens, scale: float, max_q_len: int,
                stream=None) -> None:
     """out/q: device [T, Hq, D] bf16; cu_q_lens: device int32 [B+1];
-    block_tables: device int32 [B, max_blocks]; seq_lens: device int32 [B]."""
+    block_tables: device int32 [B, max_blocks]; seq_lens: device int32 [B].
+    The rows cu_q_lens names (its last entry) must fit in q and out: that
+    value lives on the device and is not checked here."""
+    import torch
+    lay = pa_pool_layout(pool)
+    _want_rows(lay, "q", q)
+    T, Hq = int(q.shape[0]), int(q.shape[1])
+    _want(out, "out", (T, Hq, lay["head_dim"]), q.dtype)
+    _want(seq_lens, "seq_lens", (None,), torch.int32)
     B = int(seq_lens.shape[0])
-    Hq = int(q.shape[1])
+    _want(cu_q_lens, "cu_q_lens", (B + 1,), torch.int32)
+    _want(block_tables, "block_tables", (B, None), torch.int32)
+    _want_gpu(out=out, q=q, cu_q_lens=cu_q_lens, block_tables=block_tables, seq_lens=seq_lens)
     _check(lib.pa_prefill(pool, _dptr(out), _dptr(q), _dptr(cu_q_lens), _dptr(block_tables),
                           int(block_tables.shape[1]), _dptr(seq_lens), B, Hq, int(max_q_len),
                           float(scale), _stream(stream)),
@@ -363,6 +489,12 @@ class StepDesc:
                  pre_cu_q_lens=None, pre_block_tables=None, pre_seq_lens=None, pre_max_q_len: int = 0):
         self.tensors = [key, value, slot_mapping, dec_out, dec_q, dec_block_tables, dec_seq_lens, workspace,
                         pre_out, pre_q, pre_cu_q_lens, pre_block_tables, pre_seq_lens]
+        self.named = dict(key=key, value=value, slot_mapping=slot_mapping, dec_out=dec_out, dec_q=dec_q,
+                          dec_block_tables=dec_block_tables, dec_seq_lens=dec_seq_lens, workspace=workspace,
+                          pre_out=pre_out, pre_q=pre_q, pre_cu_q_lens=pre_cu_q_lens,
+                          pre_block_tables=pre_block_tables, pre_seq_lens=pre_seq_lens)
+        self.num_q_heads = int(num_q_heads)
+        self.max_blocks = int(max_blocks)
         d = _StepDesc()
         d.key, d.value, d.slot_mapping = _dptr(key), _dptr(value), _dptr(slot_mapping)
         d.num_new_tokens = 0 if slot_mapping is None else int(slot_mapping.shape[0])
@@ -380,11 +512,42 @@ class StepDesc:
         self.c = d
 
 
+def _check_step(pool: int, desc: StepDesc) -> None:
+    """Each part of the step that runs (a non-zero count) against the pool's
+    layout, as pa_write_kv, pa_decode and pa_prefill check theirs."""
+    import torch
+    lay = pa_pool_layout(pool)
+    t = desc.named
+    Hq, mb = desc.num_q_heads, desc.max_blocks
+    if t["slot_mapping"] is not None and int(t["slot_mapping"].shape[0]) > 0:
+        _want(t["slot_mapping"], "slot_mapping", (None,), torch.int64)
+        T = int(t["slot_mapping"].shape[0])
+        _want_kv_rows(lay, "key", t["key"], T)
+        _want_kv_rows(lay, "value", t["value"], T)
+    if t["dec_seq_lens"] is not None and int(t["dec_seq_lens"].shape[0]) > 0:
+        _want(t["dec_seq_lens"], "dec_seq_lens", (None,), torch.int32)
+        B = int(t["dec_seq_lens"].shape[0])
+        _want(t["dec_q"], "dec_q", (B, Hq, lay["head_dim"]), _compute_dtype(lay))
+        _want(t["dec_out"], "dec_out", (B, Hq, lay["head_dim"]), _compute_dtype(lay))
+        _want(t["dec_block_tables"], "dec_block_tables", (B, mb), torch.int32)
+        _want_workspace(t["workspace"])
+    if t["pre_seq_lens"] is not None and int(t["pre_seq_lens"].shape[0]) > 0:
+        _want(t["pre_seq_lens"], "pre_seq_lens", (None,), torch.int32)
+        B = int(t["pre_seq_lens"].shape[0])
+        _want(t["pre_q"], "pre_q", (None, Hq, lay["head_dim"]), _compute_dtype(lay))
+        _want(t["pre_out"], "pre_out", tuple(int(x) for x in t["pre_q"].shape), _compute_dtype(lay))
+        _want(t["pre_cu_q_lens"], "pre_cu_q_lens", (B + 1,), torch.int32)
+        _want(t["pre_block_tables"], "pre_block_tables", (B, mb), torch.int32)
+    _want_gpu(**t)
+
+
 def pa_step(pool: int, desc: StepDesc, stream=None) -> None:
+    _check_step(pool, desc)
     _check(lib.pa_step(pool, ctypes.byref(desc.c), _stream(stream)), "pa_step")
 
 
 def pa_step_graph_create(pool: int, desc: StepDesc) -> int:
+    _check_step(pool, desc)
     g = _vp()
     _check(lib.pa_step_graph_create(pool, ctypes.byref(desc.c), ctypes.byref(g)), "pa_step_graph_create")
     return g.value

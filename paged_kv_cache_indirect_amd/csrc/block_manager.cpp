@@ -125,7 +125,10 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
     *err = "sequence " + std::to_string(*dup) + " appears twice in the batch";
     return kErrInvalid;
   }
-  std::unordered_map<int32_t, int32_t> cow_drops;  // references dropped by copies earlier in the batch
+  // References dropped by copies earlier in the batch, per block (a member
+  // array of num_blocks counters, reset below for the blocks touched).
+  scratch_drop_.resize(ref_.size(), 0);
+  scratch_dropped_.clear();
   int64_t need = 0;
   scratch_grow_.resize(static_cast<size_t>(n));
   for (int32_t i = 0; i < n; ++i) {
@@ -134,6 +137,7 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
     const int64_t old_len = it == seqs_.end() ? 0 : it->second.len;
     const int64_t have = it == seqs_.end() ? 0 : static_cast<int64_t>(it->second.table.size());
     if (old_len + n_tokens > static_cast<int64_t>(INT32_MAX)) {
+      for (int32_t blk : scratch_dropped_) scratch_drop_[static_cast<size_t>(blk)] = 0;
       *err = "sequence length would exceed INT32_MAX";
       return kErrInvalid;
     }
@@ -143,13 +147,15 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
     if (n_tokens > 0 && have > 0 && old_len % block_size_ != 0 &&
         ref_[static_cast<size_t>(it->second.table.back())] > 1) {
       const int32_t last = it->second.table.back();
-      int32_t& dropped = cow_drops[last];
+      int32_t& dropped = scratch_drop_[static_cast<size_t>(last)];
       if (ref_[static_cast<size_t>(last)] - dropped > 1) {
+        if (dropped == 0) scratch_dropped_.push_back(last);
         ++need;
         ++dropped;
       }
     }
   }
+  for (int32_t blk : scratch_dropped_) scratch_drop_[static_cast<size_t>(blk)] = 0;
   if (need > static_cast<int64_t>(free_.size())) {
     *err = "not enough free blocks for the batch: need " + std::to_string(need) + ", have " +
            std::to_string(free_.size());
@@ -159,7 +165,8 @@ Status BlockManager::AppendBatch(const int64_t* seqs, int32_t n, int32_t n_token
   // failure here leaves the pool unchanged apart from empty entries, which
   // are removed again.
   // (Pointers to map entries stay valid while other entries are inserted.)
-  std::vector<int64_t> created;
+  std::vector<int64_t>& created = scratch_created_;
+  created.clear();
   created.reserve(static_cast<size_t>(n));  // so recording a new entry cannot throw
   try {
     for (int32_t i = 0; i < n; ++i) {

@@ -142,6 +142,9 @@ class BlockManager {
   // loop makes no heap allocation in them.
   std::vector<int64_t> scratch_ids_;
   std::vector<Seq*> scratch_grow_;
+  std::vector<int64_t> scratch_created_;  // sequences a batch append created
+  std::vector<int32_t> scratch_drop_;     // per block: copy-on-write references dropped so far in a batch
+  std::vector<int32_t> scratch_dropped_;  // blocks with a non-zero scratch_drop_ entry
   mutable std::vector<const Seq*> scratch_seqs_;
   PrefixStats pstats_;
 };

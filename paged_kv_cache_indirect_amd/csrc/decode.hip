@@ -225,13 +225,19 @@ struct NoStepArgs {};
 template <bool kFused>
 using StepArgsOf = typename std::conditional<kFused, StepArgs, NoStepArgs>::type;
 
+// The pools: read-only for the plain decode; the fused variant also stores
+// each new row into them (through the same pointers: every access to a pool
+// in the kernel goes through its parameter).
+template <bool kFused, typename KV>
+using PoolPtr = typename std::conditional<kFused, KV*, const KV*>::type;
+
 // kFused: the fused-append variant (pa_append_decode*); the plain decode is
 // compiled without that code. kArgs (with kFused): lengths and slots come
 // from the launch arguments (pa_append_decode_args), not device memory.
 template <typename T, typename KV, int D, int G, bool kFused, bool kArgs>
 __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void DecodeKernel(
-    T* __restrict__ out, const T* __restrict__ q, const KV* __restrict__ kc,
-    const KV* __restrict__ vc, const int32_t* tables,
+    T* __restrict__ out, const T* __restrict__ q, PoolPtr<kFused, KV> __restrict__ kc,
+    PoolPtr<kFused, KV> __restrict__ vc, const int32_t* tables,
     const int32_t* seq_lens_in, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int32_t B, int32_t Hkv,
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
@@ -582,8 +588,8 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
         x[h] = sum8(a) * scale_log2;
       }
       if (r == 0) {
-        KV* kd = const_cast<KV*>(kc) + nslot * row_stride + static_cast<int64_t>(g) * D;
-        KV* vd = const_cast<KV*>(vc) + nslot * row_stride + static_cast<int64_t>(g) * D;
+        KV* kd = kc + nslot * row_stride + static_cast<int64_t>(g) * D;
+        KV* vd = vc + nslot * row_stride + static_cast<int64_t>(g) * D;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
           *reinterpret_cast<uint4*>(kd + (j + kLanesPerRow * i) * EPC) = kx[i];
@@ -752,7 +758,7 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   auto launch = [&](auto kernel, const auto& meta) {
     hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(kThreads), 0, stream,
                        static_cast<T*>(a.out), static_cast<const T*>(a.q),
-                       static_cast<const KV*>(a.k_cache), static_cast<const KV*>(a.v_cache),
+                       static_cast<KV*>(a.k_cache), static_cast<KV*>(a.v_cache),
                        a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
                        __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
                        P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),

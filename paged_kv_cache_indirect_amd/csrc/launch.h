@@ -44,8 +44,8 @@ struct StepArgs {
 struct DecodeArgs {
   void* out;
   const void* q;
-  const void* k_cache;
-  const void* v_cache;
+  void* k_cache;      // written only by the fused append (new rows)
+  void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* ws;           // workspace (DecodeWorkspaceLayout); null when num_partitions == 1

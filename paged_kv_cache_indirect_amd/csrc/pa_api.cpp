@@ -5,11 +5,15 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "block_manager.h"
 #include "launch.h"
@@ -104,6 +108,115 @@ pa_status CheckHeads(const pa_pool* pool, int32_t Hq, int32_t* G) {
   if (*G != 1 && *G != 2 && *G != 4 && *G != 8)
     return Fail(PA_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads must be 1, 2, 4 or 8");
   return PA_OK;
+}
+
+// ------------------------------------------------------------ debug checks
+// Duplicate slots in one scatter and block ids outside the pool are undefined
+// behaviour for the kernels (they race, or read a clamped block). With debug
+// checks on (pa_set_debug_checks, or PA_DEBUG_CHECKS=1 in the environment when
+// the library first looks), device calls copy the slots, tables and lengths
+// they are given to the host, wait for the copy, and reject such input with
+// PA_ERR_INVALID before anything is launched.
+std::atomic<int> g_debug{-1};  // -1: not read from the environment yet
+
+bool DebugChecks() {
+  int v = g_debug.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("PA_DEBUG_CHECKS");
+    v = (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    if (!g_debug.compare_exchange_strong(expected, v)) v = expected;
+  }
+  return v != 0;
+}
+
+// n elements of device memory into *h, ordered after the work on `st`.
+template <typename T>
+pa_status DebugToHost(std::vector<T>* h, const T* d, size_t n, hipStream_t st) {
+  h->resize(n);
+  if (n == 0) return PA_OK;
+  pa_status s = FromHip(hipMemcpyAsync(h->data(), d, n * sizeof(T), hipMemcpyDeviceToHost, st), "debug check copy");
+  if (s == PA_OK) s = FromHip(hipStreamSynchronize(st), "debug check copy");
+  return s;
+}
+
+// Slots (host values) in the pool: no slot may appear twice.
+pa_status DebugCheckSlotsUnique(const pa_pool& pool, const std::vector<int64_t>& slots) {
+  const int64_t num_slots = static_cast<int64_t>(pool.layout.num_blocks) * pool.layout.block_size;
+  std::vector<int64_t> live;
+  live.reserve(slots.size());
+  for (int64_t x : slots)
+    if (x >= 0 && x < num_slots) live.push_back(x);
+  std::sort(live.begin(), live.end());
+  const auto dup = std::adjacent_find(live.begin(), live.end());
+  if (dup != live.end())
+    return Fail(PA_ERR_INVALID, "debug check: slot " + std::to_string(*dup) + " is written twice in one call");
+  return PA_OK;
+}
+
+// Table entries a call reads: for row b, logical blocks [0, ceil(L_b / bs))
+// with L_b clamped into [0, len_cap] as the kernels clamp it, must name a
+// block of the pool. new_slots (host, may be empty): a fused append fills in
+// the entry of row b's newest token itself when new_slots[b] is in the pool,
+// so that entry is not checked.
+pa_status DebugCheckTables(const pa_pool& pool, const int32_t* tables_dev, int32_t max_blocks,
+                           const std::vector<int32_t>& lens, int64_t len_cap,
+                           const std::vector<int64_t>& new_slots, hipStream_t st) {
+  const int32_t B = static_cast<int32_t>(lens.size());
+  if (B == 0) return PA_OK;
+  std::vector<int32_t> tab;
+  pa_status s = DebugToHost(&tab, tables_dev, static_cast<size_t>(B) * max_blocks, st);
+  if (s != PA_OK) return s;
+  const int64_t bs = pool.layout.block_size;
+  const int64_t num_slots = static_cast<int64_t>(pool.layout.num_blocks) * bs;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t L = std::min<int64_t>(std::max<int64_t>(lens[static_cast<size_t>(b)], 0), len_cap);
+    const int64_t nblk = std::min<int64_t>((L + bs - 1) / bs, max_blocks);
+    const bool fills = b < static_cast<int32_t>(new_slots.size()) && L > 0 &&
+                       new_slots[static_cast<size_t>(b)] >= 0 && new_slots[static_cast<size_t>(b)] < num_slots;
+    for (int64_t i = 0; i < nblk; ++i) {
+      if (fills && i == (L - 1) / bs) continue;
+      const int32_t id = tab[static_cast<size_t>(b) * max_blocks + static_cast<size_t>(i)];
+      if (id < 0 || id >= pool.layout.num_blocks)
+        return Fail(PA_ERR_INVALID, "debug check: block_tables[" + std::to_string(b) + "][" + std::to_string(i) +
+                                        "] = " + std::to_string(id) + " is not a block of the pool");
+    }
+  }
+  return PA_OK;
+}
+
+pa_status DebugCheckWrite(const pa_pool& pool, const int64_t* slots_dev, int32_t T, hipStream_t st) {
+  std::vector<int64_t> slots;
+  pa_status s = DebugToHost(&slots, slots_dev, static_cast<size_t>(std::max(T, 0)), st);
+  return s != PA_OK ? s : DebugCheckSlotsUnique(pool, slots);
+}
+
+// A decode call's tables. lens_dev or lens_host gives the lengths;
+// slots_dev or slots_host the fused append's slots (both null: plain decode).
+pa_status DebugCheckDecode(const pa_pool& pool, const pa::DecodeArgs& a, const int32_t* lens_host,
+                           const int64_t* slots_dev, const int64_t* slots_host, hipStream_t st) {
+  std::vector<int32_t> lens;
+  pa_status s = PA_OK;
+  if (lens_host) lens.assign(lens_host, lens_host + a.B);
+  else s = DebugToHost(&lens, a.seq_lens, static_cast<size_t>(a.B), st);
+  if (s != PA_OK) return s;
+  std::vector<int64_t> slots;
+  if (slots_host) slots.assign(slots_host, slots_host + a.B);
+  else if (slots_dev) s = DebugToHost(&slots, slots_dev, static_cast<size_t>(a.B), st);
+  if (s != PA_OK) return s;
+  if (!slots.empty()) {
+    s = DebugCheckSlotsUnique(pool, slots);
+    if (s != PA_OK) return s;
+  }
+  return DebugCheckTables(pool, a.block_tables, a.max_blocks, lens, a.max_seq_len, slots, st);
+}
+
+pa_status DebugCheckPrefill(const pa_pool& pool, const pa::PrefillArgs& a, hipStream_t st) {
+  std::vector<int32_t> lens;
+  pa_status s = DebugToHost(&lens, a.seq_lens, static_cast<size_t>(a.B), st);
+  if (s != PA_OK) return s;
+  return DebugCheckTables(pool, a.block_tables, a.max_blocks, lens,
+                          static_cast<int64_t>(a.max_blocks) * a.block_size, {}, st);
 }
 
 // ---------------------------------------------------------------- device ops
@@ -291,6 +404,16 @@ pa_status PrepareStep(const pa_pool& pool, const pa_step_desc& d, StepPlan* plan
                         &plan->run_pre);
 }
 
+// Debug checks of every part of a step (slots of the scatter, tables of the
+// decode and of the prefill).
+pa_status DebugCheckStep(const pa_pool& pool, const StepPlan& plan, hipStream_t st) {
+  pa_status s = PA_OK;
+  if (plan.write.T > 0) s = DebugCheckWrite(pool, plan.write.slots, plan.write.T, st);
+  if (s == PA_OK && plan.run_dec) s = DebugCheckDecode(pool, plan.dec, nullptr, nullptr, nullptr, st);
+  if (s == PA_OK && plan.run_pre) s = DebugCheckPrefill(pool, plan.pre, st);
+  return s;
+}
+
 // The pool's side stream and fork/join events, made on first use.
 pa_status EnsureSideStream(pa_pool* pool) {
   if (pool->side) return PA_OK;
@@ -345,6 +468,12 @@ pa_status EnqueueStep(const pa_pool& pool, const StepPlan& plan, hipStream_t st)
 extern "C" {
 
 const char* pa_last_error(void) { return g_error.c_str(); }
+
+int32_t pa_set_debug_checks(int32_t enable) {
+  const bool was = DebugChecks();
+  g_debug.store(enable ? 1 : 0, std::memory_order_relaxed);
+  return was ? 1 : 0;
+}
 
 pa_status pa_alloc_pool(const pa_kv_layout* layout, void* k_cache, void* v_cache,
                         const int32_t* free_order, pa_pool** out) {
@@ -432,6 +561,12 @@ pa_status pa_block_tables(const pa_pool* pool, const int64_t* seq_ids, int32_t n
   });
 }
 
+pa_status pa_pool_layout(const pa_pool* pool, pa_kv_layout* out) {
+  if (!pool || !out) return Fail(PA_ERR_INVALID, "null argument");
+  *out = pool->layout;
+  return PA_OK;
+}
+
 pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out) {
   return Guard([&]() -> pa_status {
     if (!pool || !out) return Fail(PA_ERR_INVALID, "null argument");
@@ -483,6 +618,10 @@ pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value, const i
     pa_status s = CheckWrite(*pool, w);
     if (s != PA_OK) return s;
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (DebugChecks() && T > 0) {
+      s = DebugCheckWrite(*pool, slot_mapping, T, st);
+      if (s != PA_OK) return s;
+    }
     s = FlushCopies(pool, st);
     if (s != PA_OK) return s;
     return EnqueueWrite(*pool, w, st);
@@ -519,10 +658,15 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
     if (!pool) return Fail(PA_ERR_INVALID, "null pool");
     pa::DecodeArgs a{};
     bool run = false;
-    const pa_status s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens, B, num_q_heads, scale,
-                                      max_seq_len, partition_tokens, workspace, workspace_bytes, &a, &run);
+    pa_status s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens, B, num_q_heads, scale,
+                                max_seq_len, partition_tokens, workspace, workspace_bytes, &a, &run);
     if (s != PA_OK || !run) return s;
-    return FromHip(pa::LaunchDecode(a, static_cast<hipStream_t>(stream)), "decode launch");
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (DebugChecks()) {
+      s = DebugCheckDecode(*pool, a, nullptr, nullptr, nullptr, st);
+      if (s != PA_OK) return s;
+    }
+    return FromHip(pa::LaunchDecode(a, st), "decode launch");
   });
 }
 
@@ -545,6 +689,10 @@ pa_status pa_append_decode(pa_pool* pool, void* out, const void* q, const void* 
       if (!Aligned16(key) || !Aligned16(value)) return Fail(PA_ERR_INVALID, "key and value must be 16-byte aligned");
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (run && DebugChecks()) {
+      s = DebugCheckDecode(*pool, a, nullptr, slot_mapping, nullptr, st);
+      if (s != PA_OK) return s;
+    }
     s = FlushCopies(pool, st);
     if (s != PA_OK || !run) return s;
     a.new_k = key;
@@ -580,6 +728,10 @@ pa_status pa_append_decode_args(pa_pool* pool, void* out, const void* q, const v
       if (!Aligned16(key) || !Aligned16(value)) return Fail(PA_ERR_INVALID, "key and value must be 16-byte aligned");
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (run && DebugChecks()) {
+      s = DebugCheckDecode(*pool, a, seq_lens_host, nullptr, slot_mapping_host, st);
+      if (s != PA_OK) return s;
+    }
     s = FlushCopies(pool, st);
     if (s != PA_OK || !run) return s;
     pa::StepArgs args{};
@@ -604,10 +756,15 @@ pa_status pa_prefill(pa_pool* pool, void* out, const void* q, const int32_t* cu_
     if (!pool) return Fail(PA_ERR_INVALID, "null pool");
     pa::PrefillArgs a{};
     bool run = false;
-    const pa_status s = PreparePrefill(*pool, out, q, cu_q_lens, block_tables, max_blocks, seq_lens, B,
-                                       num_q_heads, max_q_len, scale, &a, &run);
+    pa_status s = PreparePrefill(*pool, out, q, cu_q_lens, block_tables, max_blocks, seq_lens, B,
+                                 num_q_heads, max_q_len, scale, &a, &run);
     if (s != PA_OK || !run) return s;
-    return FromHip(pa::LaunchPrefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (DebugChecks()) {
+      s = DebugCheckPrefill(*pool, a, st);
+      if (s != PA_OK) return s;
+    }
+    return FromHip(pa::LaunchPrefill(a, st), "prefill launch");
   });
 }
 
@@ -618,6 +775,10 @@ pa_status pa_step(pa_pool* pool, const pa_step_desc* desc, void* stream) {
     pa_status s = PrepareStep(*pool, *desc, &plan);
     if (s != PA_OK) return s;
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (DebugChecks()) {
+      s = DebugCheckStep(*pool, plan, st);
+      if (s != PA_OK) return s;
+    }
     if (plan.run_dec && plan.run_pre) {
       s = EnsureSideStream(pool);
       if (s != PA_OK) return s;
@@ -636,6 +797,10 @@ pa_status pa_step_graph_create(pa_pool* pool, const pa_step_desc* desc, pa_step_
     StepPlan plan;
     pa_status s = PrepareStep(*pool, *desc, &plan);
     if (s != PA_OK) return s;
+    if (DebugChecks()) {   // the buffers' contents at capture time
+      s = DebugCheckStep(*pool, plan, nullptr);
+      if (s != PA_OK) return s;
+    }
     if (plan.run_dec && plan.run_pre) {
       s = EnsureSideStream(pool);
       if (s != PA_OK) return s;

@@ -63,17 +63,31 @@ hipError_t LaunchCopyBlocks(void* k_cache, void* v_cache, const BlockCopyList& l
 // the input row) into one 16-byte chunk of E4M3 codes, for K and for V.
 // Per element: fp32 quotient x / scale (IEEE division, round to nearest
 // even), clamp to ±448, then the hardware conversion (round to nearest even).
+// A NaN quotient is not clamped (fmaxf would return the bound): its code is
+// the E4M3 NaN, 0x7F with the input's sign bit.
+__device__ __forceinline__ float clamp_e4m3(float q) {
+  return q != q ? q : fminf(fmaxf(q, -448.f), 448.f);
+}
+
 __device__ __forceinline__ uint32_t quantize4_e4m3(uint32_t w0, uint32_t w1, float scale) {
   const float x0 = __uint_as_float(w0 << 16), x1 = __uint_as_float(w0 & 0xFFFF0000u);
   const float x2 = __uint_as_float(w1 << 16), x3 = __uint_as_float(w1 & 0xFFFF0000u);
-  const float lim = 448.f;
-  const float q0 = fminf(fmaxf(x0 / scale, -lim), lim);
-  const float q1 = fminf(fmaxf(x1 / scale, -lim), lim);
-  const float q2 = fminf(fmaxf(x2 / scale, -lim), lim);
-  const float q3 = fminf(fmaxf(x3 / scale, -lim), lim);
+  const float q0 = clamp_e4m3(x0 / scale);
+  const float q1 = clamp_e4m3(x1 / scale);
+  const float q2 = clamp_e4m3(x2 / scale);
+  const float q3 = clamp_e4m3(x3 / scale);
   int r = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);  // bytes 0, 1
   r = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, r, true);        // bytes 2, 3
-  return static_cast<uint32_t>(r);
+  uint32_t codes = static_cast<uint32_t>(r);
+  const uint32_t nan_bytes = (q0 != q0 ? 0x000000FFu : 0u) | (q1 != q1 ? 0x0000FF00u : 0u) |
+                             (q2 != q2 ? 0x00FF0000u : 0u) | (q3 != q3 ? 0xFF000000u : 0u);
+  if (nan_bytes) {
+    // bf16 sign bits (bits 15 and 31 of each word) become bit 7 of their byte.
+    const uint32_t signs = ((w0 >> 8) & 0x80u) | ((w0 >> 16) & 0x8000u) |
+                           (((w1 >> 8) & 0x80u) << 16) | (((w1 >> 16) & 0x8000u) << 16);
+    codes = (codes & ~nan_bytes) | ((0x7F7F7F7Fu | signs) & nan_bytes);
+  }
+  return codes;
 }
 
 __device__ __forceinline__ uint4 quantize16_e4m3(const uint4& a, const uint4& b, float scale) {

@@ -12,7 +12,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (pa_alloc_pool, pa_block_tables, pa_decode, pa_decode_workspace_bytes, pa_free_pool,
+from paged_kv_cache_indirect_amd import (pa_alloc_pool, pa_block_tables, pa_decode, pa_decode_workspace_bytes, pa_free_pool,
                pa_pool_set_kv_scales, pa_prefill, pa_seq_append, pa_seq_append_tokens, pa_seq_fork, pa_seq_free,
                pa_write_kv)
 
@@ -152,7 +152,7 @@ class MixedRunner:
     """
 
     def __init__(self, wl, device="cuda", use_graph: bool = False, partition_tokens: int = 0):
-        from . import StepDesc
+        from paged_kv_cache_indirect_amd import StepDesc
         p = wl.plan
         self.wl, self.device, self.use_graph = wl, device, use_graph
         self.Bd, self.Bp, self.chunk = p["Bd"], p["Bp"], p["chunk"]
@@ -250,7 +250,7 @@ class MixedRunner:
 
     def launch(self, stream=None) -> None:
         """The device side of a prepared step: pa_step, or the captured graph."""
-        from . import pa_step, pa_step_graph_create, pa_step_graph_launch
+        from paged_kv_cache_indirect_amd import pa_step, pa_step_graph_create, pa_step_graph_launch
         if not self.use_graph:
             pa_step(self.pool, self.desc, stream)
             return
@@ -260,7 +260,7 @@ class MixedRunner:
         pa_step_graph_launch(self.graph, stream)
 
     def close(self) -> None:
-        from . import pa_step_graph_destroy
+        from paged_kv_cache_indirect_amd import pa_step_graph_destroy
         torch.cuda.synchronize()
         if self.graph is not None:
             pa_step_graph_destroy(self.graph)

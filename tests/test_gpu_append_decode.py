@@ -42,7 +42,8 @@ def _bits(t):
 
 
 def run_case(wl, steps, pt, skip=(), host_args=False):
-    from paged_kv_cache_indirect_amd import (harness, pa_append_decode, pa_append_decode_args, pa_block_tables,
+    from tests import harness
+    from paged_kv_cache_indirect_amd import (pa_append_decode, pa_append_decode_args, pa_block_tables,
                                              pa_decode, pa_seq_append_batch, pa_write_kv)
     print(f"[case] {wl.name} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} bs={wl.block_size} {wl.dtype} "
           f"steps={steps} pt={pt} skip={list(skip)} host_args={host_args}", flush=True)
@@ -160,7 +161,7 @@ def test_append_decode_gqa8b_full(host_args):
 
 def test_append_decode_rejects_fp8_pool():
     import paged_kv_cache_indirect_amd as pa
-    from paged_kv_cache_indirect_amd import harness
+    from tests import harness
     wl = W.make_decode("fp8_small", [20, 40], Hq=8, Hkv=2, D=128, block_size=16, dtype="bf16", seed=3,
                        kv_dtype="fp8", k_scale=0.02, v_scale=0.02)
     cache = harness.GpuCache(wl)

@@ -32,7 +32,7 @@ def _pa():
 
 
 def _harness():
-    from paged_kv_cache_indirect_amd import harness
+    from tests import harness
     return harness
 
 
@@ -77,9 +77,11 @@ def quantize_on_gpu(values_f32, k_scale, v_scale):
 def test_quantize_every_bf16_value_scale_one():
     u = np.arange(65536, dtype=np.uint32)
     f = (u << 16).view(np.float32)
-    keep = ~np.isnan(f) & ((np.abs(f) >= np.float32(1.2e-38)) | (f == 0))   # fp32 subnormals left out
+    # every bf16 value except fp32 subnormals; NaNs of both signs included
+    keep = np.isnan(f) | (np.abs(f) >= np.float32(1.2e-38)) | (f == 0)
     x = f[keep]
-    print(f"[fp8 quantize] {len(x)} bf16 values, scale 1", flush=True)
+    assert np.isnan(x).sum() == 254
+    print(f"[fp8 quantize] {len(x)} bf16 values (NaNs included), scale 1", flush=True)
     kq, vq, xin = quantize_on_gpu(x, 1.0, 1.0)
     ref = F8.quantize_e4m3(xin, 1.0)
     bad = np.nonzero(kq != ref)[0]

@@ -7,8 +7,8 @@ bar (max-abs <= 2e-2, mean-abs <= 2e-3):
 * small ragged shapes: chunk lengths that are not multiples of the query tile,
   contexts of 0 and past several KV tiles, block_size 8/16/32, G in {1,2,4,8},
   D in {64,128}, an empty chunk;
-* the full 16 x 512-row workload over U[0,7680] cached tokens on sampled rows
-  (first/last rows of query tiles, random rows);
+* the full 16 x 512-row workload over U[0,7680] cached tokens, every row and
+  head;
 * rows before the cache start (chunk longer than the cache) are zero;
 * the last row of each chunk equals GPU decode at the same cache length.
 """
@@ -27,7 +27,7 @@ MAX_ABS, MEAN_ABS = 2e-2, 2e-3
 
 
 def _h():
-    from paged_kv_cache_indirect_amd import harness
+    from tests import harness
     return harness
 
 
@@ -73,21 +73,22 @@ def test_prefill_small_shapes(ctx, qlens, Hq, Hkv, D, bs):
     gpu.close()
 
 
-def test_prefill_full_workload_sampled_rows():
+def test_prefill_full_workload_all_rows():
+    """Every row and head of the 16 x 512-row chunk workload over U[0,7680]
+    cached tokens, against the oracle's matrix form of the same causal
+    attention; a sample of rows also against its row-by-row form."""
     wl = W.config("prefill")
     gpu, ora = build(wl)
     got = OA.widen(_h().to_host(gpu.prefill(), "bf16"), "bf16")
-    rng = np.random.default_rng(3)
-    rows = []
-    for b in range(wl.B):
-        n = int(wl.q_lens[b])
-        pick = {0, 1, 31, 32, 63, 64, 255, n - 1} | set(rng.integers(0, n, 4).tolist())
-        rows += [(b, i) for i in sorted(pick) if i < n]
-    ref, _ = OA.paged_prefill(wl.queries(), wl.cu_q_lens(), ora.k_cache, ora.v_cache, ora.block_tables,
-                              ora.seq_lens, wl.scale, "bf16", rows=rows)
+    ref, _ = OA.paged_prefill_masked(wl.queries(), wl.cu_q_lens(), ora.k_cache, ora.v_cache, ora.block_tables,
+                                     ora.seq_lens, wl.scale, "bf16")
+    assert_close(got, ref, f"prefill full workload, all {got.shape[0]} rows x {got.shape[1]} heads")
+    rows = [(b, i) for b in (0, wl.B - 1) for i in (0, 63, 64, int(wl.q_lens[b]) - 1)]
+    ref_rows, _ = OA.paged_prefill(wl.queries(), wl.cu_q_lens(), ora.k_cache, ora.v_cache, ora.block_tables,
+                                   ora.seq_lens, wl.scale, "bf16", rows=rows)
     cu = wl.cu_q_lens()
     idx = [cu[b] + i for b, i in rows]
-    assert_close(got[idx], ref[idx], f"prefill full workload, {len(idx)} sampled rows")
+    np.testing.assert_allclose(ref[idx], ref_rows[idx], rtol=0, atol=1e-12)
     gpu.close()
 
 

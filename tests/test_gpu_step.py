@@ -24,7 +24,7 @@ from oracle.cache import OracleCache  # noqa: E402
 
 
 def _harness():
-    from paged_kv_cache_indirect_amd import harness
+    from tests import harness
     return harness
 
 
