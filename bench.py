@@ -164,7 +164,8 @@ def run_decode(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import (harness, pa_append_decode_args, pa_block_tables, pa_decode,
+    from tests import harness
+    from paged_kv_cache_indirect_amd import (pa_append_decode_args, pa_block_tables, pa_decode,
                                              pa_decode_partition_tokens, pa_decode_partition_tokens_for_lengths,
                                              pa_decode_workspace_bytes, pa_seq_append_batch, pa_write_kv)
 
@@ -316,7 +317,7 @@ def run_decode_fp8(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import harness
+    from tests import harness
 
     dev = torch.device("cuda:0")
     from paged_kv_cache_indirect_amd import pa_decode_partition_tokens
@@ -365,7 +366,8 @@ def run_decode_skewed(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import (harness, pa_append_decode_args, pa_decode_partition_tokens,
+    from tests import harness
+    from paged_kv_cache_indirect_amd import (pa_append_decode_args, pa_decode_partition_tokens,
                                              pa_decode_partition_tokens_for_lengths)
 
     wl = W.make_decode("skewed", [512] * 63 + [32768], Hq=32, Hkv=8, D=128, block_size=16, dtype="bf16", seed=77)
@@ -429,7 +431,7 @@ def run_mixed(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import harness
+    from tests import harness
 
     wl = W.config("mixed")
     p = wl.plan
@@ -484,7 +486,8 @@ def run_prefix_cache(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import (harness, pa_alloc_pool, pa_decode_partition_tokens, pa_free_pool,
+    from tests import harness
+    from paged_kv_cache_indirect_amd import (pa_alloc_pool, pa_decode_partition_tokens, pa_free_pool,
                                              pa_pool_prefix_stats,
                                              pa_pool_stats, pa_seq_append, pa_seq_append_tokens)
 
@@ -551,7 +554,8 @@ def run_tiered(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import harness, pa_pool_stats, pa_tier_block_size
+    from tests import harness
+    from paged_kv_cache_indirect_amd import pa_pool_stats, pa_tier_block_size
 
     out = {}
     for name in ("gqa8b", "long"):
@@ -614,7 +618,8 @@ def run_prefill(args):
     import torch
 
     import workloads as W
-    from paged_kv_cache_indirect_amd import PaError, harness
+    from tests import harness
+    from paged_kv_cache_indirect_amd import PaError
 
     dev = torch.device("cuda:0")
     wl = W.config("prefill")
