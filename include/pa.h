@@ -334,6 +334,29 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
                     float scale, int32_t max_seq_len, int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Size of the device scratch pa_decode_static keeps its partial states in. */
+#define PA_DECODE_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, kernels and output as pa_decode, without the workspace
+ * arguments. The split-KV partial states go to a scratch array of
+ * PA_DECODE_STATIC_SCRATCH_BYTES bytes that the library holds in each GPU's
+ * memory for the life of the process (a static device array; its address on
+ * a device is resolved once, when a pool is created or on the first call on
+ * that device). This call allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine. Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents (each call writes every partial state
+ * before it reads it, so nothing needs clearing): calls that overlap on one
+ * GPU (different streams, or several threads) race and must be serialised
+ * by the caller. Errors: those of pa_decode; PA_ERR_UNSUPPORTED when the
+ * partial states of this shape (B × num_q_heads × partitions × (head_dim + 2)
+ * × 4 bytes, partitions = ceil(max_seq_len / partition_tokens), 0 when one
+ * partition covers max_seq_len) exceed PA_DECODE_STATIC_SCRATCH_BYTES. */
+pa_status pa_decode_static(pa_pool* pool, void* out, const void* q, const int32_t* block_tables,
+                           int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t num_q_heads,
+                           float scale, int32_t max_seq_len, int32_t partition_tokens, void* stream);
+
 /* One decode step with the append fused in: the effect of pa_write_kv with
  * T = B followed by pa_decode, in one launch (plus the log-sum-exp pass).
  * The pages place a generated token's K/V in its page, then attend over the

@@ -28,10 +28,12 @@ __all__ = [
     "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy", "pa_seq_append_tokens",
     "pa_pool_prefix_stats", "pa_tier_block_size", "pa_decode_partition_tokens", "pa_append_decode",
     "pa_append_decode_args", "pa_decode_partition_tokens_for_lengths", "pa_pool_layout", "pa_set_debug_checks",
+    "pa_decode_static", "PA_DECODE_STATIC_SCRATCH_BYTES",
 ]
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NO_BLOCKS, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_UNKNOWN_SEQ = 0, -1, -2, -3, -4, -5
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_DECODE_STATIC_SCRATCH_BYTES = 32 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
@@ -104,6 +106,7 @@ _SIGS = {
                                      _vp, _sz, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_set_debug_checks": (_i32, [_i32]),
+    "pa_decode_static": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _i32, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -398,6 +401,19 @@ def pa_decode(pool: int, out, q, block_tables, seq_lens, scale: float, max_seq_l
                          _dptr(seq_lens), B, Hq, float(scale), int(max_seq_len), int(partition_tokens),
                          _dptr(workspace), ws_bytes, _stream(stream)),
            "pa_decode")
+
+
+def pa_decode_static(pool: int, out, q, block_tables, seq_lens, scale: float, max_seq_len: int,
+                     partition_tokens: int = 0, stream=None) -> None:
+    """pa_decode with the partial states in the library's static device
+    scratch: no workspace argument, and nothing is allocated (here or in the
+    library). Calls that overlap on one GPU share that scratch and race."""
+    _check_decode_args(pool, out, q, block_tables, seq_lens)
+    B, Hq, _ = (int(x) for x in q.shape)
+    _check(lib.pa_decode_static(pool, _dptr(out), _dptr(q), _dptr(block_tables), int(block_tables.shape[1]),
+                                _dptr(seq_lens), B, Hq, float(scale), int(max_seq_len), int(partition_tokens),
+                                _stream(stream)),
+           "pa_decode_static")
 
 
 def pa_append_decode(pool: int, out, q, key, value, slot_mapping, block_tables, seq_lens, scale: float,

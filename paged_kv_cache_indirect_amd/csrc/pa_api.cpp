@@ -11,12 +11,21 @@
 #include <cstdlib>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
 
 #include "block_manager.h"
 #include "launch.h"
+
+// Device memory of pa_decode_static: the split-KV partial states of one
+// decode call, for callers that cannot allocate. Each GPU the library runs on
+// holds its own copy of this array until the process ends. Host code never
+// uses the array's name as an address (on the host it is only a stand-in):
+// it takes each device's address once with hipGetSymbolAddress, with that
+// device current, and passes that pointer on.
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_STATIC_SCRATCH_BYTES];
 
 struct pa_pool {
   pa_kv_layout layout;
@@ -107,6 +116,31 @@ pa_status CheckHeads(const pa_pool* pool, int32_t Hq, int32_t* G) {
   *G = Hq / Hkv;
   if (*G != 1 && *G != 2 && *G != 4 && *G != 8)
     return Fail(PA_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads must be 1, 2, 4 or 8");
+  return PA_OK;
+}
+
+// ------------------------------------------------------ static scratch
+// Per-device address of `scratch`, resolved once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The address of `scratch` on the current device, resolving it on the first
+// call there (hipGetSymbolAddress; no allocation by this library).
+pa_status StaticScratch(void** out) {
+  int dev = -1;
+  pa_status s = FromHip(hipGetDevice(&dev), "hipGetDevice");
+  if (s != PA_OK) return s;
+  if (dev < 0 || dev >= kMaxDevices) return Fail(PA_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    s = FromHip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (s != PA_OK) return s;
+    if (!p) return Fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return PA_OK;
 }
 
@@ -487,6 +521,12 @@ pa_status pa_alloc_pool(const pa_kv_layout* layout, void* k_cache, void* v_cache
     if (pa::BlockManager::Validate(layout->num_blocks, layout->block_size, free_order, &err) != pa::kOk)
       return Fail(PA_ERR_INVALID, err);
     *out = new pa_pool(*layout, k_cache, v_cache, free_order);
+    // Set-up of pa_decode_static's scratch on the current device. Best
+    // effort: without a usable device (host-only use of the block manager)
+    // the address is resolved on that entry point's first call instead.
+    void* ignored = nullptr;
+    const std::string keep = g_error;
+    if (StaticScratch(&ignored) != PA_OK) g_error = keep;
     return PA_OK;
   });
 }
@@ -660,6 +700,42 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
     bool run = false;
     pa_status s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens, B, num_q_heads, scale,
                                 max_seq_len, partition_tokens, workspace, workspace_bytes, &a, &run);
+    if (s != PA_OK || !run) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (DebugChecks()) {
+      s = DebugCheckDecode(*pool, a, nullptr, nullptr, nullptr, st);
+      if (s != PA_OK) return s;
+    }
+    return FromHip(pa::LaunchDecode(a, st), "decode launch");
+  });
+}
+
+pa_status pa_decode_static(pa_pool* pool, void* out, const void* q, const int32_t* block_tables,
+                           int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t num_q_heads,
+                           float scale, int32_t max_seq_len, int32_t partition_tokens, void* stream) {
+  return Guard([&]() -> pa_status {
+    if (!pool) return Fail(PA_ERR_INVALID, "null pool");
+    if (B < 0 || num_q_heads <= 0 || max_seq_len < 0 || partition_tokens < 0)
+      return Fail(PA_ERR_INVALID, "negative size argument");
+    const pa_kv_layout& l = pool->layout;
+    const int32_t pt = partition_tokens == 0 ? pa::DecodeDefaultPartition(B, l.num_kv_heads, max_seq_len,
+                                                                            l.dtype == PA_FP8_E4M3)
+                                             : partition_tokens;
+    if (pt > 0) {
+      const size_t need = pa::DecodeWorkspaceBytes(B, num_q_heads, l.head_dim, pa::DecodePartitions(max_seq_len, pt));
+      if (need > PA_DECODE_STATIC_SCRATCH_BYTES)
+        return Fail(PA_ERR_UNSUPPORTED, "pa_decode_static: the partial states need " + std::to_string(need) +
+                                            " bytes, more than its " +
+                                            std::to_string(PA_DECODE_STATIC_SCRATCH_BYTES) +
+                                            "-byte scratch (use longer partitions or pa_decode)");
+    }
+    void* ws = nullptr;
+    pa_status s = B > 0 ? StaticScratch(&ws) : PA_OK;
+    if (s != PA_OK) return s;
+    pa::DecodeArgs a{};
+    bool run = false;
+    s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens, B, num_q_heads, scale, max_seq_len, pt,
+                      ws, PA_DECODE_STATIC_SCRATCH_BYTES, &a, &run);
     if (s != PA_OK || !run) return s;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (DebugChecks()) {
