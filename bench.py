@@ -57,11 +57,13 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode KV GB/s and % of HBM peak; decode tok/s at batch 64, 8B shape"
 HBM_PEAK_GBPS = 8000.0
-EVENT_EVERY = 4   # decode-step event pairs on every 4th timed step (each pair costs stream time)
+SAMPLE_STEPS = 60   # decode steps after the timed region, each between its own event pair
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "device_common.h", "launch.h"],
+    "decode_fp8": ["decode.hip", "device_common.h", "launch.h"],
+    "decode_prefix": ["decode.hip", "device_common.h", "launch.h"],
     "prefill": ["prefill.hip", "device_common.h", "launch.h"],
 }
 
@@ -121,6 +123,53 @@ def settle(fn, seconds: float) -> None:
         torch.cuda.synchronize()
 
 
+def time_calls(fn, n: int, stream) -> dict:
+    """Time ``fn`` (one call of the op on ``stream``) two ways: n calls each
+    between its own pair of fence-free HIP events (per-call samples: mean,
+    median, min), then n calls back to back between one pair (the average
+    time per call when the GPU runs them in a row, launch gaps included)."""
+    import numpy as np
+    import torch
+    e0 = [TimingEvent() for _ in range(n)]
+    e1 = [TimingEvent() for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        e0[i].record(stream)
+        fn()
+        e1[i].record(stream)
+    r0, r1 = TimingEvent(), TimingEvent()
+    r0.record(stream)
+    for _ in range(n):
+        fn()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in zip(e0, e1)]) * 1e3
+    return {"calls": n, "us_mean": float(us.mean()), "us_median": float(np.median(us)), "us_min": float(us.min()),
+            "us_back_to_back": r0.elapsed_time(r1) * 1e3 / n}
+
+
+def blas_info() -> dict:
+    """Thread count and vendor of the BLAS NumPy uses (the oracle's matmuls)."""
+    import numpy as np
+    info = {"threads": 1, "blas": "unknown"}
+    try:
+        from threadpoolctl import threadpool_info
+        pools = threadpool_info()
+        info["threads"] = max([1] + [int(i.get("num_threads", 1)) for i in pools])
+        blas = [i for i in pools if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+    except Exception:
+        pass
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        info["numpy_blas"] = f"{b.get('name')} {b.get('version')}"
+    except Exception:
+        pass
+    return info
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -171,7 +220,9 @@ def run_decode(args):
 
     dev = torch.device("cuda:0")
     wl = W.config("gqa8b")
-    S = args.warmup + args.steps
+    # warm-up steps, the timed steps, then SAMPLE_STEPS more steps each
+    # between its own event pair (per-launch median and min)
+    S = args.warmup + args.steps + SAMPLE_STEPS
     log(f"[bench] building gqa8b cache: B={wl.B} nb={wl.num_blocks} max_len={wl.max_seq_len}")
     cache = harness.GpuCache(wl, device=dev, poison=False)
     pool = cache.pool
@@ -197,12 +248,14 @@ def run_decode(args):
 
     seq_ids = np.arange(B, dtype=np.int64)
     stream = torch.cuda.current_stream()
-    # HIP events around the decode call on every EVENT_EVERY-th timed step:
-    # a pair costs about 6 us of stream time in the fused step, which the
-    # other steps then run without.
-    timed_events = {s for s in range(args.warmup, S) if (s - args.warmup) % EVENT_EVERY == 0}
+    # The timed steps run without events in between (one fence-free pair
+    # brackets the whole region); the sample steps after them each have a
+    # pair around the decode call.
+    t_end = args.warmup + args.steps
+    timed_events = set(range(t_end, S))
     ev_dec0 = {s: TimingEvent() for s in timed_events}
     ev_dec1 = {s: TimingEvent() for s in timed_events}
+    region0, region1 = TimingEvent(), TimingEvent()
     lens_per_step = []
     ring = 2
 
@@ -270,26 +323,33 @@ def run_decode(args):
     torch.cuda.synchronize()
     log(f"[bench] warm-up done ({args.warmup} steps); timing {args.steps} steps")
     t0 = time.perf_counter()
-    for s in range(args.warmup, S):
+    region0.record(stream)
+    for s in range(args.warmup, t_end):
         step(s)
+    region1.record(stream)
     host_s = time.perf_counter() - t0          # host side of the steps (launches are asynchronous)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed decode steps done: {elapsed * 1e3:.2f} ms (host {host_s * 1e3:.2f} ms)")
+    for s in range(t_end, S):
+        step(s)
+    torch.cuda.synchronize()
 
-    timed = range(args.warmup, S)
+    timed = range(args.warmup, t_end)
     sampled = sorted(timed_events)
     dec_ms = [ev_dec0[s].elapsed_time(ev_dec1[s]) for s in sampled]
-    step_bytes = [decode_bytes(wl, lens_per_step[s]) for s in sampled]
-    step_kv = [int(np.asarray(lens_per_step[s], np.int64).sum()) * Hkv * D * 2 * wl.elem_bytes for s in timed]
-    dec_avg_s = float(np.mean(dec_ms)) * 1e-3
-    achieved = float(np.mean(step_bytes)) / dec_avg_s / 1e9
+    step_bytes = [decode_bytes(wl, lens_per_step[s]) for s in timed]
+    step_kv = [int(np.asarray(lens_per_step[s], np.int64).sum()) * Hkv * D * 2 * wl.elem_bytes
+               for s in timed]
+    region_us = region0.elapsed_time(region1) * 1e3 / args.steps   # GPU time per step, steps back to back
+    achieved = float(np.mean(step_bytes)) / (region_us * 1e-6) / 1e9
     res = {
         "elapsed_s": elapsed,
         "ms_per_step": elapsed * 1e3 / args.steps,
         "host_us_per_step": host_s * 1e6 / args.steps,
         "value": sum(step_kv) / elapsed / 1e9,
         "tok_per_s": B * args.steps / elapsed,
+        "region_us_per_launch": region_us,
         "event_samples": len(dec_ms),
         "decode_us_mean": float(np.mean(dec_ms)) * 1e3,
         "decode_us_median": float(np.median(dec_ms)) * 1e3,
@@ -307,6 +367,80 @@ def run_decode(args):
     del cache, k_steps, v_steps, q_steps, workspace
     torch.cuda.empty_cache()
     return wl, res
+
+
+# ------------------------------------------------------------ every config
+def oracle_decode_seconds(wl, min_seconds: float = 1.0):
+    """The oracle's fp64 paged decode of the whole batch on this host (cache
+    built first, not timed), repeated until ``min_seconds`` have passed;
+    returns (seconds per batch, repetitions)."""
+    import oracle.attention as OA
+    from oracle.cache import OracleCache
+    ora = OracleCache(wl, poison=False)
+    q = wl.queries()
+    reps, total = 0, 0.0
+    while reps == 0 or total < min_seconds:
+        t0 = time.perf_counter()
+        OA.paged_decode(q, ora.k_cache, ora.v_cache, ora.block_tables, ora.seq_lens, wl.scale, wl.dtype)
+        total += time.perf_counter() - t0
+        reps += 1
+    return total / reps, reps
+
+
+def run_configs(args):
+    """The decode configurations, each as configured: the tiny fp32 batch
+    (latency), the 8B-shaped batch as a plain read-only pa_decode in the
+    library's partition, the long-context batch in 512-token partitions and
+    in the library's partition, and the shared-prefix batch (logical and
+    unique K/V bytes). Each GPU figure is over at least 50 calls; each config
+    also times the CPU oracle on the same batch once (``--no-cpu-baseline``
+    skips those)."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from tests import harness
+    from paged_kv_cache_indirect_amd import pa_decode_partition_tokens
+
+    n = max(50, args.config_calls)
+    stream = torch.cuda.current_stream()
+    out = {}
+    plan = [("C1_tiny", "tiny", [0]), ("C2_gqa8b", "gqa8b", [0]), ("C3_long", "long", [512, 0]),
+            ("C4_prefix", "prefix", [0])]
+    for key, name, pts in plan:
+        wl = W.config(name)
+        log(f"[bench] config {key}: B={wl.B} max_len={wl.max_seq_len} {wl.dtype}")
+        cache = harness.GpuCache(wl, poison=False)
+        nbytes = decode_bytes(wl, wl.seq_lens)
+        res = {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "block_size": wl.block_size,
+               "dtype": wl.dtype, "seed": wl.seed, "mean_len": float(np.mean(wl.seq_lens)),
+               "bytes_per_call": nbytes, "kv_bytes": wl.kv_bytes()}
+        if wl.prefix_len:
+            res["unique_kv_bytes"] = wl.unique_kv_bytes()
+        for pt in pts:
+            ws = cache.workspace_for(pt)
+            settle(lambda: cache.decode(pt, ws), 0.05)
+            t = time_calls(lambda: cache.decode(pt, ws), n, stream)
+            used = pt or pa_decode_partition_tokens(cache.pool, wl.B, wl.max_seq_len)
+            sec = t["us_back_to_back"] * 1e-6
+            leg = dict(t, partition_tokens=used, gbps=nbytes / sec / 1e9,
+                       frac=nbytes / sec / 1e9 / HBM_PEAK_GBPS, tok_per_s=wl.B / sec)
+            if wl.prefix_len:
+                leg["unique_gbps"] = wl.unique_kv_bytes() / sec / 1e9
+            res["partition_" + ("default" if pt == 0 else str(pt))] = leg
+            log(f"[bench]   pt {used}: {t['us_back_to_back']:.1f} us/call back to back, "
+                f"{t['us_median']:.1f} us median per call, {leg['gbps']:.0f} GB/s")
+        cache.close()
+        del cache
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            sec, reps = oracle_decode_seconds(wl, 0.5)
+            res["cpu_oracle"] = {"seconds_per_batch": sec, "repetitions": reps, "gbps": nbytes / sec / 1e9,
+                                 "tok_per_s": wl.B / sec, **blas_info()}
+            log(f"[bench]   cpu oracle: {sec:.2f} s per batch")
+        wl.drop_cached()
+        out[key] = res
+    return out
 
 
 # ----------------------------------------------------------------- FP8 decode
@@ -329,31 +463,22 @@ def run_decode_fp8(args):
     pt_used = pt or pa_decode_partition_tokens(cache.pool, wl.B, wl.max_seq_len)
     ws = cache.workspace_for(pt)
     settle(lambda: cache.decode(pt, ws), 0.05)
-    n = args.steps
-    e0 = [TimingEvent() for _ in range(n)]
-    e1 = [TimingEvent() for _ in range(n)]
     stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    for i in range(n):
-        e0[i].record(stream)
-        cache.decode(pt, ws)
-        e1[i].record(stream)
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in zip(e0, e1)]
-    t = float(np.mean(ms)) * 1e-3
+    tm = time_calls(lambda: cache.decode(pt, ws), max(50, args.config_calls), stream)
+    t = tm["us_back_to_back"] * 1e-6
     nbytes = decode_bytes(wl, wl.seq_lens)
     gbps = nbytes / t / 1e9
     cache.close()
-    log(f"[bench] fp8 decode: {t * 1e6:.1f} us, {gbps:.0f} GB/s")
+    log(f"[bench] fp8 decode: {t * 1e6:.1f} us back to back, {gbps:.0f} GB/s")
     return {
         "workload": "8B-shaped GQA decode over an FP8 (OCP E4M3) pool: batch 64, 32 q / 8 kv heads, "
                     "head_dim 128, bf16 q/out, block_size 16, lengths U[512,4096] (seed 1006), "
                     "per-tensor scales k 0.0137 / v 0.0129",
-        "partition_tokens": pt_used,
-        "us_mean": t * 1e6, "us_median": float(np.median(ms)) * 1e3, "us_min": float(np.min(ms)) * 1e3,
+        "partition_tokens": pt_used, **tm,
         "tok_per_s": wl.B / t,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "bytes_per_launch": nbytes},
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("decode_fp8"),
+                     "bytes_per_launch": nbytes},
     }
 
 
@@ -631,33 +756,41 @@ def run_prefill(args):
         cache.close()
         return wl, {"status": f"unavailable: {e}"}
     torch.cuda.synchronize()
-    n = args.prefill_iters
+    n = max(50, args.prefill_iters)
     settle(cache.prefill, 0.1)
-    e0 = [TimingEvent() for _ in range(n)]
-    e1 = [TimingEvent() for _ in range(n)]
     stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    for i in range(n):
-        e0[i].record(stream)
-        cache.prefill()
-        e1[i].record(stream)
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in zip(e0, e1)]
+    tm = time_calls(cache.prefill, n, stream)
     flops = causal_flops(wl)
-    t = float(np.mean(ms)) * 1e-3
+    t = tm["us_back_to_back"] * 1e-6
     tflops = flops / t / 1e12
     cache.close()
-    log(f"[bench] prefill: {t * 1e6:.1f} us, {tflops:.1f} TFLOP/s")
+    log(f"[bench] prefill: {t * 1e6:.1f} us back to back, {tm['us_median']:.1f} us median per call, "
+        f"{tflops:.1f} TFLOP/s")
     traffic = measured_traffic("prefill")
-    return wl, {
+    res = {
         "workload": "16 x 512-token causal chunks over paged context U[0,7680] (seed 1004), "
                     "Hq 32 / Hkv 8, D 128, bf16, block_size 32",
-        "us_mean": t * 1e6, "us_median": float(np.median(ms)) * 1e3, "us_min": float(np.min(ms)) * 1e3,
+        "calls": n, "us_back_to_back": tm["us_back_to_back"], "us_mean": tm["us_mean"],
+        "us_median": tm["us_median"], "us_min": tm["us_min"],
         "tokens_per_s": int(wl.q_lens.sum()) / t,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
                      "flops_per_launch": flops},
     }
+    if not args.no_cpu_baseline:
+        import oracle.attention as OA
+        from oracle.cache import OracleCache
+        ora = OracleCache(wl, poison=False)
+        t0 = time.perf_counter()
+        OA.paged_prefill_masked(wl.queries(), wl.cu_q_lens(), ora.k_cache, ora.v_cache, ora.block_tables,
+                                ora.seq_lens, wl.scale, wl.dtype)
+        sec = time.perf_counter() - t0
+        res["cpu_oracle"] = {"seconds": sec, "gflops": flops / sec / 1e9, **blas_info(),
+                             "what": "oracle's matrix-form fp64 causal prefill of the whole workload, once"}
+        log(f"[bench] prefill cpu oracle: {sec:.1f} s ({flops / sec / 1e9:.1f} GFLOP/s)")
+        del ora
+    wl.drop_cached()
+    return wl, res
 
 
 # --------------------------------------------------------------- CPU oracle
@@ -688,8 +821,10 @@ def run_cpu_baseline(args, wl):
         reps += 1
         log(f"[bench] cpu baseline rep {reps}: {t_total:.1f} s")
     t = t_total / reps
+    info = blas_info()
     return {
-        "value": kv / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "value": kv / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle", "blas": info.get("blas"),
+        "numpy_blas": info.get("numpy_blas"),
         "sample": f"full 64-sequence decode batch (one step, mean length {float(ora.seq_lens.mean()):.0f}), "
                   f"fp64 NumPy gather + exact softmax attention, {reps} repetition(s), {t:.2f} s each; "
                   f"host has {len(os.sched_getaffinity(0))} cores available",
@@ -707,7 +842,11 @@ def main() -> int:
                     help="decode step as pa_write_kv + whole-table upload + pa_decode (default: pa_append_decode_args)")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="KV partition of the decode legs (0: the library's choice, pa_decode_partition_tokens)")
-    ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--prefill-iters", type=int, default=50, help="prefill calls timed (at least 50)")
+    ap.add_argument("--config-calls", type=int, default=50, help="calls timed per config leg (at least 50)")
+    ap.add_argument("--legs", default="all",
+                    help="comma list of legs to run besides the headline decode step: configs, prefill, fp8, "
+                         "mixed, extras, cpu (default all)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -743,17 +882,37 @@ def main() -> int:
         del src, dst
         torch.cuda.empty_cache()
 
+    legs = {"configs", "prefill", "fp8", "mixed", "extras", "cpu"} if args.legs == "all" else \
+        set(x.strip() for x in args.legs.split(",") if x.strip())
+    if args.no_prefill:
+        legs.discard("prefill")
+    if args.no_fp8:
+        legs.discard("fp8")
+    if args.no_mixed:
+        legs.discard("mixed")
+    if args.no_extras:
+        legs.discard("extras")
+    if args.no_cpu_baseline:
+        legs.discard("cpu")
+    args.no_cpu_baseline = "cpu" not in legs
+
     wl, dec = run_decode(args)
     frac = dec["achieved_gbps"] / HBM_PEAK_GBPS
-    log(f"[bench] decode: {dec['decode_us_mean']:.1f} us/launch, {dec['achieved_gbps']:.0f} GB/s "
+    log(f"[bench] decode: {dec['region_us_per_launch']:.1f} us/launch back to back "
+        f"({dec['decode_us_median']:.1f} us median per launch), {dec['achieved_gbps']:.0f} GB/s "
         f"({100 * frac:.1f}% of HBM peak); step {dec['ms_per_step'] * 1e3:.1f} us")
-    pre = None if args.no_prefill else run_prefill(args)[1]
-    fp8 = None if args.no_fp8 else run_decode_fp8(args)
-    mixed = None if args.no_mixed else run_mixed(args)
-    pcache = None if args.no_extras else run_prefix_cache(args)
-    tiers = None if args.no_extras else run_tiered(args)
-    skewed = None if args.no_extras else run_decode_skewed(args)
-    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, wl)
+    configs = run_configs(args) if "configs" in legs else None
+    pre = run_prefill(args)[1] if "prefill" in legs else None
+    if configs is not None and pre is not None:
+        configs["C5_prefill"] = {k: v for k, v in pre.items() if k != "roofline"}
+        configs["C5_prefill"]["frac"] = pre["roofline"]["frac"]
+        configs["C5_prefill"]["tflops"] = pre["roofline"]["achieved"]
+    fp8 = run_decode_fp8(args) if "fp8" in legs else None
+    mixed = run_mixed(args) if "mixed" in legs else None
+    pcache = run_prefix_cache(args) if "extras" in legs else None
+    tiers = run_tiered(args) if "extras" in legs else None
+    skewed = run_decode_skewed(args) if "extras" in legs else None
+    cpu = run_cpu_baseline(args, wl) if "cpu" in legs else None
 
     line = {
         "metric": METRIC,
@@ -782,11 +941,12 @@ def main() -> int:
         "decode": {
             "tok_per_s": dec["tok_per_s"],
             "tok_per_s_8b_32_layers": dec["tok_per_s"] / 32.0,
-            "kernel_us_mean": dec["decode_us_mean"],
-            "kernel_us_median": dec["decode_us_median"],
-            "kernel_us_min": dec["decode_us_min"],
-            "kv_gbps_kernel": dec["kv_bytes_per_step"] / (dec["decode_us_mean"] * 1e-6) / 1e9,
+            "launch_us_back_to_back": dec["region_us_per_launch"],
+            "launch_us_mean": dec["decode_us_mean"],
+            "launch_us_median": dec["decode_us_median"],
+            "launch_us_min": dec["decode_us_min"],
             "event_timed_launches": dec["event_samples"],
+            "kv_gbps_kernel": dec["kv_bytes_per_step"] / (dec["region_us_per_launch"] * 1e-6) / 1e9,
             "host_us_per_step": dec["host_us_per_step"],
         },
         "roofline": {
@@ -801,8 +961,11 @@ def main() -> int:
                        "fused append + paged decode (DecodeKernel with the step's new rows; log-sum-exp "
                        "MergeKernel only for sequences split into partitions)"),
             "bytes_per_launch": dec["bytes_per_launch"],
+            "timing": "timed steps back to back between one pair of fence-free HIP events on the launch "
+                      "stream; achieved = algorithmic bytes per launch / (region time / steps)",
         },
         "cpu_baseline": cpu,
+        "configs": configs,
         "prefill": pre,
         "decode_fp8": fp8,
         "mixed_step": mixed,
