@@ -219,10 +219,15 @@ def run_decode(args):
                                              pa_decode_workspace_bytes, pa_seq_append_batch, pa_write_kv)
 
     dev = torch.device("cuda:0")
-    wl = W.config("gqa8b")
     # warm-up steps, the timed steps, then SAMPLE_STEPS more steps each
     # between its own event pair (per-launch median and min)
     S = args.warmup + args.steps + SAMPLE_STEPS
+    # The 8B-shaped batch (same lengths, values and queries), its shuffled
+    # pool sized at 1.1x the blocks the sequences need after all S steps.
+    base = W.config("gqa8b")
+    need = sum(-(-(int(L) + S) // base.block_size) for L in base.seq_lens)
+    wl = W.make_decode("gqa8b", base.seq_lens, Hq=base.Hq, Hkv=base.Hkv, D=base.D, block_size=base.block_size,
+                       dtype=base.dtype, seed=base.seed, num_blocks=-(-11 * need // 10))
     log(f"[bench] building gqa8b cache: B={wl.B} nb={wl.num_blocks} max_len={wl.max_seq_len}")
     cache = harness.GpuCache(wl, device=dev, poison=False)
     pool = cache.pool

@@ -90,14 +90,14 @@ void BlockManager::Grow(Seq& s, int32_t n, int64_t* slots_out) {
   if (cow) {  // the shared, partly filled last block: this sequence writes into its own copy
     const int32_t old_blk = s.table.back();
     const int32_t blk = PopFree();
-    ++ref_[static_cast<size_t>(blk)];
-    --ref_[static_cast<size_t>(old_blk)];
+    AddRef(blk);
+    DropRef(old_blk);
     s.table.back() = blk;
     pending_.emplace_back(old_blk, blk);
   }
   for (int64_t i = 0; i < tail; ++i) {
     const int32_t blk = PopFree();
-    ++ref_[static_cast<size_t>(blk)];
+    AddRef(blk);
     s.table.push_back(blk);
   }
   s.len = new_len;
@@ -202,7 +202,7 @@ Status BlockManager::Fork(int64_t src, int64_t dst, std::string* err) {
     return kErrInvalid;
   }
   Seq copy = it->second;  // may throw before any mutation
-  for (int32_t blk : copy.table) ++ref_[static_cast<size_t>(blk)];
+  for (int32_t blk : copy.table) AddRef(blk);
   seqs_.emplace(dst, std::move(copy));
   return kOk;
 }
@@ -216,7 +216,7 @@ Status BlockManager::Free(int64_t seq, std::string* err) {
   // free_ never exceeds num_blocks_ entries: reserve once so push_back cannot throw.
   free_.reserve(static_cast<size_t>(num_blocks_));
   for (int32_t blk : it->second.table) {
-    if (--ref_[static_cast<size_t>(blk)] == 0) {
+    if (DropRef(blk) == 0) {
       // A pending copy into this block stays: a later copy may read the
       // block, and the scatter that follows the copies overwrites whatever
       // rows a new owner gets.
@@ -275,9 +275,9 @@ PoolStats BlockManager::Stats() const {
   for (int32_t b = 0; b < num_blocks_; ++b) {
     int32_t r = ref_[static_cast<size_t>(b)];
     if (r > 0) ++st.used_blocks;
-    if (r > 1) ++st.shared_blocks;
     st.filled_slots += fill[static_cast<size_t>(b)];
   }
+  st.shared_blocks = shared_count_;
   st.free_blocks = static_cast<int32_t>(free_.size());
   st.allocated_slots = static_cast<int64_t>(st.used_blocks) * bs;
   return st;
@@ -417,14 +417,14 @@ Status BlockManager::AppendTokens(int64_t seq, const int32_t* tokens, int32_t n,
   for (const Planned& f : full)
     if (f.hit >= 0) {
       if (ref_[static_cast<size_t>(f.hit)] == 0) TakeFree(f.hit);
-      ++ref_[static_cast<size_t>(f.hit)];
+      AddRef(f.hit);
     }
   // (2) the copy-on-write block
   if (cow) {
     const int32_t old_blk = s.table.back();
     const int32_t blk = PopFree();
-    ++ref_[static_cast<size_t>(blk)];
-    --ref_[static_cast<size_t>(old_blk)];
+    AddRef(blk);
+    DropRef(old_blk);
     s.table.back() = blk;
     pending_.emplace_back(old_blk, blk);
   }
@@ -441,12 +441,12 @@ Status BlockManager::AppendTokens(int64_t seq, const int32_t* tokens, int32_t n,
       continue;
     }
     const int32_t blk = PopFree();
-    ++ref_[static_cast<size_t>(blk)];
+    AddRef(blk);
     s.table.push_back(blk);
   }
   if (rem > 0) {
     const int32_t blk = PopFree();
-    ++ref_[static_cast<size_t>(blk)];
+    AddRef(blk);
     s.table.push_back(blk);
   }
   // registration of the blocks this call filled

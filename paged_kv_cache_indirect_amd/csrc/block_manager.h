@@ -78,6 +78,9 @@ class BlockManager {
   int32_t num_blocks() const { return num_blocks_; }
   int32_t block_size() const { return block_size_; }
   int32_t refcount(int32_t blk) const { return ref_[blk]; }
+  // Blocks with more than one reference (shared prefixes, forks), kept up to
+  // date by every reference change.
+  int32_t shared_blocks() const { return shared_count_; }
   int32_t free_count() const { return static_cast<int32_t>(free_.size()); }
 
   // Block copies (src, dst) recorded by copy-on-write appends, in order.
@@ -129,6 +132,17 @@ class BlockManager {
   void Grow(Seq& s, int32_t n, int64_t* slots_out);
   // Takes a given (cached) block off the free list.
   void TakeFree(int32_t blk);
+  // One more / one fewer reference to blk; keeps shared_count_. DropRef
+  // returns the new count.
+  void AddRef(int32_t blk) {
+    if (++ref_[static_cast<size_t>(blk)] == 2) ++shared_count_;
+  }
+  int32_t DropRef(int32_t blk) {
+    const int32_t r = --ref_[static_cast<size_t>(blk)];
+    if (r == 1) --shared_count_;
+    return r;
+  }
+  int32_t shared_count_ = 0;
   int32_t num_blocks_;
   int32_t block_size_;
   std::vector<int32_t> free_;  // stack: back() is the next block handed out

@@ -211,6 +211,24 @@ struct Widen<Fp8E4M3> {
   }
 };
 
+// One 16-byte chunk of a cached K/V row. kStream: loaded non-temporally.
+// Decode reads each K/V byte once, so streamed rows should not displace what
+// stays useful in the caches (block ids, queries, partial states); measured
+// on MI355X on the 8B-shaped batch, 112.3 -> 99.7 us per launch. A pool with
+// shared blocks (a prefix that many sequences read) uses ordinary loads, so
+// the shared rows stay in L2 for the sequences that read them next (the
+// shared-prefix batch: 116.7 us streamed, 112.5 us with ordinary loads).
+template <bool kStream>
+__device__ __forceinline__ uint4 load_kv(const void* p) {
+  if constexpr (kStream) {
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v v = __builtin_nontemporal_load(static_cast<const u32x4v*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *static_cast<const uint4*>(p);
+  }
+}
+
 __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
   return (static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks)) ? blk : 0;
 }
@@ -234,7 +252,8 @@ using PoolPtr = typename std::conditional<kFused, KV*, const KV*>::type;
 // kFused: the fused-append variant (pa_append_decode*); the plain decode is
 // compiled without that code. kArgs (with kFused): lengths and slots come
 // from the launch arguments (pa_append_decode_args), not device memory.
-template <typename T, typename KV, int D, int G, bool kFused, bool kArgs>
+// kStream: K/V rows are loaded non-temporally (see load_kv).
+template <typename T, typename KV, int D, int G, bool kFused, bool kArgs, bool kStream>
 __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void DecodeKernel(
     T* __restrict__ out, const T* __restrict__ q, PoolPtr<kFused, KV> __restrict__ kc,
     PoolPtr<kFused, KV> __restrict__ vc, const int32_t* tables,
@@ -386,6 +405,20 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   const int ntok = max(0, min(w0 + TPW, L) - w0) - (holds_new ? 1 : 0);
   const int nsteps = (ntok + kRowsPerStep - 1) / kRowsPerStep;
 
+  // The new token's K/V row (this wave's head), loaded now so that its
+  // latency overlaps the streaming loop rather than following it.
+  uint4 kxn[CPL], vxn[CPL];
+  if constexpr (kFusable) {
+    if (holds_new) {
+      const int64_t nrow = (static_cast<int64_t>(b) * Hkv + g) * D;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        kxn[i] = *reinterpret_cast<const uint4*>(knew + nrow + (j + kLanesPerRow * i) * EPC);
+        vxn[i] = *reinterpret_cast<const uint4*>(vnew + nrow + (j + kLanesPerRow * i) * EPC);
+      }
+    }
+  }
+
   // q fragments: this lane's chunks (j, j + 8, ...) of the G heads.
   uint4 qf[G][CPL][QPC];
   {
@@ -451,8 +484,8 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     const KV* vrow = vbase + slot0 * row_stride;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      kx[i] = *reinterpret_cast<const uint4*>(krow + (j + kLanesPerRow * i) * EPC);
-      vx[i] = *reinterpret_cast<const uint4*>(vrow + (j + kLanesPerRow * i) * EPC);
+      kx[i] = load_kv<kStream>(krow + (j + kLanesPerRow * i) * EPC);
+      vx[i] = load_kv<kStream>(vrow + (j + kLanesPerRow * i) * EPC);
     }
   };
 
@@ -572,13 +605,8 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // pool.
   if constexpr (kFusable) {
     if (holds_new) {
-      const int64_t nrow = (static_cast<int64_t>(b) * Hkv + g) * D;
-      uint4 kx[CPL], vx[CPL];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        kx[i] = *reinterpret_cast<const uint4*>(knew + nrow + (j + kLanesPerRow * i) * EPC);
-        vx[i] = *reinterpret_cast<const uint4*>(vnew + nrow + (j + kLanesPerRow * i) * EPC);
-      }
+      const uint4 (&kx)[CPL] = kxn;
+      const uint4 (&vx)[CPL] = vxn;
       float x[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -755,7 +783,7 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   DecodeWorkspace ws = DecodeWorkspaceLayout(a.ws, a.B, a.Hq, a.D, P);
   static const StepArgs kNoStepArgs{};
   const StepArgs& meta = a.step_args != nullptr ? *a.step_args : kNoStepArgs;
-  auto launch = [&](auto kernel, const auto& meta) {
+  auto launch_kernel = [&](auto kernel, const auto& meta) {
     hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(kThreads), 0, stream,
                        static_cast<T*>(a.out), static_cast<const T*>(a.q),
                        static_cast<KV*>(a.k_cache), static_cast<KV*>(a.v_cache),
@@ -764,13 +792,21 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
                        P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),
                        static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, meta);
   };
-  if constexpr (sizeof(KV) == sizeof(T)) {
-    if (a.new_k != nullptr && a.step_args != nullptr) launch(DecodeKernel<T, KV, D, G, true, true>, meta);
-    else if (a.new_k != nullptr) launch(DecodeKernel<T, KV, D, G, true, false>, NoStepArgs{});
-    else launch(DecodeKernel<T, KV, D, G, false, false>, NoStepArgs{});
-  } else {
-    launch(DecodeKernel<T, KV, D, G, false, false>, NoStepArgs{});
-  }
+  auto launch = [&](auto stream_tag) {
+    constexpr bool kStream = decltype(stream_tag)::value;
+    if constexpr (sizeof(KV) == sizeof(T)) {
+      if (a.new_k != nullptr && a.step_args != nullptr)
+        launch_kernel(DecodeKernel<T, KV, D, G, true, true, kStream>, meta);
+      else if (a.new_k != nullptr)
+        launch_kernel(DecodeKernel<T, KV, D, G, true, false, kStream>, NoStepArgs{});
+      else
+        launch_kernel(DecodeKernel<T, KV, D, G, false, false, kStream>, NoStepArgs{});
+    } else {
+      launch_kernel(DecodeKernel<T, KV, D, G, false, false, kStream>, NoStepArgs{});
+    }
+  };
+  if (a.stream_loads) launch(std::true_type{});
+  else launch(std::false_type{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
   const int BH = a.B * a.Hq;

@@ -63,6 +63,8 @@ struct DecodeArgs {
   int32_t* tables_out = nullptr;
   // Slots and lengths in the launch arguments (seq_lens and new_slots null).
   const StepArgs* step_args = nullptr;
+  // K/V rows loaded non-temporally (pools without shared blocks).
+  bool stream_loads = true;
 };
 hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream);
 

@@ -376,6 +376,9 @@ pa_status PrepareDecode(const pa_pool& pool, void* out, const void* q, const int
   a->k_scale = pool.k_scale;
   a->v_scale = pool.v_scale;
   a->dtype = l.dtype;
+  // Streamed (non-temporal) K/V loads unless some block is shared: a shared
+  // prefix is read by many sequences and should stay in the caches.
+  a->stream_loads = pool.bm.shared_blocks() == 0;
   *run = true;
   return PA_OK;
 }

@@ -63,7 +63,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = kPrefillRows;  // query rows (positions x heads) per workgroup
 static_assert(kRows == 32 * kWaves, "one 32-row MFMA tile per wave");
 constexpr int kKT = 64;             // KV tokens per tile
-constexpr float kLazyMax = 8.f;
+// Largest sum of one half-row's weights in a tile before the running max is
+// raised (so every weight stays at most 2^15: finite in bf16 and fp32).
+constexpr float kSumLimit = 32768.f;
+constexpr uint32_t kBf16Ones = 0x3F803F80u;  // (1.0, 1.0) as packed bf16
 constexpr int kRankedBatch = 256;   // batches up to this size are ordered by cache length
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -176,13 +179,16 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
   const int apos = ctx + qpos;  // attends to keys 0..apos
   const int64_t row_off = (static_cast<int64_t>(qbeg + qpos) * Hq + g * G + hl) * D;
 
-  bf16x8v qf[PG::kKSteps];
+  // The query row, loaded here and scaled by scale·log2(e) (rounded to bf16)
+  // once the start-up loads have arrived, so that the products give scores in
+  // log2 units directly.
+  uint4 qraw[PG::kKSteps];
 #pragma unroll
   for (int s = 0; s < PG::kKSteps; ++s) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row_valid) v = *reinterpret_cast<const uint4*>(q + row_off + (D / 2) * h2 + 8 * s);
-    qf[s] = __builtin_bit_cast(bf16x8v, v);
+    qraw[s] = make_uint4(0, 0, 0, 0);
+    if (row_valid) qraw[s] = *reinterpret_cast<const uint4*>(q + row_off + (D / 2) * h2 + 8 * s);
   }
+  bf16x8v qf[PG::kKSteps];
 
   // Keys the workgroup needs: 0 .. kv_end-1 (the last valid row's position).
   const int kv_end = max(0, ctx + min(q0 + QP, nq));
@@ -337,8 +343,13 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
   for (int db = 0; db < PG::kDBlocks; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
-  float m = -INFINITY;  // running max (log2 units), lazily raised
+  float m = -INFINITY;  // running max (log2 units); raised only when a tile's weights grow large
   float l = 0.f;        // this half-wave's share of the softmax denominator
+  // -m in every element (0 while m = -inf): the score accumulators of a
+  // tile start from it, so they hold s - m and the weights are exp2 of them.
+  f32x16v negm;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) negm[v] = 0.f;
 
   // Per-lane LDS bases: MFMA operand reads then differ only by immediates.
   const int k_lane = n * PG::kKPitch + (D / 2) * h2;   // + (32*tb)*pitch + 8*st
@@ -380,7 +391,7 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
       const bf16x8v a = kop[idx % kAhead];
       if (idx + kAhead < kQK) kop[idx % kAhead] = k_operand(idx + kAhead);
       if (st == 0) {
-        s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], f32x16v{}, 0, 0, 0);
+        s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], negm, 0, 0, 0);
       } else {
         s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[tb], 0, 0, 0);
       }
@@ -394,7 +405,8 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 
     __builtin_amdgcn_s_setprio(0);
-    // Causal mask where the tile reaches past min_apos; tile max on raw scores.
+    // s[] now holds x - m for the tile's keys, in log2 units (x = scaled
+    // score). Causal mask where the tile reaches past min_apos.
     const int t0 = j * kKT;
     if (t0 + kKT - 1 > min_apos) {
 #pragma unroll
@@ -405,39 +417,59 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
           s[tb][v] = t <= apos ? s[tb][v] : -INFINITY;
         }
     }
-    float tmax = -INFINITY;
+    // Weights P = 2^(s[] - shift) as bf16, packed per 16-key MFMA step; the
+    // returned tile sum adds the rounded weights (the values the PV product
+    // uses) two at a time with v_dot2_f32_bf16.
+    bf16x8v p[PG::kPSteps];
+    auto weights = [&](float shift) {
+      float lt = 0.f;
 #pragma unroll
-    for (int tb = 0; tb < PG::kSBlocks; ++tb)
+      for (int tb = 0; tb < PG::kSBlocks; ++tb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[tb][v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;  // scale > 0 keeps the argmax
-
-    // Lazy max: raise m only when the tile exceeds it by more than kLazyMax.
-    const bool raise = tmax > m + kLazyMax;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float mn = raise ? tmax : m;
-      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+        for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[2 * tb + hs][e] = static_cast<__bf16>(fast_exp2(s[tb][8 * hs + e] - shift));
+          const uint4 w = __builtin_bit_cast(uint4, p[2 * tb + hs]);
+          lt = dot2_bf16(w.x, kBf16Ones, lt);
+          lt = dot2_bf16(w.y, kBf16Ones, lt);
+          lt = dot2_bf16(w.z, kBf16Ones, lt);
+          lt = dot2_bf16(w.w, kBf16Ones, lt);
+        }
+      return lt;
+    };
+    // Usually the running max stays: the weights are exp2(s[]) as they are,
+    // with no max, subtraction or scaling per score. The first tile sets the
+    // max, and a tile whose weights grow large (a half-row sum above
+    // kSumLimit, so no weight exceeds it) raises it to the true running max,
+    // rescaling O and l, before its weights are taken again.
+    float lt = 0.f;
+    bool exact = j == 0;  // wave-uniform
+    if (!exact) {
+      lt = weights(0.f);
+      exact = __builtin_amdgcn_ballot_w64(!(lt <= kSumLimit)) != 0;
+    }
+    if (exact) {
+      float T = -INFINITY;  // the tile's max of s[] over the row (both half-waves)
+#pragma unroll
+      for (int tb = 0; tb < PG::kSBlocks; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) T = fmaxf(T, s[tb][v]);
+      T = fmaxf(T, __shfl_xor(T, 32));
+      const float M = m == -INFINITY ? 0.f : m;    // what the accumulators started from
+      const float mn = fmaxf(m, M + T);             // -inf only for a row with no key yet
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < PG::kDBlocks; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
       m = mn;
+      const float nm = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) negm[v] = nm;
+      lt = weights(m == -INFINITY ? 0.f : m - M);
     }
-    const float nm = (m == -INFINITY) ? 0.f : -m;
-
-    // P = 2^(scale·s - m) as bf16, packed per 16-key MFMA step.
-    bf16x8v p[PG::kPSteps];
-#pragma unroll
-    for (int tb = 0; tb < PG::kSBlocks; ++tb)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = fast_exp2(fmaf(s[tb][8 * hs + e], scale_log2, nm));
-          l += pe;
-          p[2 * tb + hs][e] = static_cast<__bf16>(pe);
-        }
+    l += lt;
 
     __builtin_amdgcn_s_setprio(1);
     // O^T += V^T · P^T, V operands read kAhead MFMAs ahead.
@@ -480,6 +512,18 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     __syncthreads();
   };
 
+  auto scale_q = [&]() {
+#pragma unroll
+    for (int st = 0; st < PG::kKSteps; ++st) {
+      const uint32_t w[4] = {qraw[st].x, qraw[st].y, qraw[st].z, qraw[st].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qf[st][2 * k] = static_cast<__bf16>(__uint_as_float(w[k] << 16) * scale_log2);
+        qf[st][2 * k + 1] = static_cast<__bf16>(__uint_as_float(w[k] & 0xFFFF0000u) * scale_log2);
+      }
+    }
+  };
+
   StageRegs sreg_a, sreg_b;
   LoadIds ids_next;
   // Start-up: the block ids of the first three tiles load together with q,
@@ -492,6 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     const int raw1 = fetch_ids(min(1, n_tiles - 1));
     const int raw2 = fetch_ids(min(2, n_tiles - 1));
     __builtin_amdgcn_s_waitcnt(0);
+    scale_q();
     LoadIds ids0, ids1;
     spread_ids(raw0, ids0);
     spread_ids(raw1, ids1);
@@ -501,6 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     store_tile(0, sreg_b);
   } else {
     __builtin_amdgcn_s_waitcnt(0);
+    scale_q();
   }
   __syncthreads();
   // Both halves of the pair run unconditionally, so every path into the next
