@@ -489,9 +489,10 @@ def run_decode_fp8(args):
 
 def run_decode_skewed(args):
     """A batch whose one long sequence dominates (63 x 512 tokens + 1 x 32768,
-    8B-shaped heads): pa_decode in the library's shape-based default partition
-    and in a fixed 512, and pa_append_decode_args (lengths on the host, no new
-    tokens) in its length-based default."""
+    8B-shaped heads): pa_decode in the library's default partition (chosen by
+    the kernel from the device lengths) and in a fixed 512, and
+    pa_append_decode_args (lengths on the host, no new tokens) in its
+    length-based default."""
     import numpy as np
     import torch
 
@@ -518,8 +519,11 @@ def run_decode_skewed(args):
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / n * 1e-3
         nbytes = decode_bytes(wl, wl.seq_lens)
-        res[label] = {"partition_tokens": pt or pa_decode_partition_tokens(cache.pool, wl.B, wl.max_seq_len),
-                      "us_mean": t * 1e6, "gbps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+        # partition_tokens 0: chosen by the kernel from the device lengths (max_seq_len >= 8192),
+        # the same partition the host rule gives for these lengths
+        used = pt or pa_decode_partition_tokens_for_lengths(cache.pool, wl.seq_lens, wl.max_seq_len)
+        res[label] = {"partition_tokens": used, "us_mean": t * 1e6, "gbps": nbytes / t / 1e9,
+                      "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
     # Lengths on the host: the partition comes from the lengths themselves.
     lens = np.asarray(wl.seq_lens, dtype=np.int32)
     no_slots = np.full(wl.B, -1, dtype=np.int64)

@@ -272,8 +272,12 @@ pa_status pa_write_kv(pa_pool* pool, const void* key, const void* value,
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_seq_len, int32_t partition_tokens);
 
-/* The KV partition pa_decode uses for partition_tokens = 0, chosen from the
- * launch shape (the host does not see the lengths). Work items are
+/* The KV partition pa_decode uses for partition_tokens = 0 when
+ * max_seq_len < 8192 (or B > 1024), chosen from the launch shape (the host
+ * does not see the lengths); for max_seq_len >= 8192 this is only the
+ * starting point: the decode kernel itself then takes the lengths into
+ * account, as pa_decode_partition_tokens_for_lengths does on the host (the
+ * shape rule stays when every sequence has at least 8192 tokens). Work items are
  * (sequence, group of kv heads, partition), with two kv heads per group
  * when the pool's kv-head count is even. For max_seq_len >= 8192 the
  * partition is the longest that still gives 256 items at max_seq_len (long
@@ -282,8 +286,7 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
  * count is at most 480 (672 for an FP8 pool): shorter partitions even out
  * the work of sequences of different lengths while every item still finds a
  * workgroup slot at once on MI355X. It is kept within [640, 8192] tokens
- * and rounded up to a multiple of 64. A batch that mixes very long and short
- * sequences runs faster with a caller-chosen partition. (The split into
+ * and rounded up to a multiple of 64. (The split into
  * partitions merged by log-sum-exp is this library's; the pages' decode
  * walks a sequence's blocks in one pass: "vLLM的'内存分页'到底多神奇",
  * xxqk.cn, §3 phase 2.) Returns 0 for a null pool or negative sizes. */
@@ -321,7 +324,11 @@ int32_t pa_decode_partition_tokens_for_lengths(const pa_pool* pool, const int32_
  * partition_tokens: long contexts are split into KV partitions of this many
  *   tokens, each reduced to (max, sum, Σ weight·V), then merged by
  *   log-sum-exp (a second launch, only when some sequence spans more than
- *   one partition). 0 = the library's choice (pa_decode_partition_tokens).
+ *   one partition). 0 = the library's choice (pa_decode_partition_tokens;
+ *   for max_seq_len >= 8192 and B <= 1024 the kernel refines it from the
+ *   lengths: the smallest multiple of 64 tokens, at least 512, giving at
+ *   most 480 work items, 672 on FP8 pools, unless every sequence has at
+ *   least 8192 tokens).
  *   Must be a multiple of 64, at most 2^24, else PA_ERR_UNSUPPORTED.
  * workspace (device, 16-byte aligned, contents irrelevant) of
  *   workspace_bytes ≥ pa_decode_workspace_bytes(...); may be NULL when that
@@ -349,10 +356,14 @@ pa_status pa_decode(pa_pool* pool, void* out, const void* q, const int32_t* bloc
  * which keeps the last call's contents (each call writes every partial state
  * before it reads it, so nothing needs clearing): calls that overlap on one
  * GPU (different streams, or several threads) race and must be serialised
- * by the caller. Errors: those of pa_decode; PA_ERR_UNSUPPORTED when the
- * partial states of this shape (B × num_q_heads × partitions × (head_dim + 2)
- * × 4 bytes, partitions = ceil(max_seq_len / partition_tokens), 0 when one
- * partition covers max_seq_len) exceed PA_DECODE_STATIC_SCRATCH_BYTES. */
+ * by the caller. partition_tokens = 0 chooses the partition as pa_decode
+ * does, except that a long-context launch keeps the shape rule of
+ * pa_decode_partition_tokens when the partial states of 512-token
+ * partitions would not fit the scratch. Errors: those of pa_decode;
+ * PA_ERR_UNSUPPORTED when the partial states of this shape (B × num_q_heads
+ * × partitions × (head_dim + 2) × 4 bytes + 16, partitions =
+ * ceil(max_seq_len / partition_tokens), 0 when one partition covers
+ * max_seq_len) exceed PA_DECODE_STATIC_SCRATCH_BYTES. */
 pa_status pa_decode_static(pa_pool* pool, void* out, const void* q, const int32_t* block_tables,
                            int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t num_q_heads,
                            float scale, int32_t max_seq_len, int32_t partition_tokens, void* stream);

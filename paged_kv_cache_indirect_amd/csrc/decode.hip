@@ -68,6 +68,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
+#include <climits>
 #include <type_traits>
 
 namespace pa {
@@ -76,7 +78,7 @@ namespace {
 
 constexpr int kWaves = 4;                 // waves per workgroup (one partition of 1, 2 or 4 kv heads)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kCompactBatch = 1024;  // batches up to this size get a compact work list
+constexpr int kCompactBatch = kDecodeCompactBatch;
 constexpr int kLanesPerRow = 8;
 constexpr int kRowsPerStep = 64 / kLanesPerRow;
 constexpr float kLazyMax = 8.f;
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
     int32_t P, int32_t per_xcd, float scale_log2, float v_scale, int32_t hsh,
     const T* __restrict__ knew, const T* __restrict__ vnew, const int64_t* new_slots_in,
-    int32_t* tables_out, const StepArgsOf<kArgs> meta) {
+    int32_t* tables_out, int32_t auto_items, int32_t* ws_pt, const StepArgsOf<kArgs> meta) {
   using RG = RowGeom<KV, D>;
   using WD = Widen<KV>;
   constexpr int CPL = RG::kChunksPerLane;
@@ -299,8 +301,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     __shared__ int s_len[kCompactBatch];  // clamped lengths
     __shared__ int s_wsum[kWaves];
     constexpr int kPer = kCompactBatch / kThreads;  // sequences per thread
-    int cnt[kPer];
-    int tsum = 0;
+    int Lv[kPer];  // this thread's clamped lengths (-1: no such sequence)
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int bb = tid * kPer + i;
@@ -311,7 +312,63 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       }
       Lb = min(max(Lb, 0), max_seq_len);
       s_len[bb] = Lb;
-      cnt[i] = bb < B ? max(1, (Lb + PT - 1) / PT) : 0;
+      Lv[i] = bb < B ? Lb : -1;
+    }
+    if (auto_items > 0) {
+      // The partition from the lengths themselves (the launch passed the
+      // shape rule's choice in PT): unless every sequence is a long context,
+      // the smallest multiple of 64 tokens, at least 512, whose item count
+      // (head groups x sum of max(1, ceil(L / pt))) is at most auto_items;
+      // one partition per sequence when even the longest length gives more.
+      // Every workgroup computes the same value; workgroup 0 records it for
+      // the merge.
+      __shared__ int s_red[2][kWaves];
+      int parity = 0;
+      auto reduce = [&](int v, auto op) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) v = op(v, __shfl_xor(v, o));
+        if (lane == 0) s_red[parity][w] = v;
+        __syncthreads();
+        int r = s_red[parity][0];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) r = op(r, s_red[parity][ww]);
+        parity ^= 1;  // the next reduction writes the other buffer
+        return r;
+      };
+      int mn = INT_MAX, mx = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (Lv[i] >= 0) {
+          mn = min(mn, Lv[i]);
+          mx = max(mx, Lv[i]);
+        }
+      mn = reduce(mn, [](int a, int c) { return min(a, c); });
+      mx = reduce(mx, [](int a, int c) { return max(a, c); });
+      if (mn < kDecodeLongContext) {
+        auto items = [&](int pt) {
+          int n = 0;
+#pragma unroll
+          for (int i = 0; i < kPer; ++i)
+            if (Lv[i] >= 0) n += max(1, (Lv[i] + pt - 1) / pt);
+          return reduce(n, [](int a, int c) { return a + c; }) * NG;
+        };
+        int lo = 512, hi = max(512, (mx + 63) / 64 * 64);
+        if (items(hi) <= auto_items) {
+          while (lo < hi) {
+            const int mid = (lo + hi) / 2 / 64 * 64;
+            if (mid < lo) break;
+            if (items(mid) <= auto_items) hi = mid; else lo = mid + 64;
+          }
+        }
+        PT = hi;
+      }
+      if (wg == 0 && tid == 0 && ws_pt != nullptr) *ws_pt = PT;
+    }
+    int cnt[kPer];
+    int tsum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      cnt[i] = Lv[i] >= 0 ? max(1, (Lv[i] + PT - 1) / PT) : 0;
       tsum += cnt[i];
     }
     // inclusive scan of tsum over the workgroup
@@ -713,7 +770,7 @@ __global__ __launch_bounds__(256) void MergeKernel(T* __restrict__ out, const fl
                                                    const float* __restrict__ ws_ml,
                                                    const int32_t* seq_lens_in, int32_t BH,
                                                    int32_t Hq, int32_t max_seq_len, int32_t PT, int32_t P,
-                                                   const StepArgsOf<kArgs> meta) {
+                                                   const int32_t* ws_pt, const StepArgsOf<kArgs> meta) {
   constexpr int EPL = D / 64;
   constexpr int kChunk = 16;
   const int lane = threadIdx.x & 63;
@@ -724,6 +781,7 @@ __global__ __launch_bounds__(256) void MergeKernel(T* __restrict__ out, const fl
   if constexpr (kArgs) L = meta.lens[b];
   else L = seq_lens_in[b];
   L = min(max(L, 0), max_seq_len);
+  if (ws_pt != nullptr) PT = *ws_pt;  // chosen from the lengths by pass 1
   const int Pb = (L + PT - 1) / PT;
   if (Pb <= 1) return;  // written by pass 1
   const float* ml = ws_ml + static_cast<int64_t>(bh) * P * 2;
@@ -775,7 +833,26 @@ template <typename T, typename KV, int D, int G>
 hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   const int P = a.num_partitions;
   const int hsh = DecodeHeadShift(a.Hkv);
-  const int64_t items = static_cast<int64_t>(P) * a.B * (a.Hkv >> hsh);
+  const int64_t NG = a.Hkv >> hsh;
+  int64_t items = static_cast<int64_t>(P) * a.B * NG;
+  if (a.auto_items > 0) {
+    // The kernel picks the partition: at most auto_items items, or one per
+    // sequence, or what the shape rule (a.partition_tokens) gives.
+    const int64_t shape = static_cast<int64_t>(DecodePartitions(a.max_seq_len, a.partition_tokens)) * a.B * NG;
+    items = std::min(items, std::max(std::max<int64_t>(a.auto_items, a.B * NG), shape));
+  } else if (a.step_args != nullptr && a.B <= kCompactBatch) {
+    // Lengths on the host: the grid holds exactly the compact list's items
+    // (the kernel builds the same list). Sized for every sequence at
+    // max_seq_len instead, a batch with one long sequence among short ones
+    // launches thousands of surplus workgroups that only run the prologue
+    // and exit (measured: 63 x 512 + 1 x 32768 tokens, 91.7 us).
+    int64_t S = 0;
+    for (int32_t b = 0; b < a.B; ++b) {
+      const int32_t L = std::min(std::max(a.step_args->lens[b], 0), a.max_seq_len);
+      S += std::max(1, (L + a.partition_tokens - 1) / a.partition_tokens);
+    }
+    items = S * NG;
+  }
   const int per_xcd = static_cast<int>((items + 7) / 8);
   const bool fp8 = sizeof(KV) == 1;
   const float scale_log2 = a.scale * (fp8 ? a.k_scale : 1.f) * 1.4426950408889634f;
@@ -790,7 +867,7 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
                        a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
                        __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
                        P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),
-                       static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, meta);
+                       static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, a.auto_items, ws.pt, meta);
   };
   auto launch = [&](auto stream_tag) {
     constexpr bool kStream = decltype(stream_tag)::value;
@@ -813,11 +890,11 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   if (a.seq_lens == nullptr) {  // lengths in the launch arguments
     hipLaunchKernelGGL((MergeKernel<T, D, true>), dim3((BH + 3) / 4), dim3(256), 0, stream,
                        static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, BH, a.Hq, a.max_seq_len,
-                       a.partition_tokens, P, meta);
+                       a.partition_tokens, P, a.auto_items > 0 ? ws.pt : nullptr, meta);
   } else {
     hipLaunchKernelGGL((MergeKernel<T, D, false>), dim3((BH + 3) / 4), dim3(256), 0, stream,
                        static_cast<T*>(a.out), ws.acc, ws.ml, a.seq_lens, BH, a.Hq, a.max_seq_len,
-                       a.partition_tokens, P, NoStepArgs{});
+                       a.partition_tokens, P, a.auto_items > 0 ? ws.pt : nullptr, NoStepArgs{});
   }
   return hipGetLastError();
 }

@@ -65,6 +65,11 @@ struct DecodeArgs {
   const StepArgs* step_args = nullptr;
   // K/V rows loaded non-temporally (pools without shared blocks).
   bool stream_loads = true;
+  // > 0: the decode kernel chooses the partition from the device lengths
+  // (at most this many items; partition_tokens then holds the shape rule's
+  // choice, used when every sequence is a long context) and records it in
+  // the workspace for the merge. num_partitions is sized for 512 tokens.
+  int32_t auto_items = 0;
 };
 hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream);
 
@@ -116,6 +121,7 @@ inline int32_t DecodeHeadShift(int32_t Hkv) { return Hkv % 2 == 0 ? 1 : 0; }
 //    instructions per byte and gain from more of them).
 // The partition is kept within [kDecodeMinPartition, kDecodeDefaultMaxPartition]
 // and rounded up to a multiple of 64.
+constexpr int32_t kDecodeCompactBatch = 1024;  // batches up to this size get the compact work list
 constexpr int32_t kDecodeLongContext = 8192;
 constexpr int64_t kDecodeLongItems = 256;
 constexpr int64_t kDecodeShortItems = 480;
@@ -182,21 +188,24 @@ inline int32_t DecodePartitions(int32_t max_seq_len, int32_t partition_tokens) {
   return p < 1 ? 1 : p;
 }
 // Workspace of a decode call with more than one partition: the fp32 partial
-// state of every (sequence, q head, partition):
-//   [acc: B*Hq*P*D f32][max, sum: B*Hq*P*2 f32]
+// state of every (sequence, q head, partition), then the partition the
+// kernel chose from the lengths (when it chooses):
+//   [acc: B*Hq*P*D f32][max, sum: B*Hq*P*2 f32][partition: int32, 16 bytes]
 inline size_t DecodeWorkspaceBytes(int32_t B, int32_t Hq, int32_t D, int32_t P) {
   if (P <= 1) return 0;
-  return static_cast<size_t>(B) * Hq * P * (static_cast<size_t>(D) + 2) * sizeof(float);
+  return static_cast<size_t>(B) * Hq * P * (static_cast<size_t>(D) + 2) * sizeof(float) + 16;
 }
 struct DecodeWorkspace {
   float* acc;
   float* ml;
+  int32_t* pt;
 };
 inline DecodeWorkspace DecodeWorkspaceLayout(void* ws, int32_t B, int32_t Hq, int32_t D, int32_t P) {
-  DecodeWorkspace w{nullptr, nullptr};
+  DecodeWorkspace w{nullptr, nullptr, nullptr};
   if (!ws || P <= 1) return w;
   w.acc = static_cast<float*>(ws);
   w.ml = w.acc + static_cast<size_t>(B) * Hq * P * D;
+  w.pt = reinterpret_cast<int32_t*>(w.ml + static_cast<size_t>(B) * Hq * P * 2);
   return w;
 }
 

@@ -328,7 +328,7 @@ pa_status EnqueueWrite(const pa_pool& pool, const WriteCall& w, hipStream_t st) 
 pa_status PrepareDecode(const pa_pool& pool, void* out, const void* q, const int32_t* block_tables,
                         int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t num_q_heads, float scale,
                         int32_t max_seq_len, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                        pa::DecodeArgs* a, bool* run) {
+                        pa::DecodeArgs* a, bool* run, bool seq_lens_on_device = true) {
   *run = false;
   if (B < 0 || max_blocks < 0 || max_seq_len < 0 || partition_tokens < 0)
     return Fail(PA_ERR_INVALID, "negative size argument");
@@ -347,9 +347,24 @@ pa_status PrepareDecode(const pa_pool& pool, void* out, const void* q, const int
   if (pt % 64 || pt > pa::kDecodeMaxPartition)
     return Fail(PA_ERR_UNSUPPORTED, "partition_tokens must be a multiple of 64, at most " +
                                         std::to_string(pa::kDecodeMaxPartition));
-  const int32_t P = pa::DecodePartitions(max_seq_len, pt);
+  int32_t P = pa::DecodePartitions(max_seq_len, pt);
   if (static_cast<int64_t>(P) * B * l.num_kv_heads >= (int64_t{1} << 31) - 8)
     return Fail(PA_ERR_UNSUPPORTED, "grid too large");
+  // The library's choice for long contexts is made on the device, from the
+  // lengths (the shape rule above cannot see a batch where one long
+  // sequence sits among short ones). That needs the workspace of 512-token
+  // partitions, the shortest the device can choose; without room for it
+  // (pa_decode_static's fixed scratch), the shape rule stays.
+  int32_t auto_items = 0;
+  if (partition_tokens == 0 && seq_lens_on_device && B <= pa::kDecodeCompactBatch &&
+      max_seq_len >= pa::kDecodeLongContext) {
+    const int32_t P512 = pa::DecodePartitions(max_seq_len, 512);
+    if (static_cast<int64_t>(P512) * B * l.num_kv_heads < (int64_t{1} << 31) - 8 && workspace &&
+        workspace_bytes >= pa::DecodeWorkspaceBytes(B, num_q_heads, l.head_dim, P512)) {
+      P = P512;
+      auto_items = static_cast<int32_t>(l.dtype == PA_FP8_E4M3 ? pa::kDecodeShortItemsFp8 : pa::kDecodeShortItems);
+    }
+  }
   const size_t need = pa::DecodeWorkspaceBytes(B, num_q_heads, l.head_dim, P);
   if (need && (!workspace || workspace_bytes < need))
     return Fail(PA_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
@@ -372,6 +387,7 @@ pa_status PrepareDecode(const pa_pool& pool, void* out, const void* q, const int
   a->max_seq_len = max_seq_len;
   a->partition_tokens = pt;
   a->num_partitions = P;
+  a->auto_items = auto_items;
   a->scale = scale;
   a->k_scale = pool.k_scale;
   a->v_scale = pool.v_scale;
@@ -737,8 +753,8 @@ pa_status pa_decode_static(pa_pool* pool, void* out, const void* q, const int32_
     if (s != PA_OK) return s;
     pa::DecodeArgs a{};
     bool run = false;
-    s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens, B, num_q_heads, scale, max_seq_len, pt,
-                      ws, PA_DECODE_STATIC_SCRATCH_BYTES, &a, &run);
+    s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens, B, num_q_heads, scale, max_seq_len,
+                      partition_tokens, ws, PA_DECODE_STATIC_SCRATCH_BYTES, &a, &run);
     if (s != PA_OK || !run) return s;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (DebugChecks()) {
@@ -800,7 +816,7 @@ pa_status pa_append_decode_args(pa_pool* pool, void* out, const void* q, const v
                            ? pa::DecodePartitionForLengths(seq_lens_host, B, pool->layout.num_kv_heads, max_seq_len)
                            : partition_tokens;
     pa_status s = PrepareDecode(*pool, out, q, block_tables, max_blocks, seq_lens_host, B, num_q_heads, scale,
-                                max_seq_len, pt, workspace, workspace_bytes, &a, &run);
+                                max_seq_len, pt, workspace, workspace_bytes, &a, &run, false);
     if (s != PA_OK) return s;
     if (run) {
       if (!key || !value || !slot_mapping_host) return Fail(PA_ERR_INVALID, "null argument");

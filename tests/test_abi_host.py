@@ -322,7 +322,7 @@ def test_device_entry_points_validate_before_launch():
     assert st == 0
     dummy = 0x40000
     ws = pa.lib.pa_decode_workspace_bytes(64, 32, 128, 4097, 512)   # 9 partitions
-    assert ws == 64 * 32 * 9 * 130 * 4
+    assert ws == 64 * 32 * 9 * 130 * 4 + 16   # partial states + the recorded partition
     assert pa.lib.pa_decode_workspace_bytes(64, 32, 128, 512, 512) == 0   # one partition covers it
     # G = 3 is outside the supported set
     assert pa.lib.pa_decode(pool, dummy, dummy, dummy, 256, dummy, 4, 24, 0.1, 4096, 0, dummy, ws, None) \

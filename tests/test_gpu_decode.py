@@ -295,3 +295,30 @@ def test_decode_partition_invariance_and_max_seq_len_slack():
     spread = max(np.abs(o - outs[0]).max() for o in outs)
     assert spread <= 2e-2
     gpu.close()
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv", [
+    ([300] * 15 + [9000], 32, 8),          # one long context among short ones
+    ([9000, 8500, 12000, 64, 1], 8, 2),    # long contexts plus two tiny ones
+    ([8192, 9000, 10000], 8, 2),           # every sequence long: the shape rule stays
+])
+def test_decode_default_partition_from_device_lengths(lens, Hq, Hkv):
+    """pa_decode with partition_tokens = 0 and max_seq_len >= 8192 picks its
+    partition on the device from the lengths: bit-identical to pa_decode at
+    the partition the host rule gives for the same lengths
+    (pa_decode_partition_tokens_for_lengths), and within the bf16 bar of
+    the oracle."""
+    from paged_kv_cache_indirect_amd import pa_decode_partition_tokens_for_lengths, pa_decode_partition_tokens
+    wl = small(lens, Hq=Hq, Hkv=Hkv, D=128, bs=16, seed=41)
+    gpu, ora = build_both(wl)
+    msl = wl.max_seq_len
+    host_pt = pa_decode_partition_tokens_for_lengths(gpu.pool, wl.seq_lens, msl)
+    if min(lens) >= 8192:
+        assert host_pt == pa_decode_partition_tokens(gpu.pool, wl.B, msl)
+    print(f"[auto partition] lens={lens} host rule {host_pt}", flush=True)
+    auto = gpu.decode(0, gpu.workspace_for(0)).clone()
+    fixed = gpu.decode(host_pt, gpu.workspace_for(host_pt)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(auto.view(torch.int16), fixed.view(torch.int16)), "device choice differs from the host rule"
+    assert_close(widen_out(auto, wl.dtype), oracle_out(wl, ora), wl.dtype, f"auto partition {lens}")
+    gpu.close()
