@@ -422,6 +422,7 @@ def run_configs(args):
                "bytes_per_call": nbytes, "kv_bytes": wl.kv_bytes()}
         if wl.prefix_len:
             res["unique_kv_bytes"] = wl.unique_kv_bytes()
+            res["hbm_bytes_per_call_measured"] = measured_traffic("decode_prefix")
         for pt in pts:
             ws = cache.workspace_for(pt)
             settle(lambda: cache.decode(pt, ws), 0.05)

@@ -19,8 +19,8 @@
 //  * The contraction runs on v_mfma_f32_32x32x16_bf16 in transposed form:
 //    S^T = K · Q^T and O^T = V^T · P^T. In the accumulator layout a lane then
 //    owns one query row (lane % 32) and 16 keys (or 16 dims) of it, so the
-//    online softmax is lane-local except one max exchange between the two
-//    half-waves per KV tile, and P goes from the S^T accumulators straight
+//    online softmax is lane-local (the two half-waves exchange a max only
+//    when the running max is raised), and P goes from the S^T accumulators straight
 //    into the B operand of the second product with no data movement: the key
 //    order inside each 16-key step is permuted consistently on both sides
 //    (V^T is written to LDS in that permuted order).
@@ -42,10 +42,17 @@
 //  * MFMA operands are read from LDS four MFMAs ahead of their use.
 //  * Wave priority: 0 during the softmax of a tile, 1 otherwise, so that of
 //    the two waves sharing a SIMD the one with MFMAs to issue goes first.
-//  * Online softmax in base 2: the tile max is taken on raw scores, the
-//    scale is folded into one FMA ahead of exp2, and the running max is
-//    raised lazily (only when a tile exceeds it by more than 8), so most
-//    tiles skip the O rescale; weights stay ≤ 2^8, exact up to rounding.
+//  * Online softmax in base 2 with no per-score max, subtraction or scaling
+//    in the common case: q is scaled by scale·log2(e) once (rounded to
+//    bf16), and each tile's score accumulators start from -m (the running
+//    max), so the products are already x - m and the weights are exp2 of
+//    them. The weights, packed to bf16 for the PV product, are summed two at
+//    a time with v_dot2_f32_bf16 (the denominator adds exactly the values
+//    the numerator multiplies). The first tile, and a tile whose half-row
+//    weight sum exceeds 2^15 (so no weight is larger), take the tile max,
+//    raise m to the true running max, rescale O and l, and take the weights
+//    again; every weight stays ≤ 2^15, and the result is exact up to
+//    rounding.
 //  * Causal mask only on tiles that reach past the smallest position of the
 //    workgroup. Work items are mapped XCD-major with the kv head outermost;
 //    within it all query tiles of one sequence run together (they share each
