@@ -38,7 +38,7 @@
 //    element with v_perm and contracted with v_dot2_f32_bf16 against the two
 //    weights rounded to bf16 (fp32 accumulate) — half the instructions of
 //    unpack + FMA. fp32 caches use plain FMAs.
-//  * At the end the 8 row groups of a wave merge by DPP/shuffles and the
+//  * At the end the 8 row groups of a wave merge by DPP and row swaps and the
 //    waves of one head through LDS, by log-sum-exp. A sequence that fits in
 //    one partition writes its output directly; otherwise every partition
 //    writes its partial state (max, sum, Σ w·V) and a second, small kernel
@@ -325,8 +325,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       __shared__ int s_red[2][kWaves];
       int parity = 0;
       auto reduce = [&](int v, auto op) {
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) v = op(v, __shfl_xor(v, o));
+        v = wave_reduce(v, op);
         if (lane == 0) s_red[parity][w] = v;
         __syncthreads();
         int r = s_red[parity][0];
@@ -803,9 +802,7 @@ __global__ __launch_bounds__(256) void MergeKernel(T* __restrict__ out, const fl
     for (int k = 0; k < kChunk; ++k)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) v[k][e] = k < n ? acc[static_cast<int64_t>(x0 + k) * D + e] : 0.f;
-    float Mc = mx;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) Mc = fmaxf(Mc, __shfl_xor(Mc, s));
+    const float Mc = wave_reduce(mx, OpMax{});
     const float Mn = fmaxf(M, Mc);
     const float f = fast_exp2(M - Mn);
     lsum *= f;
@@ -816,13 +813,12 @@ __global__ __launch_bounds__(256) void MergeKernel(T* __restrict__ out, const fl
     lsum = fmaf(wgt, lx, lsum);
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const float wk = __shfl(wgt, k);
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), k));
 #pragma unroll
       for (int e = 0; e < EPL; ++e) a[e] = k < n ? fmaf(wk, v[k][e], a[e]) : a[e];
     }
   }
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) lsum += __shfl_xor(lsum, s);
+  lsum = wave_reduce(lsum, OpAdd{});
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
