@@ -57,6 +57,11 @@
 //    outermost: consecutive hardware workgroup ids go to different XCDs, so
 //    each XCD owns a contiguous range (half a head group when Hkv = 8) and a
 //    shared prefix block of those heads is re-read from few XCDs' L2.
+//    With the lengths in the launch arguments and no shared blocks, the host
+//    sorts the sequences by partition length instead and workgroup i takes
+//    the i-th item, head groups innermost: the first workgroup on each CU
+//    (workgroups 0..255), whose waves the SIMDs serve first, gets the longer
+//    items, and the second the shorter ones.
 //  * Fused append (a decode step in one call): each sequence's new token is
 //    the last of its sequence, so it ends the range of exactly one wave per
 //    kv head. That wave streams the rest of its range as usual, then adds
@@ -301,13 +306,16 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     __shared__ int s_len[kCompactBatch];  // clamped lengths
     __shared__ int s_wsum[kWaves];
     constexpr int kPer = kCompactBatch / kThreads;  // sequences per thread
+    // Position bb of the list holds sequence bb, or the host's order[bb].
+    bool ordered = false;
+    if constexpr (kArgs) ordered = meta.ordered != 0;
     int Lv[kPer];  // this thread's clamped lengths (-1: no such sequence)
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int bb = tid * kPer + i;
       int Lb = 0;
       if (bb < B) {
-        if constexpr (kArgs) Lb = meta.lens[bb];
+        if constexpr (kArgs) Lb = meta.lens[ordered ? meta.order[bb] : bb];
         else Lb = seq_lens_in[bb];
       }
       Lb = min(max(Lb, 0), max_seq_len);
@@ -390,20 +398,32 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     if (tid == kThreads - 1) s_pref[kCompactBatch] = run;
     __syncthreads();
     const int S = s_pref[kCompactBatch];  // items per kv head
-    const int per_xcd_real = (NG * S + 7) / 8;
-    if ((wg >> 3) >= per_xcd_real) return;
-    const int item = (wg & 7) * per_xcd_real + (wg >> 3);
-    if (item >= NG * S) return;
-    gq = item / S;
-    const int k = item - gq * S;
+    int k;
+    if (ordered) {
+      // Items by decreasing length, head groups innermost, workgroup i takes
+      // item i: consecutive workgroup ids go to different XCDs, and each
+      // CU's first workgroup (the first 32 per XCD), whose waves the SIMDs
+      // serve first, gets the longer items.
+      if (wg >= NG * S) return;
+      gq = wg % NG;
+      k = wg / NG;
+    } else {
+      const int per_xcd_real = (NG * S + 7) / 8;
+      if ((wg >> 3) >= per_xcd_real) return;
+      const int item = (wg & 7) * per_xcd_real + (wg >> 3);
+      if (item >= NG * S) return;
+      gq = item / S;
+      k = item - gq * S;
+    }
     int lo = 0, hi = B - 1;  // largest b with s_pref[b] <= k
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pref[mid] <= k) lo = mid; else hi = mid - 1;
     }
+    p = k - s_pref[lo];
+    L = s_len[lo];
     b = lo;
-    p = k - s_pref[b];
-    L = s_len[b];
+    if constexpr (kArgs) b = ordered ? meta.order[lo] : lo;
   } else {
     const int item = (wg & 7) * per_xcd + (wg >> 3);
     if (item >= NG * B * P) return;
@@ -637,6 +657,13 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       uint4 kB[U][CPL], vB[U][CPL];
       const int nbat = (nsteps + U - 1) / U;
       issue_batch(0, kA, vA);
+      // A CU holds two of these workgroups; the SIMDs issue for the older
+      // wave first, so the second workgroup's waves (wave slot 1) stream
+      // about 1.4x slower than the first's (measured on the 8B-shaped batch:
+      // 7.2 against 10.1 tokens per us per wave) and finish last. Raising
+      // their priority evens the two out.
+      if ((__builtin_amdgcn_s_getreg((3 << 11) | 4) & 0xF) != 0)  // HW_ID.WAVE_ID
+        __builtin_amdgcn_s_setprio(1);
       for (int n = 0; n < nbat; n += 2) {
         issue_batch((n + 1) * U, kB, vB);
         __builtin_amdgcn_sched_barrier(0);
@@ -855,7 +882,25 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   const float v_scale = fp8 ? a.v_scale : 1.f;
   DecodeWorkspace ws = DecodeWorkspaceLayout(a.ws, a.B, a.Hq, a.D, P);
   static const StepArgs kNoStepArgs{};
-  const StepArgs& meta = a.step_args != nullptr ? *a.step_args : kNoStepArgs;
+  StepArgs sorted;
+  const StepArgs* meta_src = a.step_args != nullptr ? a.step_args : &kNoStepArgs;
+  if (a.step_args != nullptr && a.auto_items == 0 && a.stream_loads && a.B <= kStepArgBatch) {
+    // Sequences by decreasing partition length (the kernel's equal split),
+    // stable, so that the longest items go to the workgroups served first.
+    sorted = *a.step_args;
+    int32_t part_len[kStepArgBatch];
+    for (int32_t b = 0; b < a.B; ++b) {
+      const int32_t L = std::min(std::max(sorted.lens[b], 0), a.max_seq_len);
+      const int32_t Pb = std::max(1, (L + a.partition_tokens - 1) / a.partition_tokens);
+      part_len[b] = ((L + Pb - 1) / Pb + 63) & ~63;
+      sorted.order[b] = static_cast<uint8_t>(b);
+    }
+    std::stable_sort(sorted.order, sorted.order + a.B,
+                     [&](uint8_t x, uint8_t y) { return part_len[x] > part_len[y]; });
+    sorted.ordered = 1;
+    meta_src = &sorted;
+  }
+  const StepArgs& meta = *meta_src;
   auto launch_kernel = [&](auto kernel, const auto& meta) {
     hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(kThreads), 0, stream,
                        static_cast<T*>(a.out), static_cast<const T*>(a.q),

@@ -39,6 +39,11 @@ constexpr int kStepArgBatch = 128;
 struct StepArgs {
   int64_t slots[kStepArgBatch];
   int32_t lens[kStepArgBatch];
+  // ordered != 0: order lists the sequences by decreasing partition length
+  // (the host sorts them), and the decode kernel gives workgroup i the i-th
+  // work item of that list, kv-head groups innermost.
+  uint8_t order[kStepArgBatch];
+  int32_t ordered;
 };
 
 struct DecodeArgs {
