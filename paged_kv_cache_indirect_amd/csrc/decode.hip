@@ -259,6 +259,43 @@ using StepArgsOf = typename std::conditional<kFused, StepArgs, NoStepArgs>::type
 template <bool kFused, typename KV>
 using PoolPtr = typename std::conditional<kFused, KV*, const KV*>::type;
 
+// The decode work list over positions of the batch: the thread holding
+// positions tid * kPer .. + kPer - 1 (lengths Lv, -1 past the batch) writes
+// s_pref[i] = the first item of the sequence at position i, and thread
+// kThreads - 1 writes s_pref[kCompactBatch] = the items per kv-head group
+// (a sequence of length L has max(1, ceil(L / PT)) items). Ends with a
+// workgroup barrier.
+template <int kPer>
+__device__ __forceinline__ void build_work_list(const int (&Lv)[kPer], int PT, int tid, int lane, int w,
+                                                int* s_wsum, int* s_pref) {
+  int cnt[kPer];
+  int tsum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    cnt[i] = Lv[i] >= 0 ? max(1, (Lv[i] + PT - 1) / PT) : 0;
+    tsum += cnt[i];
+  }
+  // inclusive scan of tsum over the workgroup
+  int incl = tsum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int ww = 0; ww < w; ++ww) wbase += s_wsum[ww];
+  int run = wbase + incl - tsum;  // exclusive prefix of this thread
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    s_pref[tid * kPer + i] = run;
+    run += cnt[i];
+  }
+  if (tid == kThreads - 1) s_pref[kCompactBatch] = run;
+  __syncthreads();
+}
+
 // kFused: the fused-append variant (pa_append_decode*); the plain decode is
 // compiled without that code. kArgs (with kFused): lengths and slots come
 // from the launch arguments (pa_append_decode_args), not device memory.
@@ -272,7 +309,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
     int32_t P, int32_t per_xcd, float scale_log2, float v_scale, int32_t hsh,
     const T* __restrict__ knew, const T* __restrict__ vnew, const int64_t* new_slots_in,
-    int32_t* tables_out, int32_t auto_items, int32_t* ws_pt, const StepArgsOf<kArgs> meta) {
+    int32_t* tables_out, int32_t auto_items, int32_t* ws_pt, int32_t place_cus, const StepArgsOf<kArgs> meta) {
   using RG = RowGeom<KV, D>;
   using WD = Widen<KV>;
   constexpr int CPL = RG::kChunksPerLane;
@@ -299,7 +336,10 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // ---- work item (XCD-major; kv-head group, then sequence, then partition)
   const int wg = blockIdx.x;
   int p, b, gq;  // gq: group of (1 << hsh) kv heads
-  bool ordered = false;  // items taken in the host's order (see StepArgs)
+  // ordered: the work list runs through the sequences by decreasing
+  // partition length (sorted by the host, or below), and the items are
+  // placed on the place_cus CUs by rank.
+  bool ordered = false;
   int L;          // the sequence's length, clamped to [0, max_seq_len]
   const int NG = Hkv >> hsh;
   if (B <= kCompactBatch) {
@@ -311,7 +351,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     __shared__ int s_wsum[kWaves];
     constexpr int kPer = kCompactBatch / kThreads;  // sequences per thread
     // Position bb of the list holds sequence bb, or the host's order[bb].
-    if constexpr (kArgs) ordered = meta.ordered != 0;
+    if constexpr (kArgs) ordered = meta.ordered != 0 && place_cus > 0;
     int Lv[kPer];  // this thread's clamped lengths (-1: no such sequence)
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -374,44 +414,64 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       }
       if (wg == 0 && tid == 0 && ws_pt != nullptr) *ws_pt = PT;
     }
-    int cnt[kPer];
-    int tsum = 0;
+    build_work_list<kPer>(Lv, PT, tid, lane, w, s_wsum, s_pref);
+    // Device lengths, up to kSortBatch sequences, whose items fill more than
+    // one workgroup per CU but at most two (where the placement by rank
+    // pays; measured worse with more): the sequences are ranked by
+    // decreasing partition length (ties by index) and the list is rebuilt in
+    // that order; position i then holds sequence s_ord[i]. (Pipelined
+    // variants only: the launch places items only for them.)
+    constexpr int kSortBatch = 256;
+    bool dev_sort = false;
+    __shared__ int s_ord[kSortBatch];
+    if constexpr (!kArgs && Pipelined<T, KV, D, G>::value) {
+      static_assert(kSortBatch <= kCompactBatch, "sorted batches use the compact list");
+      __shared__ __align__(16) int s_key[kSortBatch];
+      const int n_items = NG * s_pref[kCompactBatch];
+      dev_sort = place_cus > 0 && B <= kSortBatch && n_items > place_cus && n_items <= 2 * place_cus;
+      if (dev_sort) {
+        static_assert(kSortBatch <= kThreads && kSortBatch % 4 == 0, "one sequence per thread");
+        // Thread t ranks sequence t (keys past the batch are -1, below every
+        // sequence): rank = sequences with a longer partition, or as long
+        // and earlier. The keys are read four at a time.
+        int key = -1;
+        if (tid < B) {
+          const int Lt = s_len[tid];
+          const int Pb = max(1, (Lt + PT - 1) / PT);
+          key = ((Lt + Pb - 1) / Pb + 63) & ~63;
+        }
+        if (tid < kSortBatch) s_key[tid] = key;
+        __syncthreads();
+        int rank = 0;
+        for (int x = 0; x < B; x += 4) {
+          const int4 k4 = *reinterpret_cast<const int4*>(&s_key[x]);
+          rank += (k4.x > key) | ((k4.x == key) & (x < tid));
+          rank += (k4.y > key) | ((k4.y == key) & (x + 1 < tid));
+          rank += (k4.z > key) | ((k4.z == key) & (x + 2 < tid));
+          rank += (k4.w > key) | ((k4.w == key) & (x + 3 < tid));
+        }
+        if (tid < B) s_ord[rank] = tid;
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      cnt[i] = Lv[i] >= 0 ? max(1, (Lv[i] + PT - 1) / PT) : 0;
-      tsum += cnt[i];
+        for (int i = 0; i < kPer; ++i) {
+          const int bb = tid * kPer + i;
+          Lv[i] = bb < B ? s_len[s_ord[bb]] : -1;
+        }
+        build_work_list<kPer>(Lv, PT, tid, lane, w, s_wsum, s_pref);
+        ordered = true;
+      }
     }
-    // inclusive scan of tsum over the workgroup
-    int incl = tsum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) s_wsum[w] = incl;
-    __syncthreads();
-    int wbase = 0;
-    for (int ww = 0; ww < w; ++ww) wbase += s_wsum[ww];
-    int run = wbase + incl - tsum;  // exclusive prefix of this thread
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      s_pref[tid * kPer + i] = run;
-      run += cnt[i];
-    }
-    if (tid == kThreads - 1) s_pref[kCompactBatch] = run;
-    __syncthreads();
     const int S = s_pref[kCompactBatch];  // items per kv head
     int k;
     if (ordered) {
       // Items ranked by decreasing length, head groups innermost. Workgroups
-      // c and c + C (C = the CU count in meta.ordered) run on the same CU,
+      // c and c + C (C = place_cus, the CU count) run on the same CU,
       // two per CU: when the items fill more than one workgroup per CU but
       // at most two, the CUs left with one workgroup take the longest items,
       // and each other CU pairs a longer item in its first workgroup (whose
       // waves the SIMDs serve first) with a shorter one in its second, so
       // that the CUs' totals even out. Otherwise workgroup i takes rank i.
-      int C = 0;
-      if constexpr (kArgs) C = meta.ordered;
+      const int C = place_cus;
       const int n = NG * S;
       if (wg >= n) return;
       int rank = wg;
@@ -437,9 +497,10 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       if (s_pref[mid] <= k) lo = mid; else hi = mid - 1;
     }
     p = k - s_pref[lo];
-    L = s_len[lo];
     b = lo;
+    if (dev_sort) b = s_ord[lo];
     if constexpr (kArgs) b = ordered ? meta.order[lo] : lo;
+    L = s_len[dev_sort ? b : lo];  // s_len: by sequence, or by position (host order)
   } else {
     const int item = (wg & 7) * per_xcd + (wg >> 3);
     if (item >= NG * B * P) return;
@@ -915,11 +976,18 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   static const StepArgs kNoStepArgs{};
   StepArgs sorted;
   const StepArgs* meta_src = a.step_args != nullptr ? a.step_args : &kNoStepArgs;
-  if (a.step_args != nullptr && a.auto_items == 0 && a.stream_loads && a.B <= kStepArgBatch &&
-      Pipelined<T, KV, D, G>::value && DeviceCuCount() > 0) {
+  // Placement of the items by length rank (pools without shared blocks, whose
+  // rows are streamed; pipelined variants, which run two workgroups per CU
+  // as the placement assumes; more items than CUs but at most two per CU):
+  // lengths in the launch arguments are sorted here, device lengths of up to
+  // 256 sequences by the kernel.
+  const int32_t place_cus =
+      a.place_by_rank && a.stream_loads && Pipelined<T, KV, D, G>::value && a.B <= kCompactBatch ? DeviceCuCount()
+                                                                                                : 0;
+  if (a.step_args != nullptr && a.auto_items == 0 && place_cus > 0 && a.B <= kStepArgBatch &&
+      items > place_cus && items <= 2 * static_cast<int64_t>(place_cus)) {
     // Sequences by decreasing partition length (the kernel's equal split,
-    // stable); the kernel places the items on the CUs by rank. Pipelined
-    // variants run two workgroups per CU, which the placement assumes.
+    // stable).
     sorted = *a.step_args;
     int32_t part_len[kStepArgBatch];
     for (int32_t b = 0; b < a.B; ++b) {
@@ -930,7 +998,7 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
     }
     std::stable_sort(sorted.order, sorted.order + a.B,
                      [&](uint8_t x, uint8_t y) { return part_len[x] > part_len[y]; });
-    sorted.ordered = DeviceCuCount();
+    sorted.ordered = 1;
     meta_src = &sorted;
   }
   const StepArgs& meta = *meta_src;
@@ -941,7 +1009,8 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
                        a.block_tables, a.seq_lens, ws.acc, ws.ml, a.B, a.Hkv, a.max_blocks,
                        __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
                        P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),
-                       static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, a.auto_items, ws.pt, meta);
+                       static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, a.auto_items, ws.pt, place_cus,
+                       meta);
   };
   auto launch = [&](auto stream_tag) {
     constexpr bool kStream = decltype(stream_tag)::value;

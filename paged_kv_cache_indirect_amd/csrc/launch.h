@@ -40,8 +40,8 @@ struct StepArgs {
   int64_t slots[kStepArgBatch];
   int32_t lens[kStepArgBatch];
   // ordered != 0: order lists the sequences by decreasing partition length
-  // (the host sorts them), and the decode kernel gives workgroup i the i-th
-  // work item of that list, kv-head groups innermost.
+  // (the host sorts them); the decode kernel builds its work list in that
+  // order and places the items on the CUs by rank.
   uint8_t order[kStepArgBatch];
   int32_t ordered;
 };
@@ -70,6 +70,9 @@ struct DecodeArgs {
   const StepArgs* step_args = nullptr;
   // K/V rows loaded non-temporally (pools without shared blocks).
   bool stream_loads = true;
+  // Items placed on the CUs by length rank, which assumes the decode has the
+  // whole GPU (off when it shares the GPU with a concurrent prefill).
+  bool place_by_rank = true;
   // > 0: the decode kernel chooses the partition from the device lengths
   // (at most this many items; partition_tokens then holds the shape rule's
   // choice, used when every sequence is a long context) and records it in

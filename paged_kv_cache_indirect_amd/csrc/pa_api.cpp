@@ -503,8 +503,10 @@ pa_status EnqueueStep(const pa_pool& pool, const StepPlan& plan, hipStream_t st)
     if (s != PA_OK) return s;
     const pa_status pre = FromHip(pa::LaunchPrefill(plan.pre, pool.side), "prefill launch");
     const pa_status rec = FromHip(hipEventRecord(pool.join, pool.side), "join record");
+    pa::DecodeArgs beside = plan.dec;
+    beside.place_by_rank = false;  // the prefill holds some of the CUs
     const pa_status dec = pre == PA_OK && rec == PA_OK
-                              ? FromHip(pa::LaunchDecode(plan.dec, st), "decode launch") : PA_OK;
+                              ? FromHip(pa::LaunchDecode(beside, st), "decode launch") : PA_OK;
     const pa_status wait = rec == PA_OK ? FromHip(hipStreamWaitEvent(st, pool.join, 0), "join wait") : rec;
     return pre != PA_OK ? pre : dec != PA_OK ? dec : wait;
   }
