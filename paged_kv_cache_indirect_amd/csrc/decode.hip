@@ -429,6 +429,9 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       __shared__ __align__(16) int s_key[kSortBatch];
       const int n_items = NG * s_pref[kCompactBatch];
       dev_sort = place_cus > 0 && B <= kSortBatch && n_items > place_cus && n_items <= 2 * place_cus;
+      // Workgroup ids from n_items on hold no item when placed by rank: the
+      // grid's surplus (sized for every sequence at max_seq_len) leaves now.
+      if (dev_sort && wg >= n_items) return;
       if (dev_sort) {
         static_assert(kSortBatch <= kThreads && kSortBatch % 4 == 0, "one sequence per thread");
         // Thread t ranks sequence t (keys past the batch are -1, below every

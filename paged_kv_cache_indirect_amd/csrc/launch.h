@@ -125,15 +125,18 @@ inline int32_t DecodeHeadShift(int32_t Hkv) { return Hkv % 2 == 0 ? 1 : 0; }
 //    as uniform in [0, max_seq_len], a sequence has max_seq_len / (2 pt) +
 //    1/2 partitions on average; the partition is the smallest whose
 //    expected item count stays within kDecodeShortItems
-//    (kDecodeShortItemsFp8 for E4M3 pools, whose waves spend more
-//    instructions per byte and gain from more of them).
+//    (kDecodeShortItemsFp8 for E4M3 pools). Both stay below two items per
+//    CU (512), where the decode kernel places the items on the CUs by
+//    length rank; the E4M3 count keeps more margin, measured on the
+//    8B-shaped FP8 batch: 72.1 us at 960 tokens (748 items, no placement),
+//    67.4 us at 1664 (500 items).
 // The partition is kept within [kDecodeMinPartition, kDecodeDefaultMaxPartition]
 // and rounded up to a multiple of 64.
 constexpr int32_t kDecodeCompactBatch = 1024;  // batches up to this size get the compact work list
 constexpr int32_t kDecodeLongContext = 8192;
 constexpr int64_t kDecodeLongItems = 256;
 constexpr int64_t kDecodeShortItems = 480;
-constexpr int64_t kDecodeShortItemsFp8 = 672;
+constexpr int64_t kDecodeShortItemsFp8 = 448;
 constexpr int32_t kDecodeMinPartition = 640;
 constexpr int32_t kDecodeDefaultMaxPartition = 8192;
 constexpr int32_t kDecodeMaxPartition = 1 << 24;
