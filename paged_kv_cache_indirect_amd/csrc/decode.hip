@@ -57,13 +57,17 @@
 //    outermost: consecutive hardware workgroup ids go to different XCDs, so
 //    each XCD owns a contiguous range (half a head group when Hkv = 8) and a
 //    shared prefix block of those heads is re-read from few XCDs' L2.
-//    With the lengths in the launch arguments and no shared blocks, the host
-//    sorts the sequences by partition length instead, and the items are
-//    placed on the CUs by rank: workgroups c and c + (CU count) share a CU,
-//    so the CUs left with one workgroup take the longest items and every
-//    other CU pairs a longer item (in its first workgroup, whose waves the
-//    SIMDs serve first) with a shorter one. Measured on the 8B-shaped batch:
-//    98.8 -> 94.8 us per fused step.
+//    Pools without shared blocks, where the items number more than one but
+//    at most two per CU, place them by length rank instead: the sequences
+//    are ranked by partition length (by the host when the lengths come in
+//    the launch arguments, by each workgroup for device lengths of up to 256
+//    sequences), workgroups c and c + (CU count) share a CU, and the CUs
+//    left with one workgroup take the longest items while every other CU
+//    pairs a longer item (in its first workgroup, whose waves the SIMDs
+//    serve first) with a shorter one. Measured on the 8B-shaped batch:
+//    98.8 -> 94.8 us per fused step, 98.3 -> 95.3 us per plain decode.
+//    Without that placement a CU's second workgroup raises its waves'
+//    priority instead.
 //  * Fused append (a decode step in one call): each sequence's new token is
 //    the last of its sequence, so it ends the range of exactly one wave per
 //    kv head. That wave streams the rest of its range as usual, then adds
