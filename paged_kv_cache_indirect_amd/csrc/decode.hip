@@ -937,20 +937,6 @@ __global__ __launch_bounds__(256) void MergeKernel(T* __restrict__ out, const fl
     out[static_cast<int64_t>(bh) * D + lane * EPL + e] = from_f32<T>(a[e] * inv);
 }
 
-// Compute units of the current device (0 if the query fails), cached per device.
-int DeviceCuCount() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cus[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 template <typename T, typename KV, int D, int G>
 hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   const int P = a.num_partitions;
@@ -1066,6 +1052,19 @@ hipError_t DispatchD(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int DeviceCuCount() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;

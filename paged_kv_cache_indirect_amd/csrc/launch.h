@@ -81,6 +81,10 @@ struct DecodeArgs {
 };
 hipError_t LaunchDecode(const DecodeArgs& a, hipStream_t stream);
 
+// Compute units of the current device (0 if the query fails), cached per
+// device; sizes the launches that place work by CU.
+int DeviceCuCount();
+
 struct PrefillArgs {
   void* out;
   const void* q;
