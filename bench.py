@@ -571,36 +571,41 @@ def run_mixed(args):
     wl = W.config("mixed")
     p = wl.plan
     res = {}
+    runs = 2                                         # fresh pools per run; the steps of both are averaged
     for mode in ("eager", "graph"):
-        log(f"[bench] mixed step ({mode}): Bd={p['Bd']} Bp={p['Bp']} chunk={p['chunk']} steps={p['steps']}")
-        run = harness.MixedRunner(wl, use_graph=(mode == "graph"))
-        run.stage_inputs()                           # step inputs resident in HBM before timing
-        stream = torch.cuda.current_stream()
+        log(f"[bench] mixed step ({mode}): Bd={p['Bd']} Bp={p['Bp']} chunk={p['chunk']} steps={p['steps']} "
+            f"runs={runs}")
         gpu_ms, host_ms, steps_bytes, steps_flops = [], [], [], []
-        for s in range(p["steps"]):
-            t0 = time.perf_counter()
-            run.prepare(s)
-            e0, e1 = TimingEvent(), TimingEvent()
-            e0.record(stream)
-            run.launch()
-            e1.record(stream)
-            host_ms.append((time.perf_counter() - t0) * 1e3)
-            torch.cuda.synchronize()
-            gpu_ms.append(e0.elapsed_time(e1))
-            lens = run.host_lens
-            dl = lens[:p["Bd"]].astype(np.int64)
-            steps_bytes.append(int(dl.sum()) * wl.Hkv * wl.D * 2 * wl.elem_bytes + run.T * wl.Hkv * wl.D * 2 * 2 *
-                               wl.elem_bytes)
-            ctx = lens[p["Bd"]:].astype(np.int64) - p["chunk"]
-            n = p["chunk"]
-            steps_flops.append(4.0 * wl.D * wl.Hq * float(np.sum(n * ctx + n * (n + 1) // 2)))
-        run.close()
-        timed = slice(2, None)                       # the first two steps warm up (and capture)
-        t = float(np.mean(gpu_ms[timed])) * 1e-3
-        floor = float(np.mean(steps_bytes[timed])) / (HBM_PEAK_GBPS * 1e9) + \
-            float(np.mean(steps_flops[timed])) / (BF16_MFMA_PEAK_TFLOPS * 1e12)
-        res[mode] = {"gpu_us_per_step": t * 1e6, "host_us_per_step": float(np.mean(host_ms[timed])) * 1e3,
-                     "roofline_floor_us": floor * 1e6, "frac_of_floor": floor / t}
+        for _ in range(runs):
+            run = harness.MixedRunner(wl, use_graph=(mode == "graph"))
+            run.stage_inputs()                       # step inputs resident in HBM before timing
+            stream = torch.cuda.current_stream()
+            for s in range(p["steps"]):
+                t0 = time.perf_counter()
+                run.prepare(s)
+                e0, e1 = TimingEvent(), TimingEvent()
+                e0.record(stream)
+                run.launch()
+                e1.record(stream)
+                host = (time.perf_counter() - t0) * 1e3
+                torch.cuda.synchronize()
+                if s < 2:                            # the first two steps warm up (and capture)
+                    continue
+                host_ms.append(host)
+                gpu_ms.append(e0.elapsed_time(e1))
+                lens = run.host_lens
+                dl = lens[:p["Bd"]].astype(np.int64)
+                steps_bytes.append(int(dl.sum()) * wl.Hkv * wl.D * 2 * wl.elem_bytes +
+                                   run.T * wl.Hkv * wl.D * 2 * 2 * wl.elem_bytes)
+                ctx = lens[p["Bd"]:].astype(np.int64) - p["chunk"]
+                n = p["chunk"]
+                steps_flops.append(4.0 * wl.D * wl.Hq * float(np.sum(n * ctx + n * (n + 1) // 2)))
+            run.close()
+        t = float(np.mean(gpu_ms)) * 1e-3
+        floor = float(np.mean(steps_bytes)) / (HBM_PEAK_GBPS * 1e9) + \
+            float(np.mean(steps_flops)) / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        res[mode] = {"gpu_us_per_step": t * 1e6, "host_us_per_step": float(np.mean(host_ms)) * 1e3,
+                     "roofline_floor_us": floor * 1e6, "frac_of_floor": floor / t, "timed_steps": len(gpu_ms)}
     res["workload"] = ("mixed serving step: 56 decode sequences U[512,4096] + 8 chunked-prefill sequences "
                        "(256-token chunks over cached context U[0,4096]), Hq 32 / Hkv 8, D 128, bf16, bs 16 "
                        "(seed 1007); step = scatter of all new rows + decode + prefill")

@@ -97,6 +97,9 @@ struct PrefillArgs {
   int32_t block_size, num_blocks, max_blocks;
   int32_t max_q_len;
   float scale;
+  // Running beside a concurrent decode on other CUs: the kernel serves its
+  // items with the fewest CUs that keep its span near its longest item.
+  bool beside_decode = false;
 };
 hipError_t LaunchPrefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -76,6 +76,12 @@
 //    evens out the slots' totals). A grid of one workgroup per item left CUs
 //    idle between a workgroup's end and the next one's start; this order
 //    measured about 1.5% faster.
+//  * Beside a concurrent decode (a mixed serving step) a prefill workgroup
+//    still takes a whole CU, and the decode's workgroups wait for CUs. There
+//    the kernel serves each XCD's items with the fewest slots whose span
+//    stays within kBesideSpanAllowance x the XCD's longest item (costs in key
+//    tiles, from the lengths on the device); the workgroups of the other
+//    slots leave at once and their CUs go to the decode.
 #include "device_common.h"
 #include "launch.h"
 
@@ -95,6 +101,12 @@ constexpr int kKT = 64;             // KV tokens per tile
 constexpr float kSumLimit = 32768.f;
 constexpr uint32_t kBf16Ones = 0x3F803F80u;  // (1.0, 1.0) as packed bf16
 constexpr int kRankedBatch = 256;   // batches up to this size are ordered by cache length
+// Beside a concurrent decode, the prefill may stretch its span to this many
+// times its longest item to leave CUs to the decode. Measured on MI355X, a
+// step of 56 decode sequences beside 8 x 256-row chunks (graph replay) took
+// 262 us with every CU open to the prefill, 242 / 232 / 236 us at 1.0 / 1.1 /
+// 1.25, and 294 / 335 us at 1.5 / 2 (the prefill then outlasts the decode).
+constexpr float kBesideSpanAllowance = 1.1f;
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x16v __attribute__((ext_vector_type(16)));
@@ -138,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
     const char* __restrict__ vc, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens, int32_t B,
     int32_t Hkv, int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t n_qtiles,
-    int32_t per_xcd, float scale_log2) {
+    int32_t per_xcd, float scale_log2, float span_allowance) {
   using PG = PGeom<D>;
   constexpr int QP = kRows / G;  // positions per workgroup
   constexpr int kKeysPerLoad = PG::kKeysPerLoad, kChunkBytes = PG::kChunkBytes, kSwz = PG::kSwz;
@@ -179,10 +191,48 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
   // is workgroup-uniform.
   const int xcd = wg & 7;
   const int slot = wg >> 3;
-  const int nslots = static_cast<int>(gridDim.x) >> 3;
+  int nslots = static_cast<int>(gridDim.x) >> 3;
   const int total = Hkv * n_qtiles * B;
   const int lo_item = xcd * per_xcd;
   const int count = max(0, min(per_xcd, total - lo_item));
+  if (span_allowance > 0.f) {
+    // Beside a concurrent decode: serve the XCD's items with the fewest slots
+    // whose span stays within span_allowance x its longest item (in key
+    // tiles, plus one per item for its start and end), so the other CUs go
+    // to the decode from the start. The workgroups of the unused slots leave.
+    float tsum = 0.f, tmax = 0.f;
+    for (int i = tid; i < count; i += kThreads) {
+      const int item = lo_item + i;
+      const int rem = item % (n_qtiles * B);
+      const int q0 = (n_qtiles - 1 - rem % n_qtiles) * QP;
+      int b = rem / n_qtiles;
+      if (B <= kRankedBatch) b = s_order[b];
+      const int nq = cu_q_lens[b + 1] - cu_q_lens[b];
+      if (q0 >= nq) continue;
+      const int L = min(max(seq_lens[b], 0), max_blocks << bs_shift);
+      const int keys = max(L - nq + min(q0 + QP, nq), 0);
+      const float c = static_cast<float>((keys + kKT - 1) / kKT + 1);
+      tsum += c;
+      tmax = fmaxf(tmax, c);
+    }
+    __shared__ float s_red[2][kWaves];
+    tsum = wave_reduce(tsum, OpAdd{});
+    tmax = wave_reduce(tmax, OpMax{});
+    if (lane == 0) {
+      s_red[0][w] = tsum;
+      s_red[1][w] = tmax;
+    }
+    __syncthreads();
+    tsum = 0.f;
+    tmax = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      tsum += s_red[0][v];
+      tmax = fmaxf(tmax, s_red[1][v]);
+    }
+    if (tmax > 0.f) nslots = min(nslots, max(1, static_cast<int>(ceilf(tsum / (span_allowance * tmax)))));
+    if (slot >= nslots) return;
+  }
   for (int band = 0; band * nslots < count; ++band) {
     const int local = band * nslots + ((band & 1) ? nslots - 1 - slot : slot);
     if (local >= count) continue;  // workgroup-uniform
@@ -587,7 +637,8 @@ hipError_t LaunchTyped(const PrefillArgs& a, hipStream_t stream) {
                      static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
                      a.cu_q_lens, a.block_tables, a.seq_lens, a.B, a.Hkv, a.max_blocks,
-                     __builtin_ctz(a.block_size), a.num_blocks, n_qtiles, per_xcd, scale_log2);
+                     __builtin_ctz(a.block_size), a.num_blocks, n_qtiles, per_xcd, scale_log2,
+                     a.beside_decode ? kBesideSpanAllowance : 0.f);
   return hipGetLastError();
 }
 

@@ -8,6 +8,11 @@ pa_step and through a captured HIP graph (pa_step_graph_*).
 * The eager step matches the fp64 oracle (decode and prefill rows) at the
   last step, within the bf16 tolerances (max-abs <= 2e-2, mean-abs <= 2e-3),
   and both pools' tables match the oracle's block manager.
+
+Two batches: a small decode, beside which the prefill keeps every CU, and a
+decode of 160 sequences (one item for every second CU or more), beside which
+the prefill serves its items with fewer workgroups and leaves the other CUs
+to the decode; its 100-row chunks end in a partial query tile.
 """
 import dataclasses
 
@@ -37,8 +42,16 @@ def small_mixed():
                         block_size=16, dtype="bf16", seed=31)
 
 
-def test_graph_replays_match_eager_and_oracle():
-    wl = small_mixed()
+def wide_mixed():
+    rng = np.random.default_rng(47)
+    dec = rng.integers(1, 300, 160).tolist()
+    pre = [0, 45, 700, 2500, 3000] + rng.integers(0, 3000, 19).tolist()
+    return W.make_mixed("mixed_wide", dec, pre, 100, 2, Hq=8, Hkv=2, D=128, block_size=16, dtype="bf16", seed=47)
+
+
+@pytest.mark.parametrize("make", [small_mixed, wide_mixed], ids=["small_decode", "prefill_beside_decode"])
+def test_graph_replays_match_eager_and_oracle(make):
+    wl = make()
     h = _harness()
     eager = h.MixedRunner(wl, use_graph=False)
     graph = h.MixedRunner(wl, use_graph=True)
