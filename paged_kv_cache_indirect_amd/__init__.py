@@ -526,13 +526,19 @@ class StepDesc:
         d.pre_batch = 0 if pre_seq_lens is None else int(pre_seq_lens.shape[0])
         d.pre_max_q_len = int(pre_max_q_len)
         self.c = d
+        self._checked = None  # (pool handle, pool layout) the tensors were last checked against
 
 
 def _check_step(pool: int, desc: StepDesc) -> None:
     """Each part of the step that runs (a non-zero count) against the pool's
-    layout, as pa_write_kv, pa_decode and pa_prefill check theirs."""
+    layout, as pa_write_kv, pa_decode and pa_prefill check theirs. The
+    description's pointers and counts are fixed when it is built, so the
+    check runs once per pool (handle and layout) it is used with."""
     import torch
     lay = pa_pool_layout(pool)
+    key = (pool, tuple(sorted(lay.items())))
+    if desc._checked == key:
+        return
     t = desc.named
     Hq, mb = desc.num_q_heads, desc.max_blocks
     if t["slot_mapping"] is not None and int(t["slot_mapping"].shape[0]) > 0:
@@ -555,6 +561,7 @@ def _check_step(pool: int, desc: StepDesc) -> None:
         _want(t["pre_cu_q_lens"], "pre_cu_q_lens", (B + 1,), torch.int32)
         _want(t["pre_block_tables"], "pre_block_tables", (B, mb), torch.int32)
     _want_gpu(**t)
+    desc._checked = key
 
 
 def pa_step(pool: int, desc: StepDesc, stream=None) -> None:
