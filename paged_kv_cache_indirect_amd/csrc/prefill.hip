@@ -46,17 +46,22 @@
 //    and PV of tile j - 1 and then the QK of tile j. Both start a tile
 //    together after its barrier. V of tile j - 1 is still read during tile
 //    j, so the ring holds j - 1, j, j + 1 (landing) and j + 2 (in flight).
-//    (Measured on MI355X, VALU work of one wave does not issue while another
-//    wave of the same SIMD streams MFMAs, so the two orders do not overlap
-//    softmax with products; they mostly even out the waves' barrier waits.)
+//    (Measured on MI355X with probes: exp, add, fma, max, select and bf16
+//    packing of one wave issue while the other wave of the SIMD streams
+//    MFMAs, but v_dot2_f32_bf16 and v_mov_b64 wait for them. The LDS serves
+//    one read instruction per 4 cycles per CU, 256 B/cycle with
+//    ds_read_b128 and 128 with ds_read_b64_tr_b16, so the 384 K and V reads
+//    of a tile and the direct loads' writes keep it busy about 1800 cycles,
+//    beside the SIMDs' 2048 MFMA cycles per tile.)
 //  * MFMA operands are read from LDS four MFMAs ahead of their use.
 //  * Online softmax in base 2 with no per-score max, subtraction or scaling
 //    in the common case: q is scaled by scale·log2(e) once (rounded to
 //    bf16), and each tile's score accumulators start from -m (the running
 //    max), so the products are already x - m and the weights are exp2 of
-//    them. The weights, packed to bf16 for the PV product, are summed two at
-//    a time with v_dot2_f32_bf16 (the denominator adds exactly the values
-//    the numerator multiplies). The first tile, and a tile whose half-row
+//    them. The weights are packed to bf16 for the PV product and summed in
+//    fp32 before the rounding (v_add_f32): a v_dot2_f32_bf16 sum of the
+//    packed values, measured on MI355X, does not issue while another wave of
+//    the SIMD runs MFMAs, and stalled the softmax behind them. The first tile, and a tile whose half-row
 //    weight sum exceeds 2^15 (so no weight is larger), take the tile max,
 //    raise m to the true running max, rescale O and l, and take the weights
 //    again; every weight stays ≤ 2^15, and the result is exact up to
@@ -99,7 +104,6 @@ constexpr int kKT = 64;             // KV tokens per tile
 // Largest sum of one half-row's weights in a tile before the running max is
 // raised (so every weight stays at most 2^15: finite in bf16 and fp32).
 constexpr float kSumLimit = 32768.f;
-constexpr uint32_t kBf16Ones = 0x3F803F80u;  // (1.0, 1.0) as packed bf16
 constexpr int kRankedBatch = 256;   // batches up to this size are ordered by cache length
 // Beside a concurrent decode, the prefill may stretch its span to this many
 // times its longest item to leave CUs to the decode. Measured on MI355X, a
@@ -436,20 +440,18 @@ __global__ __launch_bounds__(kThreads, 1) void PrefillKernel(
           }
       }
       auto weights = [&](float shift) {
-        float lt = 0.f;
+        float lt[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int tb = 0; tb < kSBlocks; ++tb)
 #pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
+          for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[2 * tb + hs][e] = static_cast<__bf16>(fast_exp2(s[tb][8 * hs + e] - shift));
-            const uint4 wv = __builtin_bit_cast(uint4, p[2 * tb + hs]);
-            lt = dot2_bf16(wv.x, kBf16Ones, lt);
-            lt = dot2_bf16(wv.y, kBf16Ones, lt);
-            lt = dot2_bf16(wv.z, kBf16Ones, lt);
-            lt = dot2_bf16(wv.w, kBf16Ones, lt);
-          }
-        return lt;
+            for (int e = 0; e < 8; ++e) {
+              const float wt = fast_exp2(s[tb][8 * hs + e] - shift);
+              p[2 * tb + hs][e] = static_cast<__bf16>(wt);
+              lt[e & 3] += wt;
+            }
+        return (lt[0] + lt[1]) + (lt[2] + lt[3]);
       };
       float lt = 0.f;
       bool exact = j == 0;
