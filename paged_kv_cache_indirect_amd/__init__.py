@@ -14,6 +14,7 @@ Build it with ``python paged_kv_cache_indirect_amd/build.py`` (or
 from __future__ import annotations
 
 import ctypes
+import itertools
 import os
 from typing import Optional, Sequence, Tuple
 
@@ -229,6 +230,13 @@ def _want_host(a, name: str, n: int, dtype) -> np.ndarray:
 
 
 # ------------------------------------------------------------------- pools
+# Pools this binding created, by handle: a generation number that changes
+# whenever a handle is reused for a new pool, so a step description checked
+# against one pool is checked again against the next pool at that handle.
+_pool_gen = {}
+_pool_gen_next = itertools.count(1)
+
+
 def pa_alloc_pool(k_cache, v_cache, free_order: Optional[Sequence[int]] = None) -> int:
     """Create a pool over k_cache/v_cache (torch device tensors [nb, bs, Hkv, D]).
     Returns the opaque handle (an int)."""
@@ -247,10 +255,12 @@ def pa_alloc_pool(k_cache, v_cache, free_order: Optional[Sequence[int]] = None) 
     _check(lib.pa_alloc_pool(ctypes.byref(layout), _dptr(k_cache), _dptr(v_cache),
                              None if order is None else order.ctypes.data, ctypes.byref(handle)),
            "pa_alloc_pool")
+    _pool_gen[handle.value] = next(_pool_gen_next)
     return handle.value
 
 
 def pa_free_pool(pool: int) -> None:
+    _pool_gen.pop(pool, None)
     lib.pa_free_pool(pool)
 
 
@@ -526,19 +536,21 @@ class StepDesc:
         d.pre_batch = 0 if pre_seq_lens is None else int(pre_seq_lens.shape[0])
         d.pre_max_q_len = int(pre_max_q_len)
         self.c = d
-        self._checked = None  # (pool handle, pool layout) the tensors were last checked against
+        self._checked = None  # (pool handle, generation) the tensors were last checked against
 
 
 def _check_step(pool: int, desc: StepDesc) -> None:
     """Each part of the step that runs (a non-zero count) against the pool's
     layout, as pa_write_kv, pa_decode and pa_prefill check theirs. The
-    description's pointers and counts are fixed when it is built, so the
-    check runs once per pool (handle and layout) it is used with."""
+    description's pointers and counts are fixed when it is built, and a
+    pool's layout never changes, so the check runs once per pool this binding
+    created (every call for a pool made elsewhere)."""
     import torch
-    lay = pa_pool_layout(pool)
-    key = (pool, tuple(sorted(lay.items())))
-    if desc._checked == key:
+    gen = _pool_gen.get(pool)
+    key = None if gen is None else (pool, gen)
+    if key is not None and desc._checked == key:
         return
+    lay = pa_pool_layout(pool)
     t = desc.named
     Hq, mb = desc.num_q_heads, desc.max_blocks
     if t["slot_mapping"] is not None and int(t["slot_mapping"].shape[0]) > 0:
