@@ -9,10 +9,12 @@ pa_step and through a captured HIP graph (pa_step_graph_*).
   last step, within the bf16 tolerances (max-abs <= 2e-2, mean-abs <= 2e-3),
   and both pools' tables match the oracle's block manager.
 
-Two batches: a small decode, beside which the prefill keeps every CU, and a
-decode of 160 sequences (one item for every second CU or more), beside which
-the prefill serves its items with fewer workgroups and leaves the other CUs
-to the decode; its 100-row chunks end in a partial query tile.
+Three batches: a small decode, beside which the prefill keeps every CU, and
+two decodes of 140-160 sequences (one item for every second CU or more),
+beside which the prefill serves its items with fewer workgroups and leaves
+the other CUs to the decode: head_dim 128 with 4 q heads per kv head and
+100-row chunks, and head_dim 64 with 8 per kv head, block size 32 and 70-row
+chunks; both chunk lengths end in a partial query tile.
 """
 import dataclasses
 
@@ -49,7 +51,16 @@ def wide_mixed():
     return W.make_mixed("mixed_wide", dec, pre, 100, 2, Hq=8, Hkv=2, D=128, block_size=16, dtype="bf16", seed=47)
 
 
-@pytest.mark.parametrize("make", [small_mixed, wide_mixed], ids=["small_decode", "prefill_beside_decode"])
+def wide_mixed_d64_g8():
+    rng = np.random.default_rng(53)
+    dec = rng.integers(1, 200, 140).tolist()
+    pre = [0, 31, 900, 2000] + rng.integers(0, 2000, 12).tolist()
+    return W.make_mixed("mixed_wide_d64", dec, pre, 70, 2, Hq=16, Hkv=2, D=64, block_size=32, dtype="bf16",
+                        seed=53)
+
+
+@pytest.mark.parametrize("make", [small_mixed, wide_mixed, wide_mixed_d64_g8],
+                         ids=["small_decode", "prefill_beside_decode", "prefill_beside_decode_d64_g8"])
 def test_graph_replays_match_eager_and_oracle(make):
     wl = make()
     h = _harness()
