@@ -477,7 +477,11 @@ typedef struct {
  * call on the device current then), forked from `stream` after the scatter
  * and joined back before the call's work on `stream` ends, so the
  * bandwidth-bound decode and the matrix-bound prefill share the GPU; work
- * enqueued on `stream` afterwards sees both outputs. Steps of one pool
+ * enqueued on `stream` afterwards sees both outputs. Beside a decode with at
+ * least one (sequence, kv-head pair) for every second compute unit, the
+ * prefill serves its work with the fewest compute units that keep its span
+ * within 1.1 times its longest work item, and leaves the others to the
+ * decode (the outputs are the same either way). Steps of one pool
  * share that stream, so calls for one pool from several host threads must be
  * serialised, as for every pool call. Every part is validated before
  * anything is launched. Errors: those of pa_write_kv, pa_decode and
