@@ -58,6 +58,11 @@ SMALL = [
     ([12, 250], [65, 100], 8, 1, 64, 32),
     ([0, 77], [129, 20], 4, 2, 64, 16),
     ([40, 0, 9], [0, 50, 300], 8, 2, 128, 32),     # an empty chunk
+    # 72 short chunks at 4 q heads per kv head: 576 work items, 72 per XCD,
+    # so each persistent workgroup takes items from three bands (the second
+    # one in reverse order, the third one partial)
+    (np.random.default_rng(61).integers(0, 200, 72).tolist(),
+     np.random.default_rng(62).integers(1, 64, 72).tolist(), 32, 8, 64, 16),
 ]
 
 
