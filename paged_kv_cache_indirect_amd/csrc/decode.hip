@@ -57,6 +57,13 @@
 //    outermost: consecutive hardware workgroup ids go to different XCDs, so
 //    each XCD owns a contiguous range (half a head group when Hkv = 8) and a
 //    shared prefix block of those heads is re-read from few XCDs' L2.
+//    Plain decodes whose items would need more than two workgroups per CU
+//    (long contexts at short partitions) take one partition per wave
+//    instead: an item holds the consecutive partitions of a head's waves,
+//    each wave streams a whole partition and writes its own partial state,
+//    so there are half (a quarter at odd Hkv) as many workgroups to start
+//    and no merge of a head's waves (measured on 8 x 32768 tokens at
+//    512-token partitions: 191 -> 183 us).
 //    Pools without shared blocks, where the items number more than one but
 //    at most two per CU, place them by length rank instead: the sequences
 //    are ranked by partition length (by the host when the lengths come in
@@ -313,7 +320,8 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     int32_t max_blocks, int32_t bs_shift, int32_t num_blocks, int32_t max_seq_len, int32_t PT,
     int32_t P, int32_t per_xcd, float scale_log2, float v_scale, int32_t hsh,
     const T* __restrict__ knew, const T* __restrict__ vnew, const int64_t* new_slots_in,
-    int32_t* tables_out, int32_t auto_items, int32_t* ws_pt, int32_t place_cus, const StepArgsOf<kArgs> meta) {
+    int32_t* tables_out, int32_t auto_items, int32_t* ws_pt, int32_t place_cus, int32_t pair_cus,
+    const StepArgsOf<kArgs> meta) {
   using RG = RowGeom<KV, D>;
   using WD = Widen<KV>;
   constexpr int CPL = RG::kChunksPerLane;
@@ -344,6 +352,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   // partition length (sorted by the host, or below), and the items are
   // placed on the place_cus CUs by rank.
   bool ordered = false;
+  bool pair = false;  // one partition per wave (workgroup-uniform)
   int L;          // the sequence's length, clamped to [0, max_seq_len]
   const int NG = Hkv >> hsh;
   if (B <= kCompactBatch) {
@@ -419,6 +428,15 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       if (wg == 0 && tid == 0 && ws_pt != nullptr) *ws_pt = PT;
     }
     build_work_list<kPer>(Lv, PT, tid, lane, w, s_wsum, s_pref);
+    // One partition per wave, when the items would take more than two
+    // workgroups per CU (pair_cus, the CU count, when allowed): an item is
+    // then the 2^(2 - hsh) consecutive partitions of a head's waves, so a
+    // sequence of Pb partitions has ceil(Pb / 2^(2 - hsh)) items. Fewer
+    // workgroups mean less start-up, and no merge of a head's waves.
+    if (pair_cus > 0 && NG * s_pref[kCompactBatch] > 2 * pair_cus) {
+      pair = true;
+      build_work_list<kPer>(Lv, PT << (2 - hsh), tid, lane, w, s_wsum, s_pref);
+    }
     // Device lengths, up to kSortBatch sequences, whose items fill more than
     // one workgroup per CU but at most two (where the placement by rank
     // pays; measured worse with more): the sequences are ranked by
@@ -432,7 +450,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
       static_assert(kSortBatch <= kCompactBatch, "sorted batches use the compact list");
       __shared__ __align__(16) int s_key[kSortBatch];
       const int n_items = NG * s_pref[kCompactBatch];
-      dev_sort = place_cus > 0 && B <= kSortBatch && n_items > place_cus && n_items <= 2 * place_cus;
+      dev_sort = !pair && place_cus > 0 && B <= kSortBatch && n_items > place_cus && n_items <= 2 * place_cus;
       // Workgroup ids from n_items on hold no item when placed by rank: the
       // grid's surplus (sized for every sequence at max_seq_len) leaves now.
       if (dev_sort && wg >= n_items) return;
@@ -527,7 +545,7 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   const int Hq = Hkv * G;
 
   const int Pb = max(1, (L + PT - 1) / PT);  // partitions of this sequence
-  if (p >= Pb) return;
+  if ((pair ? p << (2 - hsh) : p) >= Pb) return;
 
   // Fused append (new_slots given): row b of knew / vnew is sequence b's
   // newest token, at position L - 1, bound for slot new_slots[b] (< 0, or
@@ -557,8 +575,11 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
     tables_out[static_cast<int64_t>(b) * max_blocks + new_lb] = new_blk;
 
   const int PTb = ((L + Pb - 1) / Pb + 63) & ~63;  // equal split, multiple of 64 (<= PT)
-  const int TPW = PTb >> WS;
-  const int w0 = p * PTb + wq * TPW;
+  // A wave streams its share of the item's partition, or with one partition
+  // per wave the whole partition (p << WS) + wq (empty past the sequence's
+  // end).
+  const int TPW = pair ? PTb : PTb >> WS;
+  const int w0 = pair ? ((p << WS) + wq) * PTb : p * PTb + wq * TPW;
   // holds_new: this wave's range ends with the fused append's token, which
   // the loop leaves for the step after it.
   const bool holds_new = has_new && w0 <= new_tok && new_tok < w0 + TPW;  // wave-uniform
@@ -839,6 +860,25 @@ __global__ __launch_bounds__(kThreads, (Pipelined<T, KV, D, G>::kMinWaves)) void
   }
   __syncthreads();
 
+  // ---- one partition per wave: each wave's state is its partition's
+  if (pair && Pb > 1) {
+    for (int idx = tid; idx < (G * D << hsh << WS); idx += kThreads) {
+      const int ww = idx / (G * D);  // wave
+      const int h = (idx / D) % G;
+      const int d = idx % D;
+      const int pw = (p << WS) + (ww & ((1 << WS) - 1));
+      if (pw >= Pb) continue;
+      const int qh = ((gq << hsh) + (ww >> WS)) * G + h;  // q head
+      const int64_t row = (static_cast<int64_t>(b) * Hq + qh) * P + pw;
+      ws_acc[row * D + d] = s_acc[ww][h][d] * v_scale;
+      if (d == 0) {
+        ws_ml[row * 2 + 0] = s_ml[ww][h][0];
+        ws_ml[row * 2 + 1] = s_ml[ww][h][1];
+      }
+    }
+    return;
+  }
+
   // ---- merge the 4 waves; write the output, or this partition's partial state
   for (int idx = tid; idx < (G * D << hsh); idx += kThreads) {
     const int hw = idx / (G * D);       // kv head within the workgroup
@@ -961,6 +1001,11 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
     }
     items = S * NG;
   }
+  // Plain decodes with the compact list may take one partition per wave
+  // (the kernel decides from the items); the grid stays sized for the items
+  // of one partition per workgroup, an upper bound.
+  const int32_t cus = DeviceCuCount();
+  const int32_t pair_cus = a.new_k == nullptr && a.B <= kCompactBatch ? cus : 0;
   const int per_xcd = static_cast<int>((items + 7) / 8);
   const bool fp8 = sizeof(KV) == 1;
   const float scale_log2 = a.scale * (fp8 ? a.k_scale : 1.f) * 1.4426950408889634f;
@@ -975,8 +1020,7 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
   // lengths in the launch arguments are sorted here, device lengths of up to
   // 256 sequences by the kernel.
   const int32_t place_cus =
-      a.place_by_rank && a.stream_loads && Pipelined<T, KV, D, G>::value && a.B <= kCompactBatch ? DeviceCuCount()
-                                                                                                : 0;
+      a.place_by_rank && a.stream_loads && Pipelined<T, KV, D, G>::value && a.B <= kCompactBatch ? cus : 0;
   if (a.step_args != nullptr && a.auto_items == 0 && place_cus > 0 && a.B <= kStepArgBatch &&
       items > place_cus && items <= 2 * static_cast<int64_t>(place_cus)) {
     // Sequences by decreasing partition length (the kernel's equal split,
@@ -1003,7 +1047,7 @@ hipError_t LaunchTyped(const DecodeArgs& a, hipStream_t stream) {
                        __builtin_ctz(a.block_size), a.num_blocks, a.max_seq_len, a.partition_tokens,
                        P, per_xcd, scale_log2, v_scale, hsh, static_cast<const T*>(a.new_k),
                        static_cast<const T*>(a.new_v), a.new_slots, a.tables_out, a.auto_items, ws.pt, place_cus,
-                       meta);
+                       pair_cus, meta);
   };
   auto launch = [&](auto stream_tag) {
     constexpr bool kStream = decltype(stream_tag)::value;

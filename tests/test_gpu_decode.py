@@ -274,6 +274,27 @@ def test_decode_large_batches(B, pt):
     gpu.close()
 
 
+@pytest.mark.parametrize("lens,Hq,Hkv,D,bs,dtype,pt", [
+    # 3 kv heads (one per workgroup, four waves each): 203 partitions x 3 = 609 items
+    ([33000, 20500, 17000, 9000, 5000, 700, 1, 64, 511, 513, 1025, 12345], 6, 3, 128, 16, "bf16", 512),
+    # 8 kv heads (pairs): odd partition counts, 135 partitions x 4 = 540 items
+    ([33000, 20000, 513, 1, 9000, 4097], 32, 8, 128, 16, "bf16", 512),
+    # fp32, head_dim 64, block size 8: 530 partitions x 1 = 530 items
+    ([40000, 35000, 30000, 20000, 9000, 3, 257], 4, 2, 64, 8, "f32", 256),
+])
+def test_decode_many_items_one_partition_per_wave(lens, Hq, Hkv, D, bs, dtype, pt):
+    """Plain decodes whose (sequence, kv-head group, partition) items exceed
+    two per CU (512 on MI355X): each wave of a head then streams a whole
+    partition and writes its own partial state. Sequences whose partition
+    count is not a multiple of the waves per head leave waves of their last
+    item empty; one-partition sequences write their output directly."""
+    wl = small(lens, Hq, Hkv, D, bs, dtype, seed=71)
+    gpu, ora = build_both(wl)
+    got = widen_out(gpu.decode(pt, gpu.workspace_for(pt)), dtype)
+    assert_close(got, oracle_out(wl, ora), dtype, f"many items G={Hq // Hkv} Hkv={Hkv} D={D} pt={pt}")
+    gpu.close()
+
+
 def test_decode_partition_invariance_and_max_seq_len_slack():
     from paged_kv_cache_indirect_amd import pa_decode
     wl = small([1, 40, 511, 512, 513, 1500], Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", seed=9)
