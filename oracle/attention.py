@@ -8,7 +8,7 @@ axis into one logical K/V tensor, then runs ordinary attention
 [num_blocks, block_size, num_heads, head_dim] is from "LLM推理优化：技术原理
 解析总览" (dpshk.com), §3.3.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * scores carry a caller-supplied ``scale`` (the pages' sketch has none);
 * grouped-query heads: q head h reads kv head h // (Hq/Hkv);
 * ``seq_lens[b]`` counts the valid cache entries at call time (the new

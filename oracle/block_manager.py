@@ -16,7 +16,7 @@ Sources:
   enough free pages exist, instead of risking an out-of-memory failure;
   aborting a request frees all of its pages.
 
-Policy choices the pages leave open (listed in the design doc):
+Policy choices the pages leave open:
 * the free list is a LIFO stack; it starts as ``free_order`` (or ascending
   ids) with ``free_order[0]`` on top; a block whose refcount drops to zero is
   pushed back on top, and a sequence's blocks are pushed in table order;

@@ -3,7 +3,7 @@
 Source: "LLM推理优化：技术原理解析总览" (dpshk.com), §5.1: keeping the KV cache
 in 16-bit precision wastes memory next to a quantised model; the remedy given
 is an FP8 KV cache. The page names neither the 8-bit format nor how values
-are scaled. Readings (listed in the design doc):
+are scaled. Readings:
 
 * the format is OCP E4M3 ("FN"): 1 sign bit, 4 exponent bits with bias 7,
   3 mantissa bits; exponent field 0 holds subnormals m/8 · 2^-6; the codes
