@@ -575,7 +575,7 @@ def run_mixed(args):
     for mode in ("eager", "graph"):
         log(f"[bench] mixed step ({mode}): Bd={p['Bd']} Bp={p['Bp']} chunk={p['chunk']} steps={p['steps']} "
             f"runs={runs}")
-        gpu_ms, host_ms, steps_bytes, steps_flops = [], [], [], []
+        gpu_ms, host_ms, prep_ms, launch_ms, steps_bytes, steps_flops = [], [], [], [], [], []
         for _ in range(runs):
             run = harness.MixedRunner(wl, use_graph=(mode == "graph"))
             run.stage_inputs()                       # step inputs resident in HBM before timing
@@ -583,15 +583,19 @@ def run_mixed(args):
             for s in range(p["steps"]):
                 t0 = time.perf_counter()
                 run.prepare(s)
+                t1 = time.perf_counter()
                 e0, e1 = TimingEvent(), TimingEvent()
                 e0.record(stream)
                 run.launch()
                 e1.record(stream)
-                host = (time.perf_counter() - t0) * 1e3
+                t2 = time.perf_counter()
+                host = (t2 - t0) * 1e3
                 torch.cuda.synchronize()
                 if s < 2:                            # the first two steps warm up (and capture)
                     continue
                 host_ms.append(host)
+                prep_ms.append((t1 - t0) * 1e3)
+                launch_ms.append((t2 - t1) * 1e3)
                 gpu_ms.append(e0.elapsed_time(e1))
                 lens = run.host_lens
                 dl = lens[:p["Bd"]].astype(np.int64)
@@ -604,7 +608,11 @@ def run_mixed(args):
         t = float(np.mean(gpu_ms)) * 1e-3
         floor = float(np.mean(steps_bytes)) / (HBM_PEAK_GBPS * 1e9) + \
             float(np.mean(steps_flops)) / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        # host time = the harness's preparation (block-manager appends, table
+        # export, input uploads) + the launch call (pa_step or the graph launch)
         res[mode] = {"gpu_us_per_step": t * 1e6, "host_us_per_step": float(np.mean(host_ms)) * 1e3,
+                     "host_prepare_us_per_step": float(np.mean(prep_ms)) * 1e3,
+                     "host_launch_us_per_step": float(np.mean(launch_ms)) * 1e3,
                      "roofline_floor_us": floor * 1e6, "frac_of_floor": floor / t, "timed_steps": len(gpu_ms)}
     res["workload"] = ("mixed serving step: 56 decode sequences U[512,4096] + 8 chunked-prefill sequences "
                        "(256-token chunks over cached context U[0,4096]), Hq 32 / Hkv 8, D 128, bf16, bs 16 "
